@@ -1,0 +1,234 @@
+"""Python binding of the C ABI in include/pi.h (libpi.so, HIP for gfx950).
+
+Argument marshalling only: every step of the sparse FFN runs in the library's
+HIP kernels.  PyTorch provides device memory and the current stream.  There is
+no CPU fallback: if the shared library is missing or fails to load, importing
+the binding's entry points raises.
+
+Entry points (same names and meaning as the C functions):
+  workspace_bytes(layers, batch)
+  predict(layer, x, idx, count, scores=None, mask=None, ws=None)
+  sparse_ffn(layer, x, idx, count, y, mask=None, ws=None)
+  ffn_stack(layers, x, out, counts=None, trace=None, ws=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpi.so")
+
+PI_OK, PI_EINVAL, PI_EUNSUPPORTED, PI_EWORKSPACE, PI_EHIP = 0, 1, 2, 3, 4
+PI_F32, PI_F16, PI_Q4_0 = 0, 1, 2
+PI_RELU, PI_REGLU = 0, 1
+
+_DTYPE = {"f32": PI_F32, "f16": PI_F16, "q4_0": PI_Q4_0}
+_ACT = {"relu": PI_RELU, "reglu": PI_REGLU}
+
+
+class PiError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+        self.status = status
+
+
+class PiMat(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+
+
+class PiLayer(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("ffn", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("p_dtype", ctypes.c_int32),
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("pbias", ctypes.c_void_p), ("gate", PiMat), ("up", PiMat), ("downT", PiMat), ("b_down", ctypes.c_void_p)]
+
+
+class PiTrace(ctypes.Structure):
+    _fields_ = [("x_in", ctypes.c_void_p), ("scores", ctypes.c_void_p), ("mask", ctypes.c_void_p),
+                ("idx", ctypes.c_void_p), ("count", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libpi.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.pi_abi_version.restype = I32
+        L.pi_status_str.argtypes = [ctypes.c_int]
+        L.pi_status_str.restype = ctypes.c_char_p
+        L.pi_workspace_bytes.argtypes = [P, I32, I32]
+        L.pi_workspace_bytes.restype = SZ
+        L.pi_predict.argtypes = [P, P, I32, P, P, P, P, P, SZ, P]
+        L.pi_predict.restype = ctypes.c_int
+        L.pi_sparse_ffn.argtypes = [P, P, I32, P, P, P, P, P, SZ, P]
+        L.pi_sparse_ffn.restype = ctypes.c_int
+        L.pi_ffn_stack.argtypes = [P, I32, P, I32, P, P, P, P, SZ, P]
+        L.pi_ffn_stack.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return int(lib().pi_abi_version())
+
+
+def status_str(s: int) -> str:
+    return lib().pi_status_str(int(s)).decode()
+
+
+def _p(t) -> Optional[int]:
+    """Device address of a tensor (or an int address), None for None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int, where: str):
+    if status != PI_OK:
+        raise PiError(status, where)
+
+
+# ------------------------------------------------------------------ layers
+class DeviceLayer:
+    """One layer's tensors resident on the GPU plus the matching pi_layer record."""
+
+    def __init__(self, *, d, ffn, rank, act, w_dtype, p_dtype, A, B, bias, up, downT, gate=None,
+                 b_down=None, pbias=None):
+        self.d, self.ffn, self.rank = int(d), int(ffn), int(rank)
+        self.act, self.w_dtype, self.p_dtype = act, w_dtype, p_dtype
+        self.A, self.B, self.bias, self.up, self.downT, self.gate, self.b_down = \
+            A, B, bias, up, downT, gate, b_down
+        self.pbias = pbias
+        self.struct = self._make_struct()
+
+    @staticmethod
+    def _mat(m):
+        if m is None:
+            return PiMat(None, None)
+        if isinstance(m, tuple):            # Q4_0: (nibbles, scales)
+            return PiMat(m[0].data_ptr(), m[1].data_ptr())
+        return PiMat(m.data_ptr(), None)
+
+    def _make_struct(self) -> PiLayer:
+        return PiLayer(self.d, self.ffn, self.rank, _ACT[self.act], _DTYPE[self.w_dtype],
+                       _DTYPE[self.p_dtype], _p(self.A), _p(self.B), _p(self.bias),
+                       _p(self.pbias), self._mat(self.gate), self._mat(self.up), self._mat(self.downT),
+                       _p(self.b_down))
+
+    @classmethod
+    def upload(cls, lw, device="cuda") -> "DeviceLayer":
+        """Copy a host layer (numpy arrays; Q4_0 matrices with .nibbles/.scales) to the GPU."""
+        import numpy as np
+        import torch
+
+        def t(a):
+            if a is None:
+                return None
+            if hasattr(a, "nibbles"):
+                nib = torch.from_numpy(np.ascontiguousarray(a.nibbles)).to(device)
+                sc = torch.from_numpy(np.ascontiguousarray(a.scales).view(np.int16)).to(device)
+                return (nib, sc)
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+        cfg = lw.cfg
+        return cls(d=cfg.d, ffn=cfg.ffn, rank=cfg.rank, act=cfg.act, w_dtype=cfg.w_dtype,
+                   p_dtype=cfg.p_dtype, A=t(lw.A), B=t(lw.B), bias=t(lw.bias), up=t(lw.up),
+                   downT=t(lw.downT), gate=t(lw.gate), b_down=t(lw.b_down),
+                   pbias=t(getattr(lw, "pbias", None)))
+
+    def nbytes(self) -> int:
+        tot = 0
+        for m in (self.A, self.B, self.bias, self.pbias, self.up, self.downT, self.gate, self.b_down):
+            if m is None:
+                continue
+            for x in (m if isinstance(m, tuple) else (m,)):
+                tot += x.numel() * x.element_size()
+        return tot
+
+
+def _layer_array(layers: Sequence[DeviceLayer]):
+    arr = (PiLayer * len(layers))()
+    for i, L in enumerate(layers):
+        arr[i] = L.struct
+    return arr
+
+
+# ------------------------------------------------------------- entry points
+def workspace_bytes(layers, batch: int = 1) -> int:
+    layers = [layers] if isinstance(layers, DeviceLayer) else list(layers)
+    arr = _layer_array(layers)
+    return int(lib().pi_workspace_bytes(ctypes.cast(arr, ctypes.c_void_p), len(layers), batch))
+
+
+def alloc_workspace(layers, batch: int = 1, device="cuda"):
+    import torch
+    n = workspace_bytes(layers, batch)
+    if n == 0:
+        raise PiError(PI_EINVAL, "workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def predict(layer: DeviceLayer, x, idx, count, scores=None, mask=None, ws=None, batch: int = 1,
+            stream=None):
+    ws = alloc_workspace(layer, batch) if ws is None else ws
+    st = lib().pi_predict(ctypes.byref(layer.struct), _p(x), batch, _p(scores), _p(mask), _p(idx),
+                          _p(count), _p(ws), ws.numel(), _stream(stream))
+    _check(st, "pi_predict")
+
+
+def sparse_ffn(layer: DeviceLayer, x, idx, count, y, mask=None, ws=None, batch: int = 1,
+               stream=None):
+    ws = alloc_workspace(layer, batch) if ws is None else ws
+    st = lib().pi_sparse_ffn(ctypes.byref(layer.struct), _p(x), batch, _p(idx), _p(count),
+                             _p(mask), _p(y), _p(ws), ws.numel(), _stream(stream))
+    _check(st, "pi_sparse_ffn")
+
+
+def make_trace(n_layers: int, recs: Sequence[dict]):
+    arr = (PiTrace * n_layers)()
+    for i, r in enumerate(recs):
+        arr[i] = PiTrace(_p(r.get("x_in")), _p(r.get("scores")), _p(r.get("mask")),
+                         _p(r.get("idx")), _p(r.get("count")))
+    return arr
+
+
+class Stack:
+    """A stack of DeviceLayers with its layer array and workspace kept alive."""
+
+    def __init__(self, layers: Sequence[DeviceLayer], batch: int = 1, ws=None):
+        self.layers = list(layers)
+        self.batch = batch
+        self.arr = _layer_array(self.layers)
+        self.ws = alloc_workspace(self.layers, batch) if ws is None else ws
+
+    def __call__(self, x, out, counts=None, trace=None, stream=None):
+        tr = None if trace is None else ctypes.cast(trace, ctypes.c_void_p)
+        st = lib().pi_ffn_stack(ctypes.cast(self.arr, ctypes.c_void_p), len(self.layers), _p(x),
+                                self.batch, _p(out), _p(counts), tr, _p(self.ws), self.ws.numel(),
+                                _stream(stream))
+        _check(st, "pi_ffn_stack")
+
+
+def ffn_stack(layers, x, out, counts=None, trace=None, ws=None, batch: int = 1, stream=None):
+    Stack(layers, batch, ws)(x, out, counts, trace, stream)
+
+
+EXPORTED = ("pi_workspace_bytes", "pi_predict", "pi_sparse_ffn", "pi_ffn_stack", "pi_status_str",
+            "pi_abi_version")

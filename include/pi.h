@@ -1,0 +1,154 @@
+/*
+ * pi.h -- C ABI of the predictor-guided, neuron-aware sparse FFN for one AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (PowerInfer pages): for the current token, a per-layer low-rank
+ * predictor marks which FFN neurons will fire, and only those neurons' rows of
+ * the up/gate projections and columns of the down projection are read and
+ * computed, with no conversion of the weights into a sparse format at run time
+ * (unite.ai article, "Online-Phase", "Adaptive Sparsity-Prädiktoren",
+ * "Neuronenbewusster Operator"; 机器之心 article, Fig. 8 paragraph; GeekNews
+ * summary, "CPU/GPUハイブリッド推論方式").  Every neuron stays resident in HBM;
+ * the hot/cold profile survives only as the storage order of the neurons.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing, keeps no pointer after it returns and never
+ *    synchronises the stream.  `stream` is a hipStream_t passed as void*
+ *    (NULL = the default stream).
+ *  - Matrices are row-major.  Neurons are in STORAGE order (hot-first in the
+ *    shipped workloads); lists and masks refer to storage slots.  A table that
+ *    maps slots back to original neuron ids is the caller's business.
+ *  - Validation is synchronous and host-only: PI_EINVAL / PI_EUNSUPPORTED /
+ *    PI_EWORKSPACE are returned before anything is enqueued.  PI_EHIP means a
+ *    launch was rejected (hipGetLastError); faults inside kernels surface at
+ *    the caller's next synchronisation.
+ *  - Rules checked: non-NULL required pointers; d, ffn, rank > 0;
+ *    bias and pbias 16-byte aligned;
+ *    d % 64 == 0; rank % 64 == 0; weight, predictor and activation pointers
+ *    16-byte aligned, Q4_0 scales 4-byte aligned; 1 <= batch <= 32;
+ *    act REGLU needs `gate`; predictor dtype F32 or F16 (Q4_0 predictor:
+ *    PI_EUNSUPPORTED); every layer of a stack has the same d.
+ *  - Calls on distinct workspaces are independent; calls sharing a workspace
+ *    must be ordered on one stream.
+ */
+#ifndef PI_H_
+#define PI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PI_ABI_VERSION 1
+
+typedef enum {
+  PI_OK = 0,
+  PI_EINVAL = 1,        /* bad argument (NULL, size, alignment, dtype/act combination) */
+  PI_EUNSUPPORTED = 2,  /* valid request this build does not implement */
+  PI_EWORKSPACE = 3,    /* ws NULL or ws_bytes < pi_workspace_bytes(...) */
+  PI_EHIP = 4           /* a kernel launch failed */
+} pi_status;
+
+typedef enum { PI_F32 = 0, PI_F16 = 1, PI_Q4_0 = 2 } pi_dtype;
+
+/* ReLU: h = max(b + W_up x, 0).  ReGLU: h = max(b + W_gate x, 0) * (W_up x).
+ * (GeekNews summary: ReLU / ReGLU / Squared-ReLU models.) */
+typedef enum { PI_RELU = 0, PI_REGLU = 1 } pi_act;
+
+/* One weight matrix [ffn][d].  F32/F16: `w` points at ffn*d elements and
+ * `scale` is NULL.  Q4_0 (blocks of 32 4-bit values q in [0,15] with one
+ * binary16 scale s, w = s*(q-8)): `w` points at nibbles uint8 [ffn][d/2] and
+ * `scale` at binary16 bits [ffn][d/32].  Inside a 32-block, weight j < 16 is
+ * the low nibble of byte j and weight j+16 the high nibble of byte j. */
+typedef struct {
+  const void* w;
+  const uint16_t* scale;
+} pi_mat;
+
+/* One FFN layer with its predictor. */
+typedef struct {
+  int32_t d;        /* model width */
+  int32_t ffn;      /* number of FFN neurons */
+  int32_t rank;     /* predictor rank r */
+  int32_t act;      /* pi_act */
+  int32_t w_dtype;  /* pi_dtype of gate/up/downT */
+  int32_t p_dtype;  /* pi_dtype of A and B (F32 or F16) */
+  const void* A;    /* [rank][d] predictor first matrix */
+  const void* B;    /* [ffn][rank] predictor second matrix, storage order */
+  const float* bias;/* [ffn] bias of the gate (ReGLU) or up (ReLU) projection */
+  const float* pbias;/* [ffn] predictor output bias, s_i = pbias_i + B[i] . (A x);
+                       NULL = use `bias` */
+  pi_mat gate;      /* [ffn][d]; REGLU only (ignored for RELU) */
+  pi_mat up;        /* [ffn][d] */
+  pi_mat downT;     /* [ffn][d]; row i is column i of W_down, so the down projection
+                       over active neurons is a row gather too */
+  const float* b_down; /* [d] or NULL */
+} pi_layer;
+
+/* Optional per-layer record written by pi_ffn_stack (any field may be NULL). */
+typedef struct {
+  float* x_in;      /* [batch][d]   input of the layer */
+  float* scores;    /* [batch][ffn] predictor scores */
+  uint8_t* mask;    /* [batch][ffn] 1 if score > 0 */
+  int32_t* idx;     /* [ffn]        ascending storage ids of the union mask */
+  int32_t* count;   /* [1]          number of entries in idx */
+} pi_trace;
+
+/* Workspace needed by any entry point for these layers at this batch.
+ * Returns 0 if the layer array is invalid. */
+size_t pi_workspace_bytes(const pi_layer* layers, int32_t n_layers, int32_t batch);
+
+/*
+ * pi_predict -- predictor, threshold and compaction for one layer
+ * (unite.ai article, "Online-Phase": predict the activated neurons of the
+ * current layer and skip the others; 机器之心 article, Fig. 8 paragraph).
+ *   t = A x_b;  s_{b,i} = pbias_i + B[i] . t  (float32 accumulation; pbias
+ *   defaults to bias)
+ *   mask_{b,i} = (s_{b,i} > 0)  strict; zero and NaN are inactive
+ *   idx = ascending storage ids i with mask_{b,i} = 1 for some b; *count = |idx|
+ * x: [batch][d] float32.  scores: [batch][ffn] or NULL.  mask: [batch][ffn],
+ * may be NULL when batch == 1.  idx: [ffn] int32.  count: [1] int32, written
+ * on the device (the host never reads it inside the library).
+ */
+pi_status pi_predict(const pi_layer* layer, const float* x, int32_t batch, float* scores,
+                     uint8_t* mask, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * pi_sparse_ffn -- neuron-aware sparse FFN over a caller-supplied list
+ * (unite.ai article, "Neuronenbewusster Operator": individual rows and columns
+ * of the matrices, no sparse-format conversion).
+ *   for each listed i (and, when batch > 1, only where mask_{b,i} = 1):
+ *     ReLU:  h = max(bias_i + up[i] . x_b, 0)
+ *     ReGLU: h = max(bias_i + gate[i] . x_b, 0) * (up[i] . x_b)
+ *   y_b = sum_i h * downT[i]  (+ b_down)
+ * idx: ascending or not, entries < ffn, first min(*count, ffn) used (count is
+ * read on the device and clamped to [0, ffn]); mask: [batch][ffn], NULL iff
+ * batch == 1.  y: [batch][d] float32, fully overwritten.
+ */
+pi_status pi_sparse_ffn(const pi_layer* layer, const float* x, int32_t batch, const int32_t* idx,
+                        const int32_t* count, const uint8_t* mask, float* y, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/*
+ * pi_ffn_stack -- n_layers layers in sequence, each predict -> sparse FFN,
+ * joined by a residual with a parameter-free RMS norm (not on the pages; it
+ * keeps firing rates stable through the stack):
+ *   x_0 = x;  x_{l+1} = v / sqrt(mean(v^2) + 1e-6),  v = x_l + y_l;  out = x_L
+ * counts: [n_layers] int32 active count per layer (union when batch > 1), or
+ * NULL.  trace: array of n_layers records, or NULL.
+ */
+pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x, int32_t batch,
+                       float* out, int32_t* counts, const pi_trace* trace, void* ws,
+                       size_t ws_bytes, void* stream);
+
+const char* pi_status_str(pi_status s);
+int32_t pi_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PI_H_ */

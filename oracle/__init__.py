@@ -12,13 +12,13 @@ matrix-vector product (``@``) is a library primitive and is used as one step.
 
 What it computes (per layer, per sequence b, x_b in R^d):
 
-  predictor   t = A x ;  s_i = b_i + sum_j B[i,j] t_j            (``predictor_scores``)
+  predictor   t = A x ;  s_i = c_i + sum_j B[i,j] t_j            (``predictor_scores``)
       A low-rank MLP predicts which FFN neurons of the current layer will
       fire (GeekNews summary, "CPU/GPUハイブリッド推論方式": adaptive predictor;
       unite.ai article, "Online-Phase" and "Adaptive Sparsity-Prädiktoren";
       机器之心 article, Fig. 8 paragraph).  Reading taken: the hidden layer is
-      the identity (a rank-r GEMV pair) and the output bias is the neuron's
-      own bias b_i.
+      the identity (a rank-r GEMV pair); the output bias c_i is the layer's
+      ``pbias`` when given, else the up/gate bias b_i.
   threshold   m_i = (float32(s_i) > 0), strict; NaN is inactive   (``threshold``)
       The pages give no threshold; 0 is the centre of the reported
       ambiguity band.  The decision is taken on the score rounded to float32,
@@ -204,7 +204,9 @@ def layer_forward(layer, X, act: str | None = None) -> dict:
     """
     act = act or _get(layer, "act") or _get(_get(layer, "cfg"), "act")
     X = np.atleast_2d(np.asarray(X, dtype=np.float64))
-    S = predictor_scores(_get(layer, "A"), _get(layer, "B"), _get(layer, "bias"), X)
+    pbias = _get(layer, "pbias")
+    S = predictor_scores(_get(layer, "A"), _get(layer, "B"),
+                         _get(layer, "bias") if pbias is None else pbias, X)
     M = threshold(S)
     idx = active_list(union_mask(M))
     Y = sparse_ffn(act, _get(layer, "gate"), _get(layer, "up"), _get(layer, "downT"),

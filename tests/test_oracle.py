@@ -254,7 +254,7 @@ def test_q4_layer_matches_float_layer(gen):
     cfg = gen.CONFIGS[4].with_(d=128, ffn=96, rank=64)
     lw = gen.make_layer(cfg, 0)
     X = gen.make_x(cfg, 0)
-    Lf = dict(act="relu", A=lw.A, B=lw.B, bias=lw.bias, gate=None, b_down=None,
+    Lf = dict(act="relu", A=lw.A, B=lw.B, bias=lw.bias, pbias=lw.pbias, gate=None, b_down=None,
               up=oracle.decode(lw.up), downT=oracle.decode(lw.downT))
     r1, r2 = oracle.layer_forward(lw, X), oracle.layer_forward(Lf, X)
     assert np.array_equal(r1["y"], r2["y"]) and np.array_equal(r1["idx"], r2["idx"])

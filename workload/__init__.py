@@ -20,8 +20,13 @@ article, "Neuronen-Platzierung und -Verwaltung").
 Layouts (row-major, storage order = hot-first unless ``order="identity"``):
   A      [rank][d]     predictor first matrix      (p_dtype)
   B      [ffn][rank]   predictor second matrix     (p_dtype)
-  bias   [ffn]         float32; gate bias (ReGLU) or up bias (ReLU), also the
-                       predictor's output bias
+  bias   [ffn]         float32; gate bias (ReGLU) or up bias (ReLU):
+                       PhiInv(p_i) * ||stored row_i||, so w_i.x + b_i > 0 with
+                       probability p_i for x ~ N(0, I)
+  pbias  [ffn]         float32; the predictor's output bias PhiInv(p_i): its
+                       output B_i.(A x) has unit variance for x ~ N(0, I)
+                       (A ~ N(0, 1/d), B ~ N(0, 1/r)), so it also marks neuron
+                       i with probability ~p_i
   gate   [ffn][d]      ReGLU only                  (w_dtype)
   up     [ffn][d]                                  (w_dtype)
   downT  [ffn][d]      row i = column i of W_down  (w_dtype)
@@ -198,7 +203,7 @@ class Q4Matrix:
         return Q4Matrix(self.nibbles[rows], self.scales[rows])
 
 
-@dataclass
+@dataclass(frozen=True)
 class FFNConfig:
     name: str
     d: int
@@ -249,6 +254,7 @@ class LayerWeights:
     downT: object
     gate: object = None    # ReGLU only
     b_down: Optional[np.ndarray] = None
+    pbias: Optional[np.ndarray] = None   # float32 [ffn], storage order
 
     @property
     def p_storage(self) -> np.ndarray:
@@ -261,7 +267,8 @@ class LayerWeights:
             if isinstance(m, Q4Matrix):
                 return m.nibbles.nbytes + m.scales.nbytes
             return m.nbytes
-        return sum(nb(m) for m in (self.A, self.B, self.bias, self.up, self.downT, self.gate))
+        return sum(nb(m) for m in (self.A, self.B, self.bias, self.pbias, self.up, self.downT,
+                                   self.gate))
 
 
 def make_layer(cfg: FFNConfig, layer: int, order: str = "hot_first", nthreads: int = 0,
@@ -288,8 +295,10 @@ def make_layer(cfg: FFNConfig, layer: int, order: str = "hot_first", nthreads: i
     up = mat(TAG_UP)
     downT = mat(TAG_DOWN)
     norms = row_norms(gate if cfg.act == "reglu" else up, nthreads)
-    bias = (ndtri(p[perm]) * norms).astype(np.float32)
-    return LayerWeights(cfg, layer, p, perm, A, B, bias, up, downT, gate, None)
+    z = ndtri(p[perm])
+    bias = (z * norms).astype(np.float32)
+    pbias = z.astype(np.float32)
+    return LayerWeights(cfg, layer, p, perm, A, B, bias, up, downT, gate, None, pbias)
 
 
 def make_x(cfg: FFNConfig, token: int, seqs: int = 1, stream: int = 0) -> np.ndarray:
