@@ -59,18 +59,32 @@ struct Dims {
   int d = 0, fmax = 0, rmax = 0;
 };
 
+constexpr int kMaxParts = 4;       // neuron splits of the down projection (partial y vectors)
+constexpr int kMaxK2Blocks = 1 << 16;
+
+int epl_of(int dt) { return dt == PI_F32 ? 4 : (dt == PI_F16 ? 8 : 32); }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Grid size of the predictor kernel (one active count per block): at most this.
+int k2_blocks_for(int ffn, int rank, int p_dtype);
+int k2_blocks_max(int ffn);
+
 struct WsLayout {
-  size_t t, xbuf, ybuf, bits, h, misc, total;
+  size_t t, xbuf, ybuf, mask, h, cnt, misc, total;
+  size_t xs, ys;   // sizes of one x / one y (all partials) buffer
 };
 
 WsLayout layout(const Dims& D, int batch) {
   WsLayout w{};
   size_t o = 0;
+  w.xs = align_up(sizeof(float) * (size_t)D.d * batch);
+  w.ys = align_up(sizeof(float) * (size_t)D.d * batch * kMaxParts);
   w.t = o;    o += align_up(sizeof(float) * (size_t)D.rmax * batch);
-  w.xbuf = o; o += align_up(sizeof(float) * (size_t)D.d * batch) * 2;
-  w.ybuf = o; o += align_up(sizeof(double) * (size_t)D.d * batch) * 2;
-  w.bits = o; o += align_up(sizeof(uint32_t) * (size_t)((D.fmax + 31) / 32) * batch);
+  w.xbuf = o; o += w.xs * 2;
+  w.ybuf = o; o += w.ys * 2;
+  w.mask = o; o += align_up((size_t)cdiv(D.fmax, 16) * 16 * batch);     // padded to 16-byte groups
   w.h = o;    o += align_up(sizeof(float) * (size_t)D.fmax * batch);
+  w.cnt = o;  o += align_up(sizeof(int32_t) * (size_t)k2_blocks_max(D.fmax));
   w.misc = o; o += kAlign;
   w.total = o;
   return w;
@@ -79,24 +93,24 @@ WsLayout layout(const Dims& D, int batch) {
 struct Ws {
   float* t;
   float* x[2];
-  double* y[2];
-  uint32_t* bits;
+  float* y[2];
+  uint8_t* mask;
   float* h;
+  int32_t* cnt;
   int32_t* misc;
 };
 
-Ws carve(void* base, const WsLayout& L, const Dims& D, int batch) {
+Ws carve(void* base, const WsLayout& L) {
   char* b = static_cast<char*>(base);
   Ws w;
   w.t = reinterpret_cast<float*>(b + L.t);
-  const size_t xs = align_up(sizeof(float) * (size_t)D.d * batch);
-  const size_t ys = align_up(sizeof(double) * (size_t)D.d * batch);
   w.x[0] = reinterpret_cast<float*>(b + L.xbuf);
-  w.x[1] = reinterpret_cast<float*>(b + L.xbuf + xs);
-  w.y[0] = reinterpret_cast<double*>(b + L.ybuf);
-  w.y[1] = reinterpret_cast<double*>(b + L.ybuf + ys);
-  w.bits = reinterpret_cast<uint32_t*>(b + L.bits);
+  w.x[1] = reinterpret_cast<float*>(b + L.xbuf + L.xs);
+  w.y[0] = reinterpret_cast<float*>(b + L.ybuf);
+  w.y[1] = reinterpret_cast<float*>(b + L.ybuf + L.ys);
+  w.mask = reinterpret_cast<uint8_t*>(b + L.mask);
   w.h = reinterpret_cast<float*>(b + L.h);
+  w.cnt = reinterpret_cast<int32_t*>(b + L.cnt);
   w.misc = reinterpret_cast<int32_t*>(b + L.misc);
   return w;
 }
@@ -115,125 +129,242 @@ bool dims_of(const pi_layer* layers, int32_t n, Dims* D) {
 
 // ---------------------------------------------------------- launch shapes
 constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / WAVE;
 
-int k1_blocks(int r) { return std::max(1, std::min(1024, (r + kWaves - 1) / kWaves)); }
+// 16-byte chunks per lane that one wave-wide pass over a row of n elements takes
+int chunks_of(int n, int dt) { return cdiv(n, WAVE * epl_of(dt)); }
 
-int k2_blocks(int f) {
-  int nb = std::min(f, 512);
-  nb = std::max(nb, (f + K2_MAX_PER_BLOCK - 1) / K2_MAX_PER_BLOCK);
-  return std::max(1, nb);
+// Smallest supported per-round chunk count >= n (the largest if none is; the
+// kernel then loops over rounds).  Loads of a round are issued unconditionally,
+// so an exact fit avoids reading chunks twice.
+template <size_t K>
+int pick(const int (&opts)[K], int n) {
+  for (size_t i = 0; i < K; ++i)
+    if (opts[i] >= n) return opts[i];
+  return opts[K - 1];
 }
 
-int epl_of(int dt) { return dt == PI_F32 ? 4 : (dt == PI_F16 ? 8 : 32); }
+// K1: one wave per row of A.
+constexpr int kK1Nch[] = {2, 4, 8, 16, 24};
+int k1_blocks(int r) { return std::max(1, cdiv(r, K1_WAVES)); }
 
-void k3_shape(int d, int dt, int* CT, int* NC) {
-  const int tw = WAVE * epl_of(dt);
-  *CT = (d + tw - 1) / tw;
-  *NC = std::max(1, std::min(64, 256 / *CT));
+// K2: chunks per lane per row of B held at once (1 or 2)
+int k2_pch_of(int rank, int p_dtype) { return chunks_of(rank, p_dtype) <= 1 ? 1 : 2; }
+int k2_pch(const pi_layer* L) { return k2_pch_of(L->rank, L->p_dtype); }
+// chunks per lane per gathered up/gate row held at once
+constexpr int kWchF32[] = {2, 8};
+constexpr int kWchF16[] = {2, 8, 14, 16};
+constexpr int kWchQ4[] = {1, 6};
+int k2_wch(const pi_layer* L) {
+  const int n = chunks_of(L->d, L->w_dtype);
+  return L->w_dtype == PI_F32 ? pick(kWchF32, n) : L->w_dtype == PI_F16 ? pick(kWchF16, n) : pick(kWchQ4, n);
+}
+// about one batch of B rows per wave, and at least ~4 waves per CU when ffn allows
+int k2_blocks_for(int ffn, int rank, int p_dtype) {
+  const int rb = 16 / k2_pch_of(rank, p_dtype);
+  const int nw = std::max(cdiv(ffn, rb), std::min(1024, cdiv(ffn, 4)));
+  return std::min(kMaxK2Blocks, std::max(1, cdiv(nw, K2_WAVES)));
+}
+int k2_blocks(const pi_layer* L) { return k2_blocks_for(L->ffn, L->rank, L->p_dtype); }
+int k2_blocks_max(int ffn) { return std::max(k2_blocks_for(ffn, 64, PI_F32), k2_blocks_for(ffn, 1 << 20, PI_F32)); }
+
+// K3: tiles of TWC = 4 chunks per row (64-byte row segments: one request per
+// row and tile, half an L2 line, the other half read by the neighbouring tile
+// on the same XCD), fewer when the row is short, and NC neuron splits so that
+// the grid has at least ~256 blocks of 8 waves.  Wider tiles scan the mask
+// fewer times per row but give fewer blocks; narrower ones multiply the L2
+// requests per byte.
+struct K3Shape {
+  int twc, ct, nc;
+};
+K3Shape k3_shape(int d, int dt) {
+  const int nchunks = d / epl_of(dt);
+  K3Shape s;
+  s.twc = nchunks >= 64 ? 4 : nchunks >= 32 ? 2 : 1;
+  s.ct = cdiv(nchunks, s.twc);
+  s.nc = std::max(1, std::min(kMaxParts, cdiv(256, s.ct)));
+  return s;
 }
 
 // ---------------------------------------------------------------- dispatch
+struct K1Args {
+  const float* x_prev;
+  const float* y_prev;
+  int y_np;
+  float* x_out;
+  float* x_trace;
+  float* t;
+};
+
+template <int PT, int NCH>
+void launch_k1_t(const pi_layer* L, const K1Args& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_predict_t<PT, NCH>), dim3(k1_blocks(L->rank)), dim3(K1_WAVES * WAVE),
+                     sizeof(float) * L->d, st, L->A, L->rank, L->d, a.x_prev, a.y_prev, a.y_np, a.x_out,
+                     a.x_trace, a.t);
+}
+
 template <int PT>
-void launch_k1(const pi_layer* L, const float* x_prev, const double* y_prev, float* x_out, float* x_trace,
-               float* t, double* zero_y, int zero_y_n, uint32_t* zero_w, int zero_w_n, hipStream_t st) {
-  const int nb = k1_blocks(L->rank);
-  hipLaunchKernelGGL(k_predict_t<PT>, dim3(nb), dim3(kThreads), sizeof(float) * L->d, st, L->A, L->rank, L->d,
-                     x_prev, y_prev, x_out, x_trace, t, zero_y, zero_y_n, zero_w, zero_w_n);
+void launch_k1_p(const pi_layer* L, const K1Args& a, hipStream_t st) {
+  switch (pick(kK1Nch, chunks_of(L->d, L->p_dtype))) {
+    case 2: return launch_k1_t<PT, 2>(L, a, st);
+    case 4: return launch_k1_t<PT, 4>(L, a, st);
+    case 8: return launch_k1_t<PT, 8>(L, a, st);
+    case 16: return launch_k1_t<PT, 16>(L, a, st);
+    default: return launch_k1_t<PT, 24>(L, a, st);
+  }
 }
 
-void k1(const pi_layer* L, const float* x_prev, const double* y_prev, float* x_out, float* x_trace, float* t,
-        double* zero_y, int zero_y_n, uint32_t* zero_w, int zero_w_n, hipStream_t st) {
+void k1(const pi_layer* L, const K1Args& a, hipStream_t st) {
   if (L->p_dtype == PI_F32)
-    launch_k1<DT_F32>(L, x_prev, y_prev, x_out, x_trace, t, zero_y, zero_y_n, zero_w, zero_w_n, st);
+    launch_k1_p<DT_F32>(L, a, st);
   else
-    launch_k1<DT_F16>(L, x_prev, y_prev, x_out, x_trace, t, zero_y, zero_y_n, zero_w, zero_w_n, st);
+    launch_k1_p<DT_F16>(L, a, st);
 }
 
-template <int PT, int WT, int ACT, bool FUSE>
-void launch_k2_t(const pi_layer* L, const float* t, const float* xcur, float* scores, uint8_t* mask,
-                 uint32_t* bits, float* h, hipStream_t st) {
-  const int nb = k2_blocks(L->ffn);
+struct K2Args {
+  const float* t;
+  const float* xcur;
+  float* scores;
+  uint8_t* mask;
+  uint8_t* mask2;
+  int32_t* cnt;
+  float* h;
+};
+
+template <int PT, int WT, int ACT, bool FUSE, int PCH, int WCH>
+void launch_k2_t(const pi_layer* L, const K2Args& a, hipStream_t st) {
   const size_t lds = sizeof(float) * ((size_t)L->rank + (FUSE ? (size_t)L->d : 0));
-  hipLaunchKernelGGL((k_score<PT, WT, ACT, FUSE>), dim3(nb), dim3(kThreads), lds, st, L->B,
-                     L->pbias ? L->pbias : L->bias, L->bias, t, L->ffn,
-                     L->rank, L->gate.w, L->gate.scale, L->up.w, L->up.scale, xcur, L->d, scores, mask, bits, h);
+  hipLaunchKernelGGL((k_score<PT, WT, ACT, FUSE, PCH, WCH>), dim3(k2_blocks(L)), dim3(K2_WAVES * WAVE), lds, st,
+                     L->B, L->pbias ? L->pbias : L->bias, L->bias, a.t, L->ffn, L->rank, L->gate.w, L->gate.scale,
+                     L->up.w, L->up.scale, a.xcur, L->d, a.scores, a.mask, a.mask2, a.cnt, a.h);
 }
 
-template <int PT, bool FUSE>
-void launch_k2_w(const pi_layer* L, const float* t, const float* xcur, float* scores, uint8_t* mask,
-                 uint32_t* bits, float* h, hipStream_t st) {
+template <int PT, int WT, int ACT, int PCH>
+void launch_k2_fused(const pi_layer* L, const K2Args& a, hipStream_t st) {
+  const int wch = k2_wch(L);
+  if constexpr (WT == DT_F32) {
+    if (wch == 2) return launch_k2_t<PT, WT, ACT, true, PCH, 2>(L, a, st);
+    return launch_k2_t<PT, WT, ACT, true, PCH, 8>(L, a, st);
+  } else if constexpr (WT == DT_F16) {
+    if (wch == 2) return launch_k2_t<PT, WT, ACT, true, PCH, 2>(L, a, st);
+    if (wch == 8) return launch_k2_t<PT, WT, ACT, true, PCH, 8>(L, a, st);
+    if (wch == 14) return launch_k2_t<PT, WT, ACT, true, PCH, 14>(L, a, st);
+    return launch_k2_t<PT, WT, ACT, true, PCH, 16>(L, a, st);
+  } else {
+    if (wch == 1) return launch_k2_t<PT, WT, ACT, true, PCH, 1>(L, a, st);
+    return launch_k2_t<PT, WT, ACT, true, PCH, 6>(L, a, st);
+  }
+}
+
+template <int PT, int PCH>
+void launch_k2_p(const pi_layer* L, bool fuse, const K2Args& a, hipStream_t st) {
+  if (!fuse) return launch_k2_t<PT, DT_F32, ACT_RELU, false, PCH, 1>(L, a, st);
   const bool reglu = L->act == PI_REGLU;
   switch (L->w_dtype) {
     case PI_F32:
-      reglu ? launch_k2_t<PT, DT_F32, ACT_REGLU, FUSE>(L, t, xcur, scores, mask, bits, h, st)
-            : launch_k2_t<PT, DT_F32, ACT_RELU, FUSE>(L, t, xcur, scores, mask, bits, h, st);
-      break;
+      return reglu ? launch_k2_fused<PT, DT_F32, ACT_REGLU, PCH>(L, a, st)
+                   : launch_k2_fused<PT, DT_F32, ACT_RELU, PCH>(L, a, st);
     case PI_F16:
-      reglu ? launch_k2_t<PT, DT_F16, ACT_REGLU, FUSE>(L, t, xcur, scores, mask, bits, h, st)
-            : launch_k2_t<PT, DT_F16, ACT_RELU, FUSE>(L, t, xcur, scores, mask, bits, h, st);
-      break;
+      return reglu ? launch_k2_fused<PT, DT_F16, ACT_REGLU, PCH>(L, a, st)
+                   : launch_k2_fused<PT, DT_F16, ACT_RELU, PCH>(L, a, st);
     default:
-      reglu ? launch_k2_t<PT, DT_Q4, ACT_REGLU, FUSE>(L, t, xcur, scores, mask, bits, h, st)
-            : launch_k2_t<PT, DT_Q4, ACT_RELU, FUSE>(L, t, xcur, scores, mask, bits, h, st);
-      break;
+      return reglu ? launch_k2_fused<PT, DT_Q4, ACT_REGLU, PCH>(L, a, st)
+                   : launch_k2_fused<PT, DT_Q4, ACT_RELU, PCH>(L, a, st);
   }
 }
 
-void k2(const pi_layer* L, bool fuse_up, const float* t, const float* xcur, float* scores, uint8_t* mask,
-        uint32_t* bits, float* h, hipStream_t st) {
-  if (L->p_dtype == PI_F32) {
-    fuse_up ? launch_k2_w<DT_F32, true>(L, t, xcur, scores, mask, bits, h, st)
-            : launch_k2_w<DT_F32, false>(L, t, xcur, scores, mask, bits, h, st);
-  } else {
-    fuse_up ? launch_k2_w<DT_F16, true>(L, t, xcur, scores, mask, bits, h, st)
-            : launch_k2_w<DT_F16, false>(L, t, xcur, scores, mask, bits, h, st);
-  }
+void k2(const pi_layer* L, bool fuse_up, const K2Args& a, hipStream_t st) {
+  const bool p2 = k2_pch(L) == 2;
+  if (L->p_dtype == PI_F32)
+    p2 ? launch_k2_p<DT_F32, 2>(L, fuse_up, a, st) : launch_k2_p<DT_F32, 1>(L, fuse_up, a, st);
+  else
+    p2 ? launch_k2_p<DT_F16, 2>(L, fuse_up, a, st) : launch_k2_p<DT_F16, 1>(L, fuse_up, a, st);
+}
+
+struct K3Args {
+  const uint8_t* mask;       // implicit mode
+  const float* h_full;
+  const int32_t* idx;        // explicit mode
+  const int32_t* count;
+  const float* h_list;
+  float* y_part;             // [nc][d]
+  const int32_t* cnt_blk;    // per-block active counts to add up, or NULL
+  int n_cnt_blk;
+  int32_t* count_out;
+  int32_t* count_out2;
+};
+
+template <int WT, int TWC, bool EXPL>
+void launch_k3_t(const pi_layer* L, const K3Shape& sh, const K3Args& a, hipStream_t st) {
+  const int nblk = sh.ct * sh.nc;
+  const int xcd = (nblk % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((k_down<WT, TWC, EXPL>), dim3(nblk), dim3(K3_WAVES * WAVE), 0, st, L->downT.w,
+                     L->downT.scale, L->ffn, L->d, sh.ct, sh.nc, xcd, a.mask, a.h_full, a.idx, a.count, a.h_list,
+                     L->b_down, a.y_part, a.cnt_blk, a.n_cnt_blk, a.count_out, a.count_out2);
 }
 
 template <int WT, bool EXPL>
-void launch_k3_t(const pi_layer* L, const uint32_t* bits, const float* h_full, const int32_t* idx,
-                 const int32_t* count, const float* h_list, double* y_acc, int32_t* count_out, hipStream_t st) {
-  int CT, NC;
-  k3_shape(L->d, L->w_dtype, &CT, &NC);
-  const size_t lds = sizeof(float) * kWaves * WAVE * Tr<WT>::EPL;
-  hipLaunchKernelGGL((k_down<WT, EXPL>), dim3(CT * NC), dim3(kThreads), lds, st, L->downT.w, L->downT.scale,
-                     L->ffn, L->d, CT, bits, h_full, idx, count, h_list, L->b_down, y_acc, count_out);
+void launch_k3_w(const pi_layer* L, const K3Shape& sh, const K3Args& a, hipStream_t st) {
+  switch (sh.twc) {
+    case 1: return launch_k3_t<WT, 1, EXPL>(L, sh, a, st);
+    case 2: return launch_k3_t<WT, 2, EXPL>(L, sh, a, st);
+    case 4: return launch_k3_t<WT, 4, EXPL>(L, sh, a, st);
+    default: return launch_k3_t<WT, 8, EXPL>(L, sh, a, st);
+  }
 }
 
+// returns the number of partial vectors written
 template <bool EXPL>
-void k3(const pi_layer* L, const uint32_t* bits, const float* h_full, const int32_t* idx, const int32_t* count,
-        const float* h_list, double* y_acc, int32_t* count_out, hipStream_t st) {
+int k3(const pi_layer* L, const K3Args& a, hipStream_t st) {
+  const K3Shape sh = k3_shape(L->d, L->w_dtype);
   switch (L->w_dtype) {
-    case PI_F32: launch_k3_t<DT_F32, EXPL>(L, bits, h_full, idx, count, h_list, y_acc, count_out, st); break;
-    case PI_F16: launch_k3_t<DT_F16, EXPL>(L, bits, h_full, idx, count, h_list, y_acc, count_out, st); break;
-    default: launch_k3_t<DT_Q4, EXPL>(L, bits, h_full, idx, count, h_list, y_acc, count_out, st); break;
+    case PI_F32: launch_k3_w<DT_F32, EXPL>(L, sh, a, st); break;
+    case PI_F16: launch_k3_w<DT_F16, EXPL>(L, sh, a, st); break;
+    default: launch_k3_w<DT_Q4, EXPL>(L, sh, a, st); break;
   }
+  return sh.nc;
+}
+
+template <int WT, int ACT, int WCH>
+void launch_up_list_w(const pi_layer* L, const float* x, const int32_t* idx, const int32_t* count, float* h_list,
+                      hipStream_t st) {
+  const int nb = std::max(1, std::min(1024, cdiv(L->ffn, 4)));
+  hipLaunchKernelGGL((k_up_list<WT, ACT, WCH>), dim3(nb), dim3(kThreads), sizeof(float) * L->d, st, L->gate.w,
+                     L->gate.scale, L->up.w, L->up.scale, L->bias, x, L->d, L->ffn, idx, count, h_list);
 }
 
 template <int WT, int ACT>
 void launch_up_list_t(const pi_layer* L, const float* x, const int32_t* idx, const int32_t* count, float* h_list,
-                      double* y_acc, hipStream_t st) {
-  const int nb = std::max(1, std::min(512, (L->ffn + kWaves - 1) / kWaves));
-  hipLaunchKernelGGL((k_up_list<WT, ACT>), dim3(nb), dim3(kThreads), sizeof(float) * L->d, st, L->gate.w,
-                     L->gate.scale, L->up.w, L->up.scale, L->bias, x, L->d, L->ffn, idx, count, h_list, y_acc);
+                      hipStream_t st) {
+  const int wch = k2_wch(L);
+  if constexpr (WT == DT_F32) {
+    if (wch == 2) return launch_up_list_w<WT, ACT, 2>(L, x, idx, count, h_list, st);
+    return launch_up_list_w<WT, ACT, 8>(L, x, idx, count, h_list, st);
+  } else if constexpr (WT == DT_F16) {
+    if (wch == 2) return launch_up_list_w<WT, ACT, 2>(L, x, idx, count, h_list, st);
+    if (wch == 8) return launch_up_list_w<WT, ACT, 8>(L, x, idx, count, h_list, st);
+    if (wch == 14) return launch_up_list_w<WT, ACT, 14>(L, x, idx, count, h_list, st);
+    return launch_up_list_w<WT, ACT, 16>(L, x, idx, count, h_list, st);
+  } else {
+    if (wch == 1) return launch_up_list_w<WT, ACT, 1>(L, x, idx, count, h_list, st);
+    return launch_up_list_w<WT, ACT, 6>(L, x, idx, count, h_list, st);
+  }
 }
 
 void up_list(const pi_layer* L, const float* x, const int32_t* idx, const int32_t* count, float* h_list,
-             double* y_acc, hipStream_t st) {
+             hipStream_t st) {
   const bool reglu = L->act == PI_REGLU;
   switch (L->w_dtype) {
     case PI_F32:
-      reglu ? launch_up_list_t<DT_F32, ACT_REGLU>(L, x, idx, count, h_list, y_acc, st)
-            : launch_up_list_t<DT_F32, ACT_RELU>(L, x, idx, count, h_list, y_acc, st);
+      reglu ? launch_up_list_t<DT_F32, ACT_REGLU>(L, x, idx, count, h_list, st)
+            : launch_up_list_t<DT_F32, ACT_RELU>(L, x, idx, count, h_list, st);
       break;
     case PI_F16:
-      reglu ? launch_up_list_t<DT_F16, ACT_REGLU>(L, x, idx, count, h_list, y_acc, st)
-            : launch_up_list_t<DT_F16, ACT_RELU>(L, x, idx, count, h_list, y_acc, st);
+      reglu ? launch_up_list_t<DT_F16, ACT_REGLU>(L, x, idx, count, h_list, st)
+            : launch_up_list_t<DT_F16, ACT_RELU>(L, x, idx, count, h_list, st);
       break;
     default:
-      reglu ? launch_up_list_t<DT_Q4, ACT_REGLU>(L, x, idx, count, h_list, y_acc, st)
-            : launch_up_list_t<DT_Q4, ACT_RELU>(L, x, idx, count, h_list, y_acc, st);
+      reglu ? launch_up_list_t<DT_Q4, ACT_REGLU>(L, x, idx, count, h_list, st)
+            : launch_up_list_t<DT_Q4, ACT_RELU>(L, x, idx, count, h_list, st);
       break;
   }
 }
@@ -276,12 +407,11 @@ pi_status pi_predict(const pi_layer* layer, const float* x, int32_t batch, float
   const WsLayout WL = layout(D, batch);
   if (!ws || ws_bytes < WL.total || !aligned(ws, kAlign)) return PI_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  Ws W = carve(ws, WL, D, batch);
-  const int nwords = (layer->ffn + 31) / 32;
+  Ws W = carve(ws, WL);
   (void)hipGetLastError();
-  k1(layer, x, nullptr, nullptr, nullptr, W.t, nullptr, 0, W.bits, nwords, st);
-  k2(layer, false, W.t, nullptr, scores, mask, W.bits, nullptr, st);
-  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.bits, layer->ffn, idx, count);
+  k1(layer, K1Args{x, nullptr, 0, nullptr, nullptr, W.t}, st);
+  k2(layer, false, K2Args{W.t, nullptr, scores, W.mask, mask, nullptr, nullptr}, st);
+  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, layer->ffn, idx, count);
   return launch_status();
 }
 
@@ -297,11 +427,12 @@ pi_status pi_sparse_ffn(const pi_layer* layer, const float* x, int32_t batch, co
   const WsLayout WL = layout(D, batch);
   if (!ws || ws_bytes < WL.total || !aligned(ws, kAlign)) return PI_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  Ws W = carve(ws, WL, D, batch);
+  Ws W = carve(ws, WL);
   (void)hipGetLastError();
-  up_list(layer, x, idx, count, W.h, W.y[0], st);
-  k3<true>(layer, nullptr, nullptr, idx, count, W.h, W.y[0], nullptr, st);
-  hipLaunchKernelGGL(k_finalize, dim3((layer->d + 255) / 256), dim3(256), 0, st, W.y[0], y, layer->d);
+  up_list(layer, x, idx, count, W.h, st);
+  const int np = k3<true>(layer, K3Args{nullptr, nullptr, idx, count, W.h, W.y[0], nullptr, 0, nullptr, nullptr},
+                          st);
+  hipLaunchKernelGGL(k_finalize, dim3(cdiv(layer->d, 256)), dim3(256), 0, st, W.y[0], np, y, layer->d);
   return launch_status();
 }
 
@@ -318,30 +449,29 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
   const WsLayout WL = layout(D, batch);
   if (!ws || ws_bytes < WL.total || !aligned(ws, kAlign)) return PI_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  Ws W = carve(ws, WL, D, batch);
+  Ws W = carve(ws, WL);
   (void)hipGetLastError();
+  int np_prev = 0;
   for (int l = 0; l < n_layers; ++l) {
     const pi_layer* L = &layers[l];
     const pi_trace* tr = trace ? &trace[l] : nullptr;
     const int cur = l & 1, prv = cur ^ 1;
-    const float* x_prev = l == 0 ? x : W.x[prv];
-    const double* y_prev = l == 0 ? nullptr : W.y[prv];
-    const int nwords = (L->ffn + 31) / 32;
-    k1(L, x_prev, y_prev, W.x[cur], tr ? tr->x_in : nullptr, W.t, W.y[cur], L->d, W.bits, nwords, st);
-    k2(L, true, W.t, W.x[cur], tr ? tr->scores : nullptr, tr ? tr->mask : nullptr, W.bits, W.h, st);
-    if (tr && tr->idx) {
-      // list for the record only; the down projection reads the mask bits directly
-      hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.bits, L->ffn, tr->idx,
+    k1(L, K1Args{l == 0 ? x : W.x[prv], l == 0 ? nullptr : W.y[prv], np_prev, W.x[cur], tr ? tr->x_in : nullptr,
+                 W.t}, st);
+    k2(L, true, K2Args{W.t, W.x[cur], tr ? tr->scores : nullptr, W.mask, tr ? tr->mask : nullptr, W.cnt, W.h},
+       st);
+    int32_t* c1 = counts ? counts + l : nullptr;
+    int32_t* c2 = (tr && tr->count && !tr->idx) ? tr->count : nullptr;
+    if (tr && tr->idx)   // ascending list for the record; the down projection reads the mask bytes directly
+      hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, tr->idx,
                          tr->count ? tr->count : W.misc);
-    }
-    const bool tr_cnt = tr && tr->count && !tr->idx;   // count record without a list
-    int32_t* cnt_out = counts ? counts + l : (tr_cnt ? tr->count : nullptr);
-    k3<false>(L, W.bits, W.h, nullptr, nullptr, nullptr, W.y[cur], cnt_out, st);
-    if (counts && tr_cnt) hipLaunchKernelGGL(k_copy_i32, dim3(1), dim3(64), 0, st, counts + l, tr->count, 1);
+    np_prev = k3<false>(L, K3Args{W.mask, W.h, nullptr, nullptr, nullptr, W.y[cur], W.cnt, k2_blocks(L), c1, c2},
+                        st);
   }
   {
     const int last = (n_layers - 1) & 1;
-    hipLaunchKernelGGL(k_glue_out, dim3(1), dim3(256), sizeof(float) * D.d, st, W.x[last], W.y[last], out, D.d);
+    hipLaunchKernelGGL(k_glue_out, dim3(1), dim3(256), sizeof(float) * D.d, st, W.x[last], W.y[last], np_prev,
+                       out, D.d);
   }
   return launch_status();
 }

@@ -1,25 +1,31 @@
 // Device code of the predictor-guided, neuron-aware sparse FFN for gfx950 (MI355X).
 //
 // Execution model (batch 1): one HIP stream, three kernels per layer, no
-// inter-block waiting anywhere (a grid-wide barrier on this GPU costs an order
-// of magnitude more than a kernel boundary in a HIP graph):
+// inter-block waiting and no global atomics anywhere (on this GPU a grid-wide
+// barrier costs far more than a kernel boundary in a HIP graph, and a kernel
+// that issues device-scope atomics pays their full round trip before it can
+// retire):
 //   K1 k_predict_t  residual RMS glue (recomputed identically by every block)
 //                   and the predictor's first GEMV t = A x
-//   K2 k_score      predictor second GEMV s = B t + b, threshold s > 0, mask
-//                   bits, and -- fused -- the gathered up/gate GEMV with ReLU or
-//                   ReGLU for the block's active neurons (h per neuron)
-//   K3 k_down       down projection over active neurons, tiled by column tile x
-//                   neuron sub-chunk; each wave walks its neurons in ascending
-//                   order (ballot over the mask bits), the block reduces its
-//                   waves in a fixed order and adds one fp64 value per column
+//   K2 k_score      predictor second GEMV s = B t + c, threshold s > 0, one mask
+//                   byte per neuron, and -- fused -- the gathered up/gate GEMV
+//                   with ReLU or ReGLU for the active neurons (h per neuron)
+//   K3 k_down       down projection over the active neurons; each block owns a
+//                   column tile (and one of NC neuron splits), builds its list
+//                   of active neurons from the mask bytes in LDS, gathers their
+//                   row segments and writes its partial y with plain stores;
+//                   the consumer adds the NC partials in a fixed order
 //
-// Loads are 16 bytes per lane (4 fp32, 8 fp16 or one Q4_0 block of 32 nibbles)
-// so that a wave reads 1 KiB contiguous per instruction; vectors that every
-// row meets (x, t) are staged in LDS.  Cross-lane sums are butterflies, so
-// every lane ends with the same bits and decisions are wave-uniform.
+// Weight loads are 16 bytes per lane (4 fp32, 8 fp16 or one Q4_0 block of 32
+// nibbles).  Every batch of loads is issued unconditionally (indices clamped
+// to valid addresses, surplus results masked) and fenced from its uses, so a
+// wave has a whole batch in flight per HBM round trip.  Cross-lane sums are
+// butterflies in a fixed order, so results are bit-reproducible.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace pik {
 
@@ -28,6 +34,12 @@ enum { ACT_RELU = 0, ACT_REGLU = 1 };
 
 constexpr int WAVE = 64;
 
+// Keeps the instruction scheduler from moving instructions across this point.
+// Placed after a batch of loads so that the whole batch is issued before the
+// first use of any of it: left alone, the scheduler interleaves load, wait and
+// use to save registers, which turns one memory round trip into many.
+#define PI_ISSUE_FENCE() __builtin_amdgcn_sched_barrier(0)
+
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
 template <int DT> struct Tr;
@@ -35,10 +47,71 @@ template <> struct Tr<DT_F32> { static constexpr int EPL = 4; };   // elements p
 template <> struct Tr<DT_F16> { static constexpr int EPL = 8; };
 template <> struct Tr<DT_Q4>  { static constexpr int EPL = 32; };
 
-__device__ __forceinline__ float wave_sum(float v) {
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+// Wave-uniform lane read (v_readlane): the value of `v` in lane `l`.
+__device__ __forceinline__ int lane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Cross-lane moves through DPP (a VALU operand modifier, no LDS round trip).
+// Lanes whose source is outside the row, and rows not in ROW_MASK, read 0.
+//   0x111..0x11F  row_shr:1..15  (lane i reads lane i-n of its 16-lane row)
+//   0x142         row_bcast:15   (lane 15 of each row feeds the next row)
+//   0x143         row_bcast:31   (lane 31 feeds rows 2 and 3)
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele inside each row, then
+// the row totals carried across rows).  The order of additions is fixed.
+__device__ __forceinline__ float wave_scan(float x) {
+  x += dpp_f<0x111>(x);
+  x += dpp_f<0x112>(x);
+  x += dpp_f<0x114>(x);
+  x += dpp_f<0x118>(x);
+  x += dpp_f<0x142, 0xa>(x);
+  x += dpp_f<0x143, 0xc>(x);
+  return x;
+}
+__device__ __forceinline__ int wave_scan(int x) {
+  x += dpp_i<0x111>(x);
+  x += dpp_i<0x112>(x);
+  x += dpp_i<0x114>(x);
+  x += dpp_i<0x118>(x);
+  x += dpp_i<0x142, 0xa>(x);
+  x += dpp_i<0x143, 0xc>(x);
+  return x;
+}
+
+// Sum over the wave, the same wave-uniform value in every lane.
+__device__ __forceinline__ float wave_sum(float v) { return lane_f(wave_scan(v), WAVE - 1); }
+__device__ __forceinline__ int wave_sum(int v) { return lane_i(wave_scan(v), WAVE - 1); }
+
+// Sum over the lanes that share lane % G (G = 1, 2, 4, 8 or 16): a scan with
+// row shifts that are multiples of G inside each 16-lane row, then the four
+// row totals (lanes 16 r + 16 - G + q) added in row order.  The result for
+// residue q is wave-uniform; `res` holds it for q = lane % G.
+template <int G>
+__device__ __forceinline__ float group_sum(float x, int lane) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "bad group");
+  if constexpr (G <= 1) x += dpp_f<0x111>(x);
+  if constexpr (G <= 2) x += dpp_f<0x110 + 2>(x);
+  if constexpr (G <= 4) x += dpp_f<0x110 + 4>(x);
+  if constexpr (G <= 8) x += dpp_f<0x110 + 8>(x);
+  float res = 0.f;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
-  return v;
+  for (int q = 0; q < G; ++q) {
+    const float t = lane_f(x, 16 - G + q) + lane_f(x, 32 - G + q) + lane_f(x, 48 - G + q) + lane_f(x, 64 - G + q);
+    if ((lane % G) == q) res = t;
+  }
+  return res;
 }
 
 // 16-byte chunk of row `row` starting at element `e` (a multiple of EPL).
@@ -128,56 +201,179 @@ __device__ __forceinline__ void chunk_axpy(uint4 c, float scale, float h, float*
   }
 }
 
-// Row `row` of a [rows][n] matrix dotted with the LDS vector xs[n]; full wave sum.
-template <int DT>
-__device__ __forceinline__ float row_dot(const void* __restrict__ w, const uint16_t* __restrict__ sc,
-                                         size_t row, int n, const float* __restrict__ xs, int lane) {
-  constexpr int EPL = Tr<DT>::EPL;
-  float a = 0.f;
-#pragma unroll 4
-  for (int e = lane * EPL; e < n; e += WAVE * EPL) {
-    const uint4 c = ld_chunk<DT>(w, row, n, e);
-    const float s = (DT == DT_Q4) ? ld_scale(sc, row, n, e) : 1.f;
-    a += chunk_dot<DT>(c, s, xs + e);
+// Copy n floats (n % 4 == 0, both pointers 16-byte aligned) from global memory
+// to LDS, starting at float4 index `first`.  A thread issues all MAXV 16-byte
+// loads of a round before the first store; indices past the end are clamped to
+// the last vector, which is then loaded and stored twice with the same value,
+// so no load sits in a branch (a load in a branch is sunk next to its use and
+// the batch is lost).
+template <int MAXV>
+__device__ __forceinline__ void stage_f32(float* __restrict__ lds, const float* __restrict__ g, int n, int tid,
+                                          int nthr, int first = 0) {
+  const int nv = n / 4;
+  for (int base = first; base < nv; base += MAXV * nthr) {
+    float4 v[MAXV];
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) v[j] = reinterpret_cast<const float4*>(g)[min(base + j * nthr + tid, nv - 1)];
+    PI_ISSUE_FENCE();
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) reinterpret_cast<float4*>(lds)[min(base + j * nthr + tid, nv - 1)] = v[j];
   }
-  return wave_sum(a);
+}
+
+// The two halves of stage_f32's first round, so that other loads can be
+// issued between them.
+template <int MAXV>
+__device__ __forceinline__ void load_f32(float4 (&v)[MAXV], const float* __restrict__ g, int n, int tid, int nthr) {
+  const int nv = n / 4;
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) v[j] = reinterpret_cast<const float4*>(g)[min(j * nthr + tid, nv - 1)];
+}
+template <int MAXV>
+__device__ __forceinline__ void store_f32(float* __restrict__ lds, const float4 (&v)[MAXV], int n, int tid,
+                                          int nthr) {
+  const int nv = n / 4;
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) reinterpret_cast<float4*>(lds)[min(j * nthr + tid, nv - 1)] = v[j];
+}
+
+// v = x + sum_{p < np} y[p] (np <= 4 partial vectors of n floats, added in the
+// order p = 0, 1, ...) into LDS, returning this thread's sum of v^2 over its
+// elements in a fixed order (the same in every block).  np == 0: v = x.
+template <int MAXV>
+__device__ __forceinline__ float stage_residual(float* __restrict__ lds, const float* __restrict__ x,
+                                                const float* __restrict__ y, int np, int n, int tid, int nthr) {
+  const int nv = n / 4;
+  float ss = 0.f;
+  for (int base = 0; base < nv; base += MAXV * nthr) {
+    float4 xv[MAXV], yv[4][MAXV];
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      const int k = min(base + j * nthr + tid, nv - 1);
+      xv[j] = reinterpret_cast<const float4*>(x)[k];
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        if (p < np) yv[p][j] = reinterpret_cast<const float4*>(y + (size_t)p * n)[k];
+    }
+    PI_ISSUE_FENCE();
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      const int kr = base + j * nthr + tid;
+      float4 v = xv[j];
+      if (np > 0) {
+        float4 y4 = yv[0][j];
+#pragma unroll
+        for (int p = 1; p < 4; ++p) {
+          if (p < np) {
+            y4.x += yv[p][j].x;
+            y4.y += yv[p][j].y;
+            y4.z += yv[p][j].z;
+            y4.w += yv[p][j].w;
+          }
+        }
+        v.x += y4.x;
+        v.y += y4.y;
+        v.z += y4.z;
+        v.w += y4.w;
+      }
+      reinterpret_cast<float4*>(lds)[min(kr, nv - 1)] = v;
+      if (kr < nv) {
+        ss = fmaf(v.x, v.x, ss);
+        ss = fmaf(v.y, v.y, ss);
+        ss = fmaf(v.z, v.z, ss);
+        ss = fmaf(v.w, v.w, ss);
+      }
+    }
+  }
+  return ss;
+}
+
+// Dot products of rows rows[0..NN) of NMAT matrices (NMAT = 2: gate, up) with
+// the LDS vector xs[d]: all NN * NMAT * NCH chunk loads of a round are issued
+// before the first multiply, one HBM round trip per round.  z[n][m] is row
+// rows[n] of matrix m dotted with xs, in every lane.  Chunks past the row
+// (ragged tail, or beyond the row's chunk count) load a clamped, valid address
+// and are masked out of the sum.
+template <int WT, int NCH, int NMAT, int NN>
+__device__ __forceinline__ void gather_rows(const void* __restrict__ w0, const uint16_t* __restrict__ s0,
+                                            const void* __restrict__ w1, const uint16_t* __restrict__ s1,
+                                            const int (&rows)[NN], int d, const float* __restrict__ xs, int lane,
+                                            float (&z)[NN][NMAT]) {
+  constexpr int EPL = Tr<WT>::EPL, TW = WAVE * EPL, NV = NN * NMAT;
+  const int nch = (d + TW - 1) / TW;
+  float a[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) a[v] = 0.f;
+  for (int q0 = 0; q0 < nch; q0 += NCH) {
+    uint4 c[NV][NCH];
+    float fs[NV][NCH];
+#pragma unroll
+    for (int n = 0; n < NN; ++n)
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int q = 0; q < NCH; ++q) {
+          const int e = min(min(q0 + q, nch - 1) * TW + lane * EPL, d - EPL);
+          c[n * NMAT + m][q] = ld_chunk<WT>(m ? w1 : w0, (size_t)rows[n], d, e);
+          fs[n * NMAT + m][q] = (WT == DT_Q4) ? ld_scale(m ? s1 : s0, (size_t)rows[n], d, e) : 1.f;
+        }
+    PI_ISSUE_FENCE();
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      const int e = (q0 + q) * TW + lane * EPL;
+      const bool ok = (q0 + q < nch) && (e < d);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const float p = chunk_dot<WT>(c[v][q], fs[v][q], xs + (ok ? e : 0));
+        a[v] += ok ? p : 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < NV; ++v) z[v / NMAT][v % NMAT] = wave_sum(a[v]);
 }
 
 // ----------------------------------------------------------------------- K1
-// t = A x', x' = glue(x_prev, y_prev) if y_prev != NULL else x_prev.
-// glue: v = x_prev + y_prev; x' = v / sqrt(mean(v^2) + 1e-6).  Every block
-// computes the same x' with the same operation order, so all blocks agree
-// bit for bit.  Blocks also write their slice of x' and clear their slice of
-// the next layer's accumulators.
-template <int PT>
+// t = A x', x' = glue(x_prev, y_prev) if y_np > 0 else x_prev, with glue
+// v = x_prev + y_prev, x' = v / sqrt(mean(v^2) + 1e-6) and y_prev given as y_np
+// partial vectors that are added in order.  One wave per row of A; the wave
+// issues the loads of its row (NCH chunks per lane per round) before the block
+// computes x', so the glue hides under the HBM latency.  Every block computes
+// the same x' with the same operation order, so all agree bit for bit.
+// Blocks also write their slice of x'.
+constexpr int K1_WAVES = 4;
+
+template <int PT, int NCH>
 __global__ void __launch_bounds__(256)
 k_predict_t(const void* __restrict__ A, int r, int d, const float* __restrict__ x_prev,
-            const double* __restrict__ y_prev, float* __restrict__ x_out, float* __restrict__ x_trace,
-            float* __restrict__ t, double* __restrict__ zero_y, int zero_y_n,
-            uint32_t* __restrict__ zero_w, int zero_w_n) {
+            const float* __restrict__ y_prev, int y_np, float* __restrict__ x_out, float* __restrict__ x_trace,
+            float* __restrict__ t) {
   extern __shared__ float xs[];
-  __shared__ float red[16];
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE, W = blockDim.x / WAVE;
+  __shared__ float red[K1_WAVES];
+  constexpr int EPL = Tr<PT>::EPL, TW = WAVE * EPL;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const int row = blockIdx.x * K1_WAVES + w;
+  const size_t rowc = (size_t)min(row, r - 1);       // a wave without a row reads row r-1 and discards it
+  const int nch = (d + TW - 1) / TW;
 
-  float ss = 0.f;
-  for (int k = tid; k < d; k += blockDim.x) {
-    float v = x_prev[k];
-    if (y_prev) v += (float)y_prev[k];
-    xs[k] = v;
-    ss = fmaf(v, v, ss);
-  }
-  if (y_prev) {
+  uint4 c[NCH];
+#pragma unroll
+  for (int q = 0; q < NCH; ++q) c[q] = ld_chunk<PT>(A, rowc, d, min(min(q, nch - 1) * TW + lane * EPL, d - EPL));
+  PI_ISSUE_FENCE();
+
+  float ss = stage_residual<4>(xs, x_prev, y_prev, y_np, d, tid, blockDim.x);
+  if (y_np > 0) {
     ss = wave_sum(ss);
     if (lane == 0) red[w] = ss;
     __syncthreads();
     float tot = 0.f;
-    for (int i = 0; i < W; ++i) tot += red[i];
+#pragma unroll
+    for (int i = 0; i < K1_WAVES; ++i) tot += red[i];
     const float inv = 1.0f / sqrtf(tot / (float)d + 1e-6f);
     for (int k = tid; k < d; k += blockDim.x) xs[k] *= inv;
   }
   __syncthreads();
 
-  // slices: x' out, trace, zeroing
   {
     const int nb = gridDim.x, b = blockIdx.x;
     const int cx = (d + nb - 1) / nb;
@@ -185,283 +381,407 @@ k_predict_t(const void* __restrict__ A, int r, int d, const float* __restrict__ 
       if (x_out) x_out[k] = xs[k];
       if (x_trace) x_trace[k] = xs[k];
     }
-    if (zero_y) {
-      const int cy = (zero_y_n + nb - 1) / nb;
-      for (int k = b * cy + tid; k < min(zero_y_n, (b + 1) * cy); k += blockDim.x) zero_y[k] = 0.0;
-    }
-    if (zero_w) {
-      const int cw = (zero_w_n + nb - 1) / nb;
-      for (int k = b * cw + tid; k < min(zero_w_n, (b + 1) * cw); k += blockDim.x) zero_w[k] = 0u;
-    }
   }
 
-  for (int j = blockIdx.x * W + w; j < r; j += gridDim.x * W) {
-    const float a = row_dot<PT>(A, nullptr, (size_t)j, d, xs, lane);
-    if (lane == 0) t[j] = a;
+  float a = 0.f;
+#pragma unroll
+  for (int q = 0; q < NCH; ++q) {
+    const int e = q * TW + lane * EPL;
+    const bool ok = q < nch && e < d;
+    const float p = chunk_dot<PT>(c[q], 1.f, xs + (ok ? e : 0));
+    a += ok ? p : 0.f;
   }
+  for (int q0 = NCH; q0 < nch; q0 += NCH) {            // rows longer than NCH chunks per lane
+#pragma unroll
+    for (int q = 0; q < NCH; ++q)
+      c[q] = ld_chunk<PT>(A, rowc, d, min(min(q0 + q, nch - 1) * TW + lane * EPL, d - EPL));
+    PI_ISSUE_FENCE();
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      const int e = (q0 + q) * TW + lane * EPL;
+      const bool ok = q0 + q < nch && e < d;
+      const float p = chunk_dot<PT>(c[q], 1.f, xs + (ok ? e : 0));
+      a += ok ? p : 0.f;
+    }
+  }
+  a = wave_sum(a);
+  if (row < r && lane == 0) t[row] = a;
 }
 
 // ----------------------------------------------------------------------- K2
-// Block b owns neurons i = b + gridDim.x * m (interleaved, so that hot-first
-// order does not load the first blocks more than the last).  Scores for all
-// of them, then -- if FUSE_UP -- the up/gate dot products of the active ones.
-constexpr int K2_MAX_PER_BLOCK = 256;
+// Scores s_i = c_i + B[i] . t, threshold s_i > 0, one mask byte per neuron,
+// and -- if FUSE -- the gathered up/gate GEMV with ReLU or ReGLU for the active
+// neurons.  Global wave g owns neurons i = g + NW m (interleaved, so the
+// hot-first order spreads the frequently active rows over all waves).  A wave
+// loads RB = 16 / PCH rows of B (PCH 16-byte chunks per lane each) before its
+// first multiply and reduces the RB dot products with one transposed
+// butterfly.  The block's active neurons then go to a list in LDS and its
+// waves take them two at a time (gate and up rows of both, WCH chunks per lane
+// per row, in one HBM round trip): the number of actives per wave varies a
+// lot, per block much less, and the slowest wave sets the kernel's time.
+// The block's active count goes to cnt_blk[block] (summed over batches).
+// Global stores come after the block barrier so that the barrier does not wait
+// for them.
+constexpr int K2_WAVES = 4;
 
-template <int PT, int WT, int ACT, bool FUSE_UP>
-__global__ void __launch_bounds__(256)
+template <int PT, int WT, int ACT, bool FUSE, int PCH, int WCH>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const float* __restrict__ bias,
         const float* __restrict__ t, int f, int r,
         const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc,
         const void* __restrict__ up_w, const uint16_t* __restrict__ up_sc,
         const float* __restrict__ xcur, int d,
-        float* __restrict__ scores, uint8_t* __restrict__ mask_u8,
-        uint32_t* __restrict__ mask_bits, float* __restrict__ h_full) {
+        float* __restrict__ scores, uint8_t* __restrict__ mask, uint8_t* __restrict__ mask2,
+        int32_t* __restrict__ cnt_blk, float* __restrict__ h_full) {
+  constexpr int RB = 16 / PCH;                               // rows of B per batch
+  constexpr int PEPL = Tr<PT>::EPL, PTW = WAVE * PEPL;
   extern __shared__ float smem[];
-  float* ts = smem;        // [r]
-  float* xs = smem + r;    // [d] (FUSE_UP only)
-  __shared__ int act_list[K2_MAX_PER_BLOCK];
-  __shared__ int n_act;
-  constexpr int PEPL = Tr<PT>::EPL;
-  constexpr int U = 4;
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE, W = blockDim.x / WAVE;
-  const int NB = gridDim.x, b = blockIdx.x;
+  float* ts = smem;          // [r]
+  float* xs = smem + r;      // [d] (FUSE only)
+  // per-batch active lists and counters, three in rotation: batch b appends to
+  // slot b % 3 before its barrier and reads it after; slot (b + 2) % 3, last
+  // read before barrier b by every wave, is cleared after it for batch b + 2
+  __shared__ int act[3][K2_WAVES * RB];
+  __shared__ int nact[3];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const int NW = gridDim.x * K2_WAVES, g = blockIdx.x * K2_WAVES + w;
+  const int M = g < f ? (f - 1 - g) / NW + 1 : 0;            // neurons of this wave
+  const int g0 = blockIdx.x * K2_WAVES;                      // the block's first wave has the most
+  const int Mb = g0 < f ? (f - 1 - g0) / NW + 1 : 0;         // block-uniform trip count
+  const int pch = (r + PTW - 1) / PTW;
+  const int my_u = min(lane, RB - 1);                        // lane u < RB reports row u of the batch
+  if (tid < 3) nact[tid] = 0;
 
-  for (int k = tid; k < r; k += blockDim.x) ts[k] = t[k];
-  if (tid == 0) n_act = 0;
+  // Rows past the wave's last neuron (all rows, for a wave without neurons)
+  // and chunks past the row end load a clamped, valid address and are
+  // discarded; no load sits in a branch.
+  uint4 bc[RB][PCH];
+  float pb = 0.f;
+  auto nrow = [&](int m) __attribute__((always_inline)) { return min(g + NW * max(min(m, M - 1), 0), f - 1); };
+  auto issue = [&](int m0, int q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const size_t row = (size_t)nrow(m0 + u);
+#pragma unroll
+      for (int q = 0; q < PCH; ++q)
+        bc[u][q] = ld_chunk<PT>(Bm, row, r, min(min(q0 + q, pch - 1) * PTW + lane * PEPL, r - PEPL));
+    }
+    if (q0 == 0) pb = pbias[nrow(m0 + my_u)];
+    PI_ISSUE_FENCE();
+  };
+
+  // t and x' are staged in LDS; their first rounds are issued unconditionally
+  // ahead of the rows of B, longer vectors finish after
+  const int nthr = blockDim.x;
+  float4 tv[1], xv[8];
+  load_f32<1>(tv, t, r, tid, nthr);
+  if constexpr (FUSE) load_f32<8>(xv, xcur, d, tid, nthr);
+  PI_ISSUE_FENCE();
+  issue(0, 0);
+  store_f32<1>(ts, tv, r, tid, nthr);
+  if constexpr (FUSE) store_f32<8>(xs, xv, d, tid, nthr);
+  if (r > 4 * nthr) stage_f32<4>(ts, t, r, tid, nthr, nthr);
+  if (FUSE && d > 32 * nthr) stage_f32<8>(xs, xcur, d, tid, nthr, 8 * nthr);
   __syncthreads();
 
-  const int M = (f - b + NB - 1) / NB;   // neurons of this block (b < f)
-  for (int m0 = w; m0 < M; m0 += W * U) {
-    float acc[U];
+  int block_count = 0;
+  for (int m0 = 0, batch = 0; m0 < Mb; m0 += RB, ++batch) {
+    float acc[RB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc[u] = 0.f;
-    for (int e = lane * PEPL; e < r; e += WAVE * PEPL) {
-      uint4 c[U];
+    for (int u = 0; u < RB; ++u) acc[u] = 0.f;
+    for (int q0 = 0; q0 < pch; q0 += PCH) {
+      if (q0 > 0) issue(m0, q0);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int m = m0 + u * W;
-        if (m < M) c[u] = ld_chunk<PT>(Bm, (size_t)b + (size_t)NB * m, r, e);
-      }
+      for (int u = 0; u < RB; ++u) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int m = m0 + u * W;
-        if (m < M) acc[u] += chunk_dot<PT>(c[u], 1.f, ts + e);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int m = m0 + u * W;
-      if (m < M) {
-        const int i = b + NB * m;
-        const float s = wave_sum(acc[u]) + pbias[i];
-        const bool on = s > 0.f;
-        if (lane == 0) {
-          if (scores) scores[i] = s;
-          if (mask_u8) mask_u8[i] = on ? 1 : 0;
-          if (on) {
-            atomicOr(&mask_bits[i >> 5], 1u << (i & 31));
-            if constexpr (FUSE_UP) act_list[atomicAdd(&n_act, 1)] = i;
-          }
+        for (int q = 0; q < PCH; ++q) {
+          const int e = (q0 + q) * PTW + lane * PEPL;
+          const bool ok = q0 + q < pch && e < r;
+          const float p = chunk_dot<PT>(bc[u][q], 1.f, ts + (ok ? e : 0));
+          acc[u] += ok ? p : 0.f;
         }
       }
     }
-  }
-  if constexpr (FUSE_UP) {
-    __syncthreads();
-    const int na = n_act;
-    if (na == 0) return;
-    for (int k = tid; k < d; k += blockDim.x) xs[k] = xcur[k];
-    __syncthreads();
-    for (int a = w; a < na; a += W) {
-      const int i = act_list[a];
-      const float zu = row_dot<WT>(up_w, up_sc, (size_t)i, d, xs, lane);
-      float h;
-      if constexpr (ACT == ACT_RELU) {
-        h = fmaxf(zu + bias[i], 0.f);
-      } else {
-        const float zg = row_dot<WT>(gate_w, gate_sc, (size_t)i, d, xs, lane);
-        h = fmaxf(zg + bias[i], 0.f) * zu;
-      }
-      if (lane == 0) h_full[i] = h;
+    float dot = 0.f;
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const float su = wave_sum(acc[u]);
+      if (lane == u) dot = su;
     }
+    const int m = m0 + my_u;
+    const bool rep = lane < RB && m < M;
+    const int i = g + NW * m;
+    const float s = dot + pb;
+    const bool on = rep && s > 0.f;
+
+    const int par = batch % 3;
+    if (on) act[par][atomicAdd(&nact[par], 1)] = i;          // LDS atomic
+    __syncthreads();
+    const int n = nact[par];
+    if (tid == 0) {
+      nact[(batch + 2) % 3] = 0;
+      block_count += n;
+    }
+    if (rep) {
+      if (scores) scores[i] = s;
+      mask[i] = on ? 1 : 0;
+      if (mask2) mask2[i] = on ? 1 : 0;
+    }
+    if constexpr (FUSE) {
+      constexpr int NMAT = (ACT == ACT_RELU) ? 1 : 2;
+      const void* w0 = (ACT == ACT_RELU) ? up_w : gate_w;
+      const uint16_t* s0 = (ACT == ACT_RELU) ? up_sc : gate_sc;
+      // wave w takes entries w, w + 4 (a pair when both exist and the pair's
+      // rows fit the registers), then w + 8, w + 12, ...
+      constexpr bool PAIR = NMAT * WCH <= 16;
+      for (int a = w; a < n; a += (PAIR ? 2 : 1) * K2_WAVES) {
+        if (PAIR && a + K2_WAVES < n) {
+          const int rows[2] = {act[par][a], act[par][a + K2_WAVES]};
+          const float b0 = bias[rows[0]], b1 = bias[rows[1]];
+          float z[2][NMAT];
+          gather_rows<WT, WCH, NMAT, 2>(w0, s0, up_w, up_sc, rows, d, xs, lane, z);
+          if (lane == 0) {
+            h_full[rows[0]] = (ACT == ACT_RELU) ? fmaxf(z[0][0] + b0, 0.f) : fmaxf(z[0][0] + b0, 0.f) * z[0][NMAT - 1];
+            h_full[rows[1]] = (ACT == ACT_RELU) ? fmaxf(z[1][0] + b1, 0.f) : fmaxf(z[1][0] + b1, 0.f) * z[1][NMAT - 1];
+          }
+        } else {
+          const int rows[1] = {act[par][a]};
+          const float b0 = bias[rows[0]];
+          float z[1][NMAT];
+          gather_rows<WT, WCH, NMAT, 1>(w0, s0, up_w, up_sc, rows, d, xs, lane, z);
+          if (lane == 0)
+            h_full[rows[0]] = (ACT == ACT_RELU) ? fmaxf(z[0][0] + b0, 0.f) : fmaxf(z[0][0] + b0, 0.f) * z[0][NMAT - 1];
+        }
+      }
+    }
+    if (m0 + RB < Mb) issue(m0 + RB, 0);       // the next batch's rows of B
   }
+  if (tid == 0 && cnt_blk) cnt_blk[blockIdx.x] = block_count;
 }
 
-// Up/gate over an explicit list (pi_sparse_ffn): h_list[j] for j < count.
-// Block 0's threads also clear the fp64 accumulator y_acc[d].
-template <int WT, int ACT>
+// Up/gate over an explicit list (pi_sparse_ffn): h_list[j] for j < count, one
+// list entry per wave at a time.  Entries outside [0, f) give h = 0 and read
+// nothing.
+template <int WT, int ACT, int WCH>
 __global__ void __launch_bounds__(256)
 k_up_list(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc,
           const void* __restrict__ up_w, const uint16_t* __restrict__ up_sc,
           const float* __restrict__ bias, const float* __restrict__ x, int d, int f,
-          const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
-          float* __restrict__ h_list, double* __restrict__ y_acc) {
+          const int32_t* __restrict__ idx, const int32_t* __restrict__ count, float* __restrict__ h_list) {
   extern __shared__ float xs[];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE, W = blockDim.x / WAVE;
-  {
-    const int nb = gridDim.x, b = blockIdx.x, cy = (d + nb - 1) / nb;
-    for (int k = b * cy + tid; k < min(d, (b + 1) * cy); k += blockDim.x) y_acc[k] = 0.0;
-  }
   const int cnt = min(max(*count, 0), f);
   if ((int)blockIdx.x * W >= cnt) return;
-  for (int k = tid; k < d; k += blockDim.x) xs[k] = x[k];
+  stage_f32<8>(xs, x, d, tid, blockDim.x);
   __syncthreads();
+  constexpr int NMAT = (ACT == ACT_RELU) ? 1 : 2;
+  const void* w0 = (ACT == ACT_RELU) ? up_w : gate_w;
+  const uint16_t* s0 = (ACT == ACT_RELU) ? up_sc : gate_sc;
   for (int j = blockIdx.x * W + w; j < cnt; j += gridDim.x * W) {
     const int i = idx[j];
     float h = 0.f;
     if (i >= 0 && i < f) {
-      const float zu = row_dot<WT>(up_w, up_sc, (size_t)i, d, xs, lane);
-      if constexpr (ACT == ACT_RELU) {
-        h = fmaxf(zu + bias[i], 0.f);
-      } else {
-        const float zg = row_dot<WT>(gate_w, gate_sc, (size_t)i, d, xs, lane);
-        h = fmaxf(zg + bias[i], 0.f) * zu;
-      }
+      const int rows[1] = {i};
+      float z[1][NMAT];
+      gather_rows<WT, WCH, NMAT, 1>(w0, s0, up_w, up_sc, rows, d, xs, lane, z);
+      h = (ACT == ACT_RELU) ? fmaxf(z[0][0] + bias[i], 0.f) : fmaxf(z[0][0] + bias[i], 0.f) * z[0][NMAT - 1];
     }
     if (lane == 0) h_list[j] = h;
   }
 }
 
 // ----------------------------------------------------------------------- K3
-// Down projection.  Block (ct, nc): column tile ct of width 64*EPL, neuron
-// sub-chunks s = nc*W + w (of S = NC*W).  Wave s accumulates, in ascending
-// neuron order, the active neurons i with i % S == s (implicit mode: mask
-// bits + h per neuron) or the list positions j % S == s (explicit mode: idx +
-// h per position).  Block partials are summed over waves in a fixed order
-// and added to y_acc (fp64) with one atomic per column.
-template <int WT, bool EXPLICIT>
-__global__ void __launch_bounds__(256)
-k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int f, int d, int CT,
-       const uint32_t* __restrict__ mask_bits, const float* __restrict__ h_full,
-       const int32_t* __restrict__ idx, const int32_t* __restrict__ count, const float* __restrict__ h_list,
-       const float* __restrict__ b_down, double* __restrict__ y_acc, int32_t* __restrict__ count_out) {
-  constexpr int EPL = Tr<WT>::EPL;
-  constexpr int TW = WAVE * EPL;
-  constexpr int U = 4;
-  extern __shared__ float red[];   // [W][TW]
-  __shared__ int cnt_red[16];
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE, W = blockDim.x / WAVE;
-  const int ct = blockIdx.x % CT, nc = blockIdx.x / CT, NC = gridDim.x / CT;
-  const int S = NC * W, s = nc * W + w;
-  const int col = ct * TW + lane * EPL;
-  const bool col_ok = col < d;
+// Down projection y = sum over active neurons i of h_i * downT[i].
+// Block (t, nc): column tile t (TWC 16-byte chunks = TWC*EPL columns) and
+// neuron split nc of NC.  With the XCD-aware order, the blocks that the
+// hardware places on one XCD (block ids congruent mod 8) own adjacent tiles,
+// so the tiles that share a 128-byte line of a row share that XCD's L2.
+// Each wave builds, in LDS, the list of active neurons among its share of the
+// mask (16-neuron groups g = nc*8 + w + S*k, S = 8*NC) or of an explicit list,
+// then gathers the tile's segments of those rows, RPW = 64 / TWC rows per
+// wave-wide load and K3_LOADS loads per HBM round trip, accumulating in fp32
+// in list order.  Lanes of one chunk column are summed with a transposed
+// butterfly, the block's waves in a fixed order, and the tile's partial sums
+// are written to y_part[nc][cols] with plain stores.
+constexpr int K3_WAVES = 8;
+constexpr int K3_CAP = 2048;     // list entries per wave
+constexpr int K3_LOADS = 16;     // row segments per lane per HBM round trip
 
-  if (!EXPLICIT && count_out && blockIdx.x == 0) {
-    int c = 0;
-    const int nwords = (f + 31) / 32;
-    for (int k = tid; k < nwords; k += blockDim.x) c += __popc(mask_bits[k]);
-    for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m, WAVE);
-    if (lane == 0) cnt_red[w] = c;
-    __syncthreads();
-    if (tid == 0) {
-      int tot = 0;
-      for (int i = 0; i < W; ++i) tot += cnt_red[i];
-      *count_out = tot;
-    }
-  }
+template <int WT, int TWC, bool EXPLICIT>
+__global__ void __launch_bounds__(512)
+k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int f, int d, int CT, int NC,
+       int xcd_order, const uint8_t* __restrict__ mask, const float* __restrict__ h_full,
+       const int32_t* __restrict__ idx, const int32_t* __restrict__ count, const float* __restrict__ h_list,
+       const float* __restrict__ b_down, float* __restrict__ y_part, const int32_t* __restrict__ cnt_blk,
+       int n_cnt_blk, int32_t* __restrict__ count_out, int32_t* __restrict__ count_out2) {
+  constexpr int EPL = Tr<WT>::EPL;
+  constexpr int RPW = WAVE / TWC;                 // rows per wave-wide load
+  constexpr int TCOL = TWC * EPL;                 // columns per tile
+  constexpr int HC = EXPLICIT ? K3_CAP : 1;
+  __shared__ int l_id[K3_WAVES][K3_CAP];
+  __shared__ float l_h[K3_WAVES][HC];
+  __shared__ float red[K3_WAVES][TCOL];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const int nblk = CT * NC;
+  int L = blockIdx.x;
+  if (xcd_order) L = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
+  const int tile = L % CT, nc = L / CT;
+  const int S = NC * K3_WAVES, s = nc * K3_WAVES + w;
+  const int q = lane % TWC, rl = lane / TWC;
+  const int col = tile * TCOL + q * EPL;
+  const int colc = min(col, d - EPL);             // lanes past d read a valid chunk, unused
+
+  // block 0 also adds up the predictor kernel's per-block active counts
+  __shared__ int cnt_red[K3_WAVES];
+  int cpart = 0;
+  if (blockIdx.x == 0 && (count_out || count_out2))
+    for (int k = tid; k < n_cnt_blk; k += blockDim.x) cpart += cnt_blk[k];
 
   float acc[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
 
-  const int n_items = EXPLICIT ? min(max(*count, 0), f) : f;
-  for (int base = s; base < n_items; base += S * WAVE) {
-    const int item = base + S * lane;
-    bool on = false;
-    if (item < n_items) {
-      if constexpr (EXPLICIT) {
-        const int i = idx[item];
-        on = (i >= 0) && (i < f);
-      } else {
-        on = (mask_bits[item >> 5] >> (item & 31)) & 1u;
-      }
+  int n = 0;                                      // entries in this wave's list
+  // gather the listed rows' segments: entry e = e0 + k*RPW + rl for wave-load
+  // k; NL loads per round, all issued before the first multiply (entries past
+  // the list repeat its last row with h = 0)
+  auto batch = [&](auto nl_c, int e0) __attribute__((always_inline)) {
+    constexpr int NL = decltype(nl_c)::value;
+    uint4 c[NL];
+    float sc[NL], hv[NL];
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int ec = min(e0 + k * RPW + rl, n - 1);
+      const int row = l_id[w][ec];
+      c[k] = ld_chunk<WT>(downT, (size_t)row, d, colc);
+      sc[k] = (WT == DT_Q4) ? ld_scale(down_sc, (size_t)row, d, colc) : 1.f;
+      if constexpr (EXPLICIT) hv[k] = l_h[w][ec];
+      else hv[k] = h_full[row];
     }
-    uint64_t bal = __ballot(on);
-    while (bal) {
-      int rows[U];
-      float hv[U];
+    PI_ISSUE_FENCE();
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        rows[u] = -1;
-        hv[u] = 0.f;
-        if (bal) {
-          const int l = __ffsll((unsigned long long)bal) - 1;
-          bal &= bal - 1;
-          const int it = base + S * l;
-          if constexpr (EXPLICIT) {
-            rows[u] = idx[it];
-            hv[u] = h_list[it];
-          } else {
-            rows[u] = it;
-            hv[u] = h_full[it];
-          }
-        }
+    for (int k = 0; k < NL; ++k) chunk_axpy<WT>(c[k], sc[k], (e0 + k * RPW + rl < n) ? hv[k] : 0.f, acc);
+  };
+  auto flush = [&]() __attribute__((always_inline)) {
+    for (int e0 = 0; e0 < n; e0 += K3_LOADS * RPW) {
+      const int nl = (n - e0 + RPW - 1) / RPW;   // wave-uniform
+      if (nl <= 4) batch(std::integral_constant<int, 4>{}, e0);
+      else if (nl <= 8) batch(std::integral_constant<int, 8>{}, e0);
+      else batch(std::integral_constant<int, K3_LOADS>{}, e0);
+    }
+    n = 0;
+  };
+
+  if constexpr (!EXPLICIT) {
+    // Each lane turns its 16 mask bytes (0 or 1) into 16 bits; a wave prefix
+    // sum of the bit counts places every lane's active neurons in the list.
+    const int ngrp = (f + 15) / 16;                // 16-neuron mask groups (the buffer is padded)
+    auto bits4 = [](uint32_t x) __attribute__((always_inline)) { return ((x & 0x01010101u) * 0x01020408u) >> 24; };
+    auto grp_of = [&](int r) __attribute__((always_inline)) { return s + S * (lane + WAVE * r); };
+    // one 16-byte group per lane per round; the next round's group is loaded
+    // while this one is scanned
+    uint4 nxt = reinterpret_cast<const uint4*>(mask)[min(grp_of(0), ngrp - 1)];
+    for (int r = 0; s + S * WAVE * r < ngrp; ++r) {
+      const uint4 cur = nxt;
+      if (s + S * WAVE * (r + 1) < ngrp) nxt = reinterpret_cast<const uint4*>(mask)[min(grp_of(r + 1), ngrp - 1)];
+      if (n > K3_CAP - 16 * WAVE) flush();
+      const int grp = grp_of(r);
+      uint32_t bits = bits4(cur.x) | (bits4(cur.y) << 4) | (bits4(cur.z) << 8) | (bits4(cur.w) << 12);
+      if (grp >= ngrp) bits = 0;
+      else if (grp * 16 + 16 > f) bits &= (1u << (f - grp * 16)) - 1u;
+      const int c = __popc(bits);
+      const int incl = wave_scan(c);
+      int pos = n + incl - c;
+      while (bits) {
+        const int b = __ffs(bits) - 1;
+        bits &= bits - 1;
+        l_id[w][pos++] = grp * 16 + b;
       }
-      uint4 c[U];
-      float sc[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        sc[u] = 1.f;
-        if (rows[u] >= 0 && col_ok) {
-          c[u] = ld_chunk<WT>(downT, (size_t)rows[u], d, col);
-          if constexpr (WT == DT_Q4) sc[u] = ld_scale(down_sc, (size_t)rows[u], d, col);
-        }
+      n += lane_i(incl, WAVE - 1);
+    }
+  } else {
+    const int cnt = min(max(*count, 0), f);
+    for (int p0 = s; p0 < cnt; p0 += S * WAVE) {
+      const int p = min(p0 + S * lane, cnt - 1);
+      const int id = idx[p];
+      const float hl = h_list[p];
+      const bool on = p0 + S * lane < cnt && id >= 0 && id < f;
+      const uint64_t bal = __ballot(on);
+      if (bal == 0) continue;
+      if (n > K3_CAP - WAVE) flush();
+      if (on) {
+        const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        l_id[w][pos] = id;
+        l_h[w][pos] = hl;
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (rows[u] >= 0 && col_ok) chunk_axpy<WT>(c[u], sc[u], hv[u], acc);
+      n += __popcll(bal);
     }
   }
+  if (n > 0) flush();
 
+  // Sum the RPW row lanes of each chunk column: lanes with equal lane % TWC
+  // hold the same columns; lane q < TWC writes the wave's sums for chunk q.
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) red[w * TW + lane * EPL + j] = acc[j];
+  for (int j = 0; j < EPL; ++j) {
+    const float v = group_sum<TWC>(acc[j], lane);
+    if (lane < TWC) red[w][lane * EPL + j] = v;
+  }
+  if (blockIdx.x == 0 && (count_out || count_out2)) {
+    cpart = wave_sum(cpart);
+    if (lane == 0) cnt_red[w] = cpart;
+  }
   __syncthreads();
-  for (int cc = tid; cc < TW; cc += blockDim.x) {
-    const int cg = ct * TW + cc;
+  if (blockIdx.x == 0 && tid == 0 && (count_out || count_out2)) {
+    int tot = 0;
+    for (int i = 0; i < K3_WAVES; ++i) tot += cnt_red[i];
+    if (count_out) *count_out = tot;
+    if (count_out2) *count_out2 = tot;
+  }
+  for (int cc = tid; cc < TCOL; cc += blockDim.x) {
+    const int cg = tile * TCOL + cc;
     if (cg >= d) continue;
     float v = 0.f;
-    for (int i = 0; i < W; ++i) v += red[i * TW + cc];
+#pragma unroll
+    for (int i = 0; i < K3_WAVES; ++i) v += red[i][cc];
     if (b_down && nc == 0) v += b_down[cg];
-    unsafeAtomicAdd(&y_acc[cg], (double)v);
+    y_part[(size_t)nc * d + cg] = v;
   }
 }
 
+
 // --------------------------------------------------------------- small ones
-// Ascending list of set mask bits (single block): idx[0..count), *count.
+// Ascending list of the neurons whose mask byte is set (single block of 1024
+// threads): idx[0..count), *count.  Each thread takes 4 bytes per round; a
+// wave-level inclusive scan of per-thread counts and a block scan of the wave
+// totals give each thread its output position.
 __global__ void __launch_bounds__(1024)
-k_compact(const uint32_t* __restrict__ mask_bits, int f, int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+k_compact(const uint8_t* __restrict__ mask, int f, int32_t* __restrict__ idx, int32_t* __restrict__ count) {
   __shared__ int wsum[16];
   __shared__ int base_s;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE, W = blockDim.x / WAVE;
-  const int nwords = (f + 31) / 32;
   if (tid == 0) base_s = 0;
   __syncthreads();
-  for (int w0 = 0; w0 < nwords; w0 += blockDim.x) {
-    const int k = w0 + tid;
-    const uint32_t bits = k < nwords ? mask_bits[k] : 0u;
+  for (int i0 = 0; i0 < f; i0 += 4 * blockDim.x) {
+    const int i = i0 + 4 * tid;
+    uint32_t bits = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (i + b < f && mask[i + b]) bits |= 1u << b;
     const int c = __popc(bits);
-    // inclusive scan within the wave
-    int inc = c;
-    for (int off = 1; off < WAVE; off <<= 1) {
-      const int v = __shfl_up(inc, off, WAVE);
-      if (lane >= off) inc += v;
-    }
+    const int inc = wave_scan(c);
     if (lane == WAVE - 1) wsum[w] = inc;
     __syncthreads();
     int wbase = 0;
-    for (int i = 0; i < w; ++i) wbase += wsum[i];
-    const int pos = base_s + wbase + inc - c;
-    uint32_t bb = bits;
-    int o = 0;
-    while (bb) {
-      const int bit = __ffs(bb) - 1;
-      bb &= bb - 1;
-      idx[pos + o++] = k * 32 + bit;
-    }
+    for (int k = 0; k < w; ++k) wbase += wsum[k];
+    int pos = base_s + wbase + inc - c;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (bits & (1u << b)) idx[pos++] = i + b;
     __syncthreads();
     if (tid == 0) {
       int tot = 0;
-      for (int i = 0; i < W; ++i) tot += wsum[i];
+      for (int k = 0; k < W; ++k) tot += wsum[k];
       base_s += tot;
     }
     __syncthreads();
@@ -469,29 +789,41 @@ k_compact(const uint32_t* __restrict__ mask_bits, int f, int32_t* __restrict__ i
   if (tid == 0) *count = base_s;
 }
 
-__global__ void k_copy_i32(const int32_t* __restrict__ src, int32_t* __restrict__ dst, int n) {
-  const int k = blockIdx.x * blockDim.x + threadIdx.x;
-  if (k < n) dst[k] = src[k];
-}
-
-// y = float(y_acc)
-__global__ void k_finalize(const double* __restrict__ y_acc, float* __restrict__ y, int n) {
-  const int k = blockIdx.x * blockDim.x + threadIdx.x;
-  if (k < n) y[k] = (float)y_acc[k];
-}
-
-// out = glue(x, y_acc): single block, same operation order as K1's glue.
+// *out = *out2 = sum of n per-block counts (single block of 256 threads; either may be NULL)
 __global__ void __launch_bounds__(256)
-k_glue_out(const float* __restrict__ x, const double* __restrict__ y_acc, float* __restrict__ out, int d) {
+k_sum_counts(const int32_t* __restrict__ cnt, int n, int32_t* __restrict__ out, int32_t* __restrict__ out2) {
+  __shared__ int red[4];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  int c = 0;
+  for (int k = tid; k < n; k += blockDim.x) c += cnt[k];
+  c = wave_sum(c);
+  if (lane == 0) red[w] = c;
+  __syncthreads();
+  if (tid == 0) {
+    const int tot = red[0] + red[1] + red[2] + red[3];
+    if (out) *out = tot;
+    if (out2) *out2 = tot;
+  }
+}
+
+// y = sum of np partial vectors of n floats, added in order
+__global__ void k_finalize(const float* __restrict__ y_part, int np, float* __restrict__ y, int n) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k < n) {
+    float v = y_part[k];
+    for (int p = 1; p < np; ++p) v += y_part[(size_t)p * n + k];
+    y[k] = v;
+  }
+}
+
+// out = glue(x, y) with y given as np partials: single block, same operation
+// order as K1's glue.
+__global__ void __launch_bounds__(256)
+k_glue_out(const float* __restrict__ x, const float* __restrict__ y_part, int np, float* __restrict__ out, int d) {
   extern __shared__ float vs[];
   __shared__ float red[16];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE, W = blockDim.x / WAVE;
-  float ss = 0.f;
-  for (int k = tid; k < d; k += blockDim.x) {
-    const float v = x[k] + (float)y_acc[k];
-    vs[k] = v;
-    ss = fmaf(v, v, ss);
-  }
+  float ss = stage_residual<4>(vs, x, y_part, np, d, tid, blockDim.x);
   ss = wave_sum(ss);
   if (lane == 0) red[w] = ss;
   __syncthreads();
