@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "pi_batch.hpp"
 #include "pi_kernels.hpp"
 
 namespace {
@@ -50,7 +51,6 @@ pi_status check_layer(const pi_layer* L) {
 
 pi_status check_batch(int32_t batch) {
   if (batch < 1 || batch > 32) return PI_EINVAL;
-  if (batch != 1) return PI_EUNSUPPORTED;
   return PI_OK;
 }
 
@@ -70,22 +70,40 @@ int k2_blocks_for(int ffn, int rank, int p_dtype);
 int k2_blocks_max(int ffn);
 
 struct WsLayout {
-  size_t t, xbuf, ybuf, mask, h, cnt, misc, total;
-  size_t xs, ys;   // sizes of one x / one y (all partials) buffer
+  size_t t, xbuf, ybuf, mask, h, cnt, misc;
+  // batched path (batch > 1)
+  size_t xh, xl, tpart, th, tl, mnm, ulist, hh, hl;
+  size_t total;
+  size_t xs, ys;   // sizes of one x / one y buffer
 };
+
+constexpr int kBatchM = pib::BM;      // padded batch rows of the batched GEMMs
+constexpr int kMaxKSplit = 16;        // K splits of the batched predictor's first GEMM
 
 WsLayout layout(const Dims& D, int batch) {
   WsLayout w{};
   size_t o = 0;
+  const size_t fpad = (size_t)cdiv(D.fmax, 16) * 16;
   w.xs = align_up(sizeof(float) * (size_t)D.d * batch);
-  w.ys = align_up(sizeof(float) * (size_t)D.d * batch * kMaxParts);
+  w.ys = align_up(sizeof(float) * (size_t)D.d * std::max(kMaxParts * batch, batch > 1 ? kBatchM : 0));
   w.t = o;    o += align_up(sizeof(float) * (size_t)D.rmax * batch);
   w.xbuf = o; o += w.xs * 2;
   w.ybuf = o; o += w.ys * 2;
-  w.mask = o; o += align_up((size_t)cdiv(D.fmax, 16) * 16 * batch);     // padded to 16-byte groups
-  w.h = o;    o += align_up(sizeof(float) * (size_t)D.fmax * batch);
+  w.mask = o; o += align_up(fpad);                       // one byte per neuron (the union when batch > 1)
+  w.h = o;    o += align_up(sizeof(float) * (size_t)D.fmax);
   w.cnt = o;  o += align_up(sizeof(int32_t) * (size_t)k2_blocks_max(D.fmax));
   w.misc = o; o += kAlign;
+  if (batch > 1) {
+    w.xh = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * D.d);
+    w.xl = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * D.d);
+    w.tpart = o; o += align_up(sizeof(float) * (size_t)kMaxKSplit * kBatchM * D.rmax);
+    w.th = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * D.rmax);
+    w.tl = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * D.rmax);
+    w.mnm = o;   o += align_up((size_t)kBatchM * D.fmax);
+    w.ulist = o; o += align_up(sizeof(int32_t) * (size_t)D.fmax);
+    w.hh = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * D.fmax);
+    w.hl = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * D.fmax);
+  }
   w.total = o;
   return w;
 }
@@ -98,11 +116,15 @@ struct Ws {
   float* h;
   int32_t* cnt;
   int32_t* misc;
+  _Float16 *xh, *xl, *th, *tl, *hh, *hl;
+  float* tpart;
+  uint8_t* mnm;
+  int32_t* ulist;
 };
 
 Ws carve(void* base, const WsLayout& L) {
   char* b = static_cast<char*>(base);
-  Ws w;
+  Ws w{};
   w.t = reinterpret_cast<float*>(b + L.t);
   w.x[0] = reinterpret_cast<float*>(b + L.xbuf);
   w.x[1] = reinterpret_cast<float*>(b + L.xbuf + L.xs);
@@ -112,6 +134,17 @@ Ws carve(void* base, const WsLayout& L) {
   w.h = reinterpret_cast<float*>(b + L.h);
   w.cnt = reinterpret_cast<int32_t*>(b + L.cnt);
   w.misc = reinterpret_cast<int32_t*>(b + L.misc);
+  if (L.xh) {
+    w.xh = reinterpret_cast<_Float16*>(b + L.xh);
+    w.xl = reinterpret_cast<_Float16*>(b + L.xl);
+    w.tpart = reinterpret_cast<float*>(b + L.tpart);
+    w.th = reinterpret_cast<_Float16*>(b + L.th);
+    w.tl = reinterpret_cast<_Float16*>(b + L.tl);
+    w.mnm = reinterpret_cast<uint8_t*>(b + L.mnm);
+    w.ulist = reinterpret_cast<int32_t*>(b + L.ulist);
+    w.hh = reinterpret_cast<_Float16*>(b + L.hh);
+    w.hl = reinterpret_cast<_Float16*>(b + L.hl);
+  }
   return w;
 }
 
@@ -369,6 +402,67 @@ void up_list(const pi_layer* L, const float* x, const int32_t* idx, const int32_
   }
 }
 
+// ----------------------------------------------------------- batched path
+// K splits of the first predictor GEMM so that the grid has ~256 blocks.
+int bksplit(int r) { return std::max(1, std::min(kMaxKSplit, cdiv(256, cdiv(r, kBatchM)))); }
+
+// x' of every sequence (glue of x_prev and y_prev, or x_prev itself when
+// y_prev is NULL) to x_out / x_trace and as fp16 hi/lo operands.
+void b_glue(const float* x_prev, const float* y_prev, int batch, int d, float* x_out, float* x_trace, const Ws& W,
+            hipStream_t st) {
+  hipLaunchKernelGGL(pib::k_bglue, dim3(kBatchM), dim3(256), sizeof(float) * d, st, x_prev, y_prev,
+                     y_prev ? 1 : 0, batch, d, x_out, x_trace, W.xh, W.xl);
+}
+
+// per-sequence scores and masks, the union and its ascending list
+void b_predict(const pi_layer* L, int batch, const Ws& W, float* scores, uint8_t* mask_out, int32_t* ulist,
+               int32_t* ucount, int32_t* ucount2, hipStream_t st) {
+  const int ks = bksplit(L->rank);
+  const dim3 g1(cdiv(L->rank, kBatchM) * ks);
+  if (L->p_dtype == PI_F16)
+    hipLaunchKernelGGL(pib::k_bpred1<DT_F16>, g1, dim3(256), 0, st, L->A, L->rank, L->d, ks, W.xh, W.xl, W.tpart);
+  else
+    hipLaunchKernelGGL(pib::k_bpred1<DT_F32>, g1, dim3(256), 0, st, L->A, L->rank, L->d, ks, W.xh, W.xl, W.tpart);
+  hipLaunchKernelGGL(pib::k_bsplit_t, dim3(cdiv(kBatchM * L->rank, 256)), dim3(256), 0, st, W.tpart, ks, L->rank,
+                     W.th, W.tl);
+  const dim3 g2(cdiv(cdiv(L->ffn, kBatchM), 4));
+  const float* pb = L->pbias ? L->pbias : L->bias;
+  if (L->p_dtype == PI_F16)
+    hipLaunchKernelGGL(pib::k_bscore<DT_F16>, g2, dim3(256), 0, st, L->B, pb, L->ffn, L->rank, batch, W.th, W.tl,
+                       W.mnm, W.mask, W.cnt, scores, mask_out);
+  else
+    hipLaunchKernelGGL(pib::k_bscore<DT_F32>, g2, dim3(256), 0, st, L->B, pb, L->ffn, L->rank, batch, W.th, W.tl,
+                       W.mnm, W.mask, W.cnt, scores, mask_out);
+  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, ulist, ucount, ucount2);
+}
+
+template <int WT, int ACT>
+void b_ffn_t(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, const int32_t* ucount, float* y,
+             hipStream_t st) {
+  hipLaunchKernelGGL((pib::k_bup<WT, ACT>), dim3(cdiv(cdiv(L->ffn, kBatchM), 4)), dim3(256), 0, st, L->gate.w,
+                     L->gate.scale, L->up.w, L->up.scale, L->bias, L->ffn, L->d, W.xh, W.xl, ulist, ucount, W.mnm,
+                     W.hh, W.hl);
+  hipLaunchKernelGGL(pib::k_bdown<WT>, dim3(cdiv(L->d, kBatchM)), dim3(256), 0, st, L->downT.w, L->downT.scale,
+                     L->ffn, L->d, ulist, ucount, W.hh, W.hl, L->b_down, batch, y);
+}
+
+// the FFN over the union list for every sequence: y [batch][d]
+void b_ffn(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, const int32_t* ucount, float* y,
+           hipStream_t st) {
+  const bool reglu = L->act == PI_REGLU;
+  switch (L->w_dtype) {
+    case PI_F32:
+      return reglu ? b_ffn_t<DT_F32, ACT_REGLU>(L, batch, W, ulist, ucount, y, st)
+                   : b_ffn_t<DT_F32, ACT_RELU>(L, batch, W, ulist, ucount, y, st);
+    case PI_F16:
+      return reglu ? b_ffn_t<DT_F16, ACT_REGLU>(L, batch, W, ulist, ucount, y, st)
+                   : b_ffn_t<DT_F16, ACT_RELU>(L, batch, W, ulist, ucount, y, st);
+    default:
+      return reglu ? b_ffn_t<DT_Q4, ACT_REGLU>(L, batch, W, ulist, ucount, y, st)
+                   : b_ffn_t<DT_Q4, ACT_RELU>(L, batch, W, ulist, ucount, y, st);
+  }
+}
+
 pi_status launch_status() {
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? PI_OK : PI_EHIP;
@@ -403,15 +497,21 @@ pi_status pi_predict(const pi_layer* layer, const float* x, int32_t batch, float
   if ((s = check_layer(layer)) != PI_OK) return s;
   if ((s = check_batch(batch)) != PI_OK) return s;
   if (!x || !aligned(x, 16) || !idx || !count) return PI_EINVAL;
+  if (batch > 1 && !mask) return PI_EINVAL;
   Dims D{layer->d, layer->ffn, layer->rank};
   const WsLayout WL = layout(D, batch);
   if (!ws || ws_bytes < WL.total || !aligned(ws, kAlign)) return PI_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Ws W = carve(ws, WL);
   (void)hipGetLastError();
+  if (batch > 1) {
+    b_glue(x, nullptr, batch, layer->d, nullptr, nullptr, W, st);
+    b_predict(layer, batch, W, scores, mask, idx, count, nullptr, st);
+    return launch_status();
+  }
   k1(layer, K1Args{x, nullptr, 0, nullptr, nullptr, W.t}, st);
   k2(layer, false, K2Args{W.t, nullptr, scores, W.mask, mask, nullptr, nullptr}, st);
-  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, layer->ffn, idx, count);
+  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, layer->ffn, idx, count, nullptr);
   return launch_status();
 }
 
@@ -422,13 +522,23 @@ pi_status pi_sparse_ffn(const pi_layer* layer, const float* x, int32_t batch, co
   if ((s = check_layer(layer)) != PI_OK) return s;
   if ((s = check_batch(batch)) != PI_OK) return s;
   if (!x || !aligned(x, 16) || !idx || !count || !y) return PI_EINVAL;
-  if (batch == 1 && mask) return PI_EINVAL;
+  if ((batch == 1) != (mask == nullptr)) return PI_EINVAL;
   Dims D{layer->d, layer->ffn, layer->rank};
   const WsLayout WL = layout(D, batch);
   if (!ws || ws_bytes < WL.total || !aligned(ws, kAlign)) return PI_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Ws W = carve(ws, WL);
   (void)hipGetLastError();
+  if (batch > 1) {
+    // the listed neurons become the union (ascending, each once) with the caller's per-sequence masks
+    b_glue(x, nullptr, batch, layer->d, nullptr, nullptr, W, st);
+    hipLaunchKernelGGL(pib::k_bclear, dim3(cdiv(layer->ffn, 256)), dim3(256), 0, st, W.mask, layer->ffn);
+    hipLaunchKernelGGL(pib::k_blist, dim3(cdiv(layer->ffn, 256)), dim3(256), 0, st, idx, count, layer->ffn, mask,
+                       batch, W.mask, W.mnm);
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, layer->ffn, W.ulist, W.misc, nullptr);
+    b_ffn(layer, batch, W, W.ulist, W.misc, y, st);
+    return launch_status();
+  }
   up_list(layer, x, idx, count, W.h, st);
   const int np = k3<true>(layer, K3Args{nullptr, nullptr, idx, count, W.h, W.y[0], nullptr, 0, nullptr, nullptr},
                           st);
@@ -451,6 +561,25 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
   hipStream_t st = static_cast<hipStream_t>(stream);
   Ws W = carve(ws, WL);
   (void)hipGetLastError();
+  if (batch > 1) {
+    for (int l = 0; l < n_layers; ++l) {
+      const pi_layer* L = &layers[l];
+      const pi_trace* tr = trace ? &trace[l] : nullptr;
+      const int cur = l & 1, prv = cur ^ 1;
+      b_glue(l == 0 ? x : W.x[prv], l == 0 ? nullptr : W.y[prv], batch, L->d, W.x[cur], tr ? tr->x_in : nullptr,
+             W, st);
+      b_predict(L, batch, W, tr ? tr->scores : nullptr, tr ? tr->mask : nullptr, W.ulist, W.misc,
+                counts ? counts + l : nullptr, st);
+      if (tr && (tr->idx || tr->count))   // the union list and count for the record
+        hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, tr->idx ? tr->idx : W.ulist,
+                           tr->count ? tr->count : W.misc + 1, nullptr);
+      b_ffn(L, batch, W, W.ulist, W.misc, W.y[cur], st);
+    }
+    const int last = (n_layers - 1) & 1;
+    hipLaunchKernelGGL(pib::k_bglue_out, dim3(batch), dim3(256), sizeof(float) * D.d, st, W.x[last], W.y[last],
+                       D.d, out);
+    return launch_status();
+  }
   int np_prev = 0;
   for (int l = 0; l < n_layers; ++l) {
     const pi_layer* L = &layers[l];
@@ -464,7 +593,7 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
     int32_t* c2 = (tr && tr->count && !tr->idx) ? tr->count : nullptr;
     if (tr && tr->idx)   // ascending list for the record; the down projection reads the mask bytes directly
       hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, tr->idx,
-                         tr->count ? tr->count : W.misc);
+                         tr->count ? tr->count : W.misc, nullptr);
     np_prev = k3<false>(L, K3Args{W.mask, W.h, nullptr, nullptr, nullptr, W.y[cur], W.cnt, k2_blocks(L), c1, c2},
                         st);
   }

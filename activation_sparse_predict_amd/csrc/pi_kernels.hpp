@@ -752,22 +752,28 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
 
 // --------------------------------------------------------------- small ones
 // Ascending list of the neurons whose mask byte is set (single block of 1024
-// threads): idx[0..count), *count.  Each thread takes 4 bytes per round; a
-// wave-level inclusive scan of per-thread counts and a block scan of the wave
-// totals give each thread its output position.
+// threads): idx[0..count), *count (and *count2 if not NULL).  The mask buffer
+// is padded to a multiple of 16 bytes and holds 0 or 1.  Each thread takes 16
+// bytes per round; a DPP scan of the per-thread counts inside each wave and a
+// scan of the wave totals give each thread its output position.
 __global__ void __launch_bounds__(1024)
-k_compact(const uint8_t* __restrict__ mask, int f, int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+k_compact(const uint8_t* __restrict__ mask, int f, int32_t* __restrict__ idx, int32_t* __restrict__ count,
+          int32_t* __restrict__ count2) {
   __shared__ int wsum[16];
   __shared__ int base_s;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE, W = blockDim.x / WAVE;
+  const int ngrp = (f + 15) / 16;
   if (tid == 0) base_s = 0;
   __syncthreads();
-  for (int i0 = 0; i0 < f; i0 += 4 * blockDim.x) {
-    const int i = i0 + 4 * tid;
+  for (int g0 = 0; g0 < ngrp; g0 += blockDim.x) {
+    const int grp = g0 + tid;
     uint32_t bits = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (i + b < f && mask[i + b]) bits |= 1u << b;
+    if (grp < ngrp) {
+      const uint4 v = reinterpret_cast<const uint4*>(mask)[grp];
+      auto b4 = [](uint32_t x) __attribute__((always_inline)) { return ((x & 0x01010101u) * 0x01020408u) >> 24; };
+      bits = b4(v.x) | (b4(v.y) << 4) | (b4(v.z) << 8) | (b4(v.w) << 12);
+      if (grp * 16 + 16 > f) bits &= (1u << (f - grp * 16)) - 1u;
+    }
     const int c = __popc(bits);
     const int inc = wave_scan(c);
     if (lane == WAVE - 1) wsum[w] = inc;
@@ -775,9 +781,11 @@ k_compact(const uint8_t* __restrict__ mask, int f, int32_t* __restrict__ idx, in
     int wbase = 0;
     for (int k = 0; k < w; ++k) wbase += wsum[k];
     int pos = base_s + wbase + inc - c;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (bits & (1u << b)) idx[pos++] = i + b;
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1;
+      idx[pos++] = grp * 16 + b;
+    }
     __syncthreads();
     if (tid == 0) {
       int tot = 0;
@@ -786,7 +794,10 @@ k_compact(const uint8_t* __restrict__ mask, int f, int32_t* __restrict__ idx, in
     }
     __syncthreads();
   }
-  if (tid == 0) *count = base_s;
+  if (tid == 0) {
+    *count = base_s;
+    if (count2) *count2 = base_s;
+  }
 }
 
 // *out = *out2 = sum of n per-block counts (single block of 256 threads; either may be NULL)

@@ -31,6 +31,13 @@
  *    PI_EUNSUPPORTED); every layer of a stack has the same d.
  *  - Calls on distinct workspaces are independent; calls sharing a workspace
  *    must be ordered on one stream.
+ *  - Batch 1 runs GEMV kernels over the active rows.  Batch 2..32 runs each
+ *    sequence's predictor, takes the union of the masks (PowerInfer pages:
+ *    batched decoding, 机器之心 article, Fig. 14 paragraph) and computes the
+ *    FFN over the union's rows as gathered GEMMs on the matrix cores, with
+ *    fp16 hi/lo splits of the activations so that results match fp32
+ *    accumulation; a sequence's output equals its own batch-1 result (a
+ *    neuron in the union but off in that sequence's mask contributes 0).
  */
 #ifndef PI_H_
 #define PI_H_
@@ -110,8 +117,9 @@ size_t pi_workspace_bytes(const pi_layer* layers, int32_t n_layers, int32_t batc
  *   mask_{b,i} = (s_{b,i} > 0)  strict; zero and NaN are inactive
  *   idx = ascending storage ids i with mask_{b,i} = 1 for some b; *count = |idx|
  * x: [batch][d] float32.  scores: [batch][ffn] or NULL.  mask: [batch][ffn],
- * may be NULL when batch == 1.  idx: [ffn] int32.  count: [1] int32, written
- * on the device (the host never reads it inside the library).
+ * may be NULL when batch == 1 and is required when batch > 1 (PI_EINVAL).
+ * idx: [ffn] int32.  count: [1] int32, written on the device (the host never
+ * reads it inside the library).
  */
 pi_status pi_predict(const pi_layer* layer, const float* x, int32_t batch, float* scores,
                      uint8_t* mask, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
@@ -125,9 +133,10 @@ pi_status pi_predict(const pi_layer* layer, const float* x, int32_t batch, float
  *     ReLU:  h = max(bias_i + up[i] . x_b, 0)
  *     ReGLU: h = max(bias_i + gate[i] . x_b, 0) * (up[i] . x_b)
  *   y_b = sum_i h * downT[i]  (+ b_down)
- * idx: ascending or not, entries < ffn, first min(*count, ffn) used (count is
- * read on the device and clamped to [0, ffn]); mask: [batch][ffn], NULL iff
- * batch == 1.  y: [batch][d] float32, fully overwritten.
+ * idx: ascending or not, distinct entries, first min(*count, ffn) used (count
+ * is read on the device and clamped to [0, ffn]); entries outside [0, ffn)
+ * are skipped.  mask: [batch][ffn] uint8, NULL iff batch == 1 (PI_EINVAL
+ * otherwise).  y: [batch][d] float32, fully overwritten.
  */
 pi_status pi_sparse_ffn(const pi_layer* layer, const float* x, int32_t batch, const int32_t* idx,
                         const int32_t* count, const uint8_t* mask, float* y, void* ws,

@@ -129,3 +129,18 @@ def test_sparse_ffn_and_stack_validation(pi):
     r = lib.pi_ffn_stack(ctypes.cast(arr, ctypes.c_void_p), 0, FAKE, 1, FAKE, None, None, FAKE,
                          1 << 30, None)
     assert r == 1
+
+
+def test_batched_validation(pi):
+    L = make_layer(pi)
+    lib = pi.lib()
+    # batch > 1 needs the per-sequence mask in pi_predict and pi_sparse_ffn
+    r = lib.pi_predict(ctypes.byref(L), FAKE, 8, None, None, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert r == 1
+    r = lib.pi_sparse_ffn(ctypes.byref(L), FAKE, 8, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None)
+    assert r == 1
+    # the batched path needs more workspace than batch 1, and an undersized one is refused
+    n1, n8, n32 = ws_bytes(pi, L, batch=1), ws_bytes(pi, L, batch=8), ws_bytes(pi, L, batch=32)
+    assert 0 < n1 < n8 < n32
+    r = lib.pi_predict(ctypes.byref(L), FAKE, 8, None, FAKE, FAKE, FAKE, FAKE, n8 - 1, None)
+    assert r == 3

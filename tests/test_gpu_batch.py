@@ -1,0 +1,197 @@
+"""GPU parity of the batched path (1 < batch <= 32) against the CPU oracle.
+
+Per sequence: scores within the threshold band, masks bit-exact outside it,
+the union list equal to the ascending list of the GPU's own union, and each
+sequence's FFN output equal to its own single-sequence result (the oracle's
+batch semantics).  The FFN is checked layer by layer on the oracle's masks,
+so that a band neuron decided differently cannot leak into the comparison.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workload
+from parity import BAND, TOL, check_list, check_scores_masks, check_y, rel_err
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import activation_sparse_predict_amd as pi  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+SMALL = {
+    "f16-relu": workload.CONFIGS[3].with_(d=1024, ffn=2085, rank=256, n_layers=2),
+    "f16-reglu": workload.CONFIGS[1].with_(d=512, ffn=1500, rank=128, n_layers=2),
+    "q4-relu": workload.CONFIGS[4].with_(d=1024, ffn=3001, rank=128, n_layers=2),
+    "q4-reglu": workload.CONFIGS[4].with_(act="reglu", d=512, ffn=777, rank=64, n_layers=2),
+    "f32-relu": workload.CONFIGS[0].with_(d=256, ffn=1000, rank=64, n_layers=2),
+}
+
+
+def run_predict(L, X):
+    nb, f = X.shape[0], L.ffn
+    scores = torch.full((nb, f), float("nan"), dtype=torch.float32, device=DEV)
+    mask = torch.full((nb, f), 7, dtype=torch.uint8, device=DEV)
+    idx = torch.full((f,), -1, dtype=torch.int32, device=DEV)
+    count = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    pi.predict(L, dev(X), idx, count, scores=scores, mask=mask, batch=nb)
+    torch.cuda.synchronize()
+    return scores.cpu().numpy(), mask.cpu().numpy(), idx.cpu().numpy(), int(count[0].item())
+
+
+def run_sparse_ffn(L, X, idx_list, masks):
+    nb, d = X.shape
+    n = max(1, len(idx_list))
+    idx = torch.zeros(n, dtype=torch.int32, device=DEV)
+    if len(idx_list):
+        idx[:len(idx_list)] = dev(np.asarray(idx_list, np.int32))
+    cnt = torch.tensor([len(idx_list)], dtype=torch.int32, device=DEV)
+    y = torch.full((nb, d), float("nan"), dtype=torch.float32, device=DEV)
+    pi.sparse_ffn(L, dev(X), idx, cnt, y, mask=dev(np.asarray(masks, np.uint8)), batch=nb)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("nb", [2, 8, 32])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_batch_layer_small(name, nb):
+    cfg = SMALL[name]
+    say(f"[batch_small] {name} batch {nb} d={cfg.d} f={cfg.ffn} r={cfg.rank}")
+    lw = workload.make_layer(cfg, 0)
+    L = pi.DeviceLayer.upload(lw, DEV)
+    X = workload.make_x(cfg, 3, seqs=nb)
+    ref = oracle.layer_forward(lw, X)
+    scores, mask, idx, count = run_predict(L, X)
+    flips = 0
+    for b in range(nb):
+        st = check_scores_masks(ref["scores"][b], scores[b], mask[b])
+        flips += st["band_flips"]
+    union = mask.astype(bool).any(axis=0)
+    check_list(union, idx, count)
+    # the FFN on the oracle's own masks and union list, per sequence
+    Y = run_sparse_ffn(L, X, ref["idx"], ref["masks"])
+    for b in range(nb):
+        check_y(Y[b], ref["y"][b], TOL[cfg.w_dtype])
+    # each sequence equals its own single-sequence result
+    single = oracle.layer_forward(lw, X[1:2])
+    check_y(Y[1], single["y"][0], TOL[cfg.w_dtype])
+    say(f"  union {count} band flips {flips} worst y err "
+        f"{max(rel_err(Y[b], ref['y'][b]) for b in range(nb)):.2e}")
+
+
+def test_batch_edge_cases():
+    cfg = SMALL["f16-relu"]
+    say("[batch_edge] empty list, all neurons, padded rows")
+    lw = workload.make_layer(cfg, 0)
+    L = pi.DeviceLayer.upload(lw, DEV)
+    nb, f = 5, cfg.ffn
+    X = workload.make_x(cfg, 9, seqs=nb)
+    Y = run_sparse_ffn(L, X, [], np.zeros((nb, f), bool))
+    assert np.array_equal(Y, np.zeros_like(Y))
+    ones = np.ones((nb, f), bool)
+    Y = run_sparse_ffn(L, X, np.arange(f), ones)
+    dense = oracle.dense_ffn(cfg.act, lw.gate, lw.up, lw.downT, lw.bias, X)
+    for b in range(nb):
+        check_y(Y[b], dense[b], TOL[cfg.w_dtype])
+    # a neuron listed for the union but off in a sequence's own mask contributes 0 there
+    rng = np.random.default_rng(4)
+    M = rng.random((nb, f)) < 0.3
+    M[2] = False                                   # sequence 2 has no active neuron at all
+    listed = np.flatnonzero(M.any(axis=0))
+    Y = run_sparse_ffn(L, X, listed[::-1].copy(), M)   # unordered list
+    ref = oracle.sparse_ffn(cfg.act, lw.gate, lw.up, lw.downT, lw.bias, X, M)
+    assert np.array_equal(Y[2], np.zeros_like(Y[2]))
+    for b in range(nb):
+        check_y(Y[b], ref[b], TOL[cfg.w_dtype])
+
+
+def test_batch_stack_deterministic_and_traced():
+    cfg = SMALL["f16-reglu"]
+    nb = 8
+    say(f"[batch_stack] {cfg.n_layers} layers, batch {nb}, traced")
+    host = [workload.make_layer(cfg, l) for l in range(cfg.n_layers)]
+    layers = [pi.DeviceLayer.upload(h, DEV) for h in host]
+    X = workload.make_x(cfg, 11, seqs=nb)
+    d, f, n = cfg.d, cfg.ffn, cfg.n_layers
+    stack = pi.Stack(layers, batch=nb)
+    outs = []
+    for rep in range(2):
+        recs = [dict(x_in=torch.empty(nb, d, device=DEV), scores=torch.empty(nb, f, device=DEV),
+                     mask=torch.empty(nb, f, dtype=torch.uint8, device=DEV),
+                     idx=torch.empty(f, dtype=torch.int32, device=DEV),
+                     count=torch.empty(1, dtype=torch.int32, device=DEV)) for _ in range(n)]
+        out = torch.empty(nb, d, device=DEV)
+        counts = torch.zeros(n, dtype=torch.int32, device=DEV)
+        stack(dev(X), out, counts, pi.make_trace(n, recs))
+        torch.cuda.synchronize()
+        outs.append((out.cpu(), counts.cpu(), [{k: v.cpu().numpy() for k, v in r.items()} for r in recs]))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    out, counts, recs = outs[0][0].numpy(), outs[0][1].numpy(), outs[0][2]
+    # layer-local replay: the oracle takes the GPU's layer input and masks
+    for l, (h, r) in enumerate(zip(host, recs)):
+        ref = oracle.layer_forward(h, r["x_in"])
+        for b in range(nb):
+            check_scores_masks(ref["scores"][b], r["scores"][b], r["mask"][b])
+        union = r["mask"].astype(bool).any(axis=0)
+        check_list(union, r["idx"], int(r["count"][0]))
+        assert int(counts[l]) == int(r["count"][0])
+        y_ref = oracle.sparse_ffn(cfg.act, h.gate, h.up, h.downT, h.bias, r["x_in"], r["mask"].astype(bool))
+        x_next = oracle.rms_glue(r["x_in"], y_ref)
+        target = recs[l + 1]["x_in"] if l + 1 < n else out
+        for b in range(nb):
+            check_y(target[b], x_next[b], max(TOL[cfg.w_dtype], 1e-5))
+
+
+FULL = [(3, 8, 1), (3, 32, 1), (4, 32, 1)]
+
+
+@pytest.mark.parametrize("ci,nb,n_layers", FULL, ids=lambda v: str(v))
+def test_batch_full_size(ci, nb, n_layers):
+    """Real layer shapes of the batched workloads, through the stack, layer-locally replayed."""
+    cfg = workload.CONFIGS[ci]
+    say(f"[batch_full] config {ci} {cfg.name}: batch {nb}, {n_layers} layer(s)")
+    host = [workload.make_layer(cfg, l) for l in range(n_layers)]
+    layers = [pi.DeviceLayer.upload(h, DEV) for h in host]
+    X = workload.make_x(cfg, 0, seqs=nb)
+    d, f = cfg.d, cfg.ffn
+    recs = [dict(x_in=torch.empty(nb, d, device=DEV), scores=torch.empty(nb, f, device=DEV),
+                 mask=torch.empty(nb, f, dtype=torch.uint8, device=DEV),
+                 idx=torch.empty(f, dtype=torch.int32, device=DEV),
+                 count=torch.empty(1, dtype=torch.int32, device=DEV)) for _ in range(n_layers)]
+    out = torch.empty(nb, d, device=DEV)
+    pi.ffn_stack(layers, dev(X), out, trace=pi.make_trace(n_layers, recs), batch=nb)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    recs = [{k: v.cpu().numpy() for k, v in r.items()} for r in recs]
+    # sample 4 sequences for the float64 replay (the oracle is slow at these sizes)
+    sample = sorted({0, 1, nb // 2, nb - 1})
+    for l, (h, r) in enumerate(zip(host, recs)):
+        ref = oracle.layer_forward(h, r["x_in"][sample])
+        flips = 0
+        for j, b in enumerate(sample):
+            flips += check_scores_masks(ref["scores"][j], r["scores"][b], r["mask"][b])["band_flips"]
+        union = r["mask"].astype(bool).any(axis=0)
+        check_list(union, r["idx"], int(r["count"][0]))
+        M = r["mask"][sample].astype(bool)
+        y_ref = oracle.sparse_ffn(cfg.act, h.gate, h.up, h.downT, h.bias, r["x_in"][sample], M)
+        x_next = oracle.rms_glue(r["x_in"][sample], y_ref)
+        worst = 0.0
+        for j, b in enumerate(sample):
+            worst = max(worst, check_y(out[b], x_next[j], max(TOL[cfg.w_dtype], 1e-5)))
+        say(f"  layer {l}: union {int(r['count'][0])} ({r['count'][0] / f:.3f}), band flips {flips}, "
+            f"worst out err {worst:.2e}")
+    del layers
+    torch.cuda.empty_cache()
