@@ -30,7 +30,8 @@ _ACT = {"relu": PI_RELU, "reglu": PI_REGLU}
 
 class PiError(RuntimeError):
     def __init__(self, status: int, where: str):
-        super().__init__(f"{where}: {status_str(status)} ({status})")
+        detail = f" [{lib().pi_last_hip_error().decode()}]" if status == PI_EHIP else ""
+        super().__init__(f"{where}: {status_str(status)} ({status}){detail}")
         self.status = status
 
 
@@ -47,7 +48,13 @@ class PiLayer(ctypes.Structure):
 
 class PiTrace(ctypes.Structure):
     _fields_ = [("x_in", ctypes.c_void_p), ("scores", ctypes.c_void_p), ("mask", ctypes.c_void_p),
-                ("idx", ctypes.c_void_p), ("count", ctypes.c_void_p)]
+                ("idx", ctypes.c_void_p), ("count", ctypes.c_void_p),
+                ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32)]
+
+
+# kernels of one layer, in the order the trace events bracket them
+LAYER_KERNELS = {1: ("k_predict_t", "k_score", "k_down"),
+                 2: ("k_bglue", "k_bpred1", "k_bsplit_t", "k_bscore", "k_compact", "k_bup", "k_bdown")}
 
 
 _lib = None
@@ -72,6 +79,7 @@ def lib():
         L.pi_sparse_ffn.restype = ctypes.c_int
         L.pi_ffn_stack.argtypes = [P, I32, P, I32, P, P, P, P, SZ, P]
         L.pi_ffn_stack.restype = ctypes.c_int
+        L.pi_last_hip_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -202,10 +210,21 @@ def sparse_ffn(layer: DeviceLayer, x, idx, count, y, mask=None, ws=None, batch: 
 
 
 def make_trace(n_layers: int, recs: Sequence[dict]):
+    """Trace records; a record's optional "events" entry is a list of hipEvent_t handles
+    (ints, e.g. from HipEvents) or objects with a .cuda_event handle."""
     arr = (PiTrace * n_layers)()
+    keep = []
     for i, r in enumerate(recs):
+        evs = r.get("events")
+        if evs:
+            ptrs = (ctypes.c_void_p * len(evs))(*[e if isinstance(e, int) else e.cuda_event for e in evs])
+            keep.append(ptrs)
+            ev_arg, n_ev = ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), len(evs)
+        else:
+            ev_arg, n_ev = None, 0
         arr[i] = PiTrace(_p(r.get("x_in")), _p(r.get("scores")), _p(r.get("mask")),
-                         _p(r.get("idx")), _p(r.get("count")))
+                         _p(r.get("idx")), _p(r.get("count")), ev_arg, n_ev)
+    arr._keep = keep
     return arr
 
 
@@ -230,5 +249,107 @@ def ffn_stack(layers, x, out, counts=None, trace=None, ws=None, batch: int = 1, 
     Stack(layers, batch, ws)(x, out, counts, trace, stream)
 
 
+# ------------------------------------------------------- HIP runtime plumbing
+_hip = None
+
+
+def hip_runtime():
+    """The HIP runtime (libamdhip64) for graphs and timing events."""
+    global _hip
+    if _hip is None:
+        H = ctypes.CDLL("libamdhip64.so")
+        P = ctypes.c_void_p
+        H.hipGetErrorString.restype = ctypes.c_char_p
+        H.hipEventCreate.argtypes = [ctypes.POINTER(P)]
+        H.hipEventDestroy.argtypes = [P]
+        H.hipEventRecord.argtypes = [P, P]
+        H.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+        H.hipStreamBeginCapture.argtypes = [P, ctypes.c_int]
+        H.hipStreamEndCapture.argtypes = [P, ctypes.POINTER(P)]
+        H.hipGraphInstantiate.argtypes = [ctypes.POINTER(P), P, P, P, ctypes.c_size_t]
+        H.hipGraphLaunch.argtypes = [P, P]
+        H.hipGraphExecDestroy.argtypes = [P]
+        H.hipGraphDestroy.argtypes = [P]
+        H.hipStreamCreate.argtypes = [ctypes.POINTER(P)]
+        H.hipStreamDestroy.argtypes = [P]
+        H.hipStreamSynchronize.argtypes = [P]
+        _hip = H
+    return _hip
+
+
+def _hip_check(r: int, where: str):
+    if r != 0:
+        raise RuntimeError(f"{where}: {hip_runtime().hipGetErrorString(r).decode()} ({r})")
+
+
+class HipEvent:
+    """A timing hipEvent_t; int(ev) is the handle."""
+
+    def __init__(self):
+        self.h = ctypes.c_void_p()
+        _hip_check(hip_runtime().hipEventCreate(ctypes.byref(self.h)), "hipEventCreate")
+
+    def __int__(self):
+        return int(self.h.value)
+
+    def record(self, stream):
+        _hip_check(hip_runtime().hipEventRecord(self.h, _stream(stream)), "hipEventRecord")
+
+    def elapsed_ms(self, later: "HipEvent") -> float:
+        ms = ctypes.c_float()
+        _hip_check(hip_runtime().hipEventElapsedTime(ctypes.byref(ms), self.h, later.h), "hipEventElapsedTime")
+        return float(ms.value)
+
+    def __del__(self):
+        if _hip is not None and self.h:
+            _hip.hipEventDestroy(self.h)
+
+
+class HipStream:
+    """A plain hipStream_t (default flags and priority); .cuda_stream is the handle."""
+
+    def __init__(self):
+        self.h = ctypes.c_void_p()
+        _hip_check(hip_runtime().hipStreamCreate(ctypes.byref(self.h)), "hipStreamCreate")
+
+    @property
+    def cuda_stream(self) -> int:
+        return int(self.h.value)
+
+    def synchronize(self):
+        _hip_check(hip_runtime().hipStreamSynchronize(self.h), "hipStreamSynchronize")
+
+    def __del__(self):
+        if _hip is not None and self.h:
+            _hip.hipStreamDestroy(self.h)
+
+
+class HipGraph:
+    """Stream capture of fn(stream) into an instantiated hipGraph, replayed on that stream.
+
+    Only library calls belong inside fn: nothing in it may allocate."""
+
+    def __init__(self, stream, fn):
+        H = hip_runtime()
+        self.stream = _stream(stream)
+        self.g, self.ge = ctypes.c_void_p(), ctypes.c_void_p()
+        _hip_check(H.hipStreamBeginCapture(self.stream, 0), "hipStreamBeginCapture")  # global mode
+        try:
+            fn(stream)
+        finally:
+            _hip_check(H.hipStreamEndCapture(self.stream, ctypes.byref(self.g)), "hipStreamEndCapture")
+        _hip_check(H.hipGraphInstantiate(ctypes.byref(self.ge), self.g, None, None, 0), "hipGraphInstantiate")
+
+    def replay(self):
+        _hip_check(hip_runtime().hipGraphLaunch(self.ge, self.stream), "hipGraphLaunch")
+
+    def __del__(self):
+        if _hip is not None:
+            if self.ge:
+                _hip.hipGraphExecDestroy(self.ge)
+            if self.g:
+                _hip.hipGraphDestroy(self.g)
+
+
 EXPORTED = ("pi_workspace_bytes", "pi_predict", "pi_sparse_ffn", "pi_ffn_stack", "pi_status_str",
-            "pi_abi_version")
+            "pi_abi_version", "pi_last_hip_error")

@@ -415,16 +415,39 @@ void b_glue(const float* x_prev, const float* y_prev, int batch, int d, float* x
 }
 
 // per-sequence scores and masks, the union and its ascending list
+// events[i] of a trace record, if it asks for one.  Under stream capture an
+// event-record node is appended to the graph being captured (after the
+// stream's current capture dependencies, which it then replaces), so that
+// every replay stamps the event; otherwise the event is recorded on the stream.
+void mark(const pi_trace* tr, int i, hipStream_t st) {
+  if (!tr || !tr->events || i >= tr->n_events || !tr->events[i]) return;
+  hipEvent_t ev = static_cast<hipEvent_t>(tr->events[i]);
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipGraph_t g = nullptr;
+  const hipGraphNode_t* deps = nullptr;
+  size_t nd = 0;
+  if (hipStreamGetCaptureInfo_v2(st, &cs, nullptr, &g, &deps, &nd) != hipSuccess) return;  // error stays pending
+  if (cs == hipStreamCaptureStatusActive) {
+    hipGraphNode_t node = nullptr;
+    if (hipGraphAddEventRecordNode(&node, g, deps, nd, ev) == hipSuccess)
+      (void)hipStreamUpdateCaptureDependencies(st, &node, 1, hipStreamSetCaptureDependencies);
+    return;
+  }
+  (void)hipEventRecord(ev, st);
+}
+
 void b_predict(const pi_layer* L, int batch, const Ws& W, float* scores, uint8_t* mask_out, int32_t* ulist,
-               int32_t* ucount, int32_t* ucount2, hipStream_t st) {
+               int32_t* ucount, int32_t* ucount2, hipStream_t st, const pi_trace* tr = nullptr) {
   const int ks = bksplit(L->rank);
   const dim3 g1(cdiv(L->rank, kBatchM) * ks);
   if (L->p_dtype == PI_F16)
     hipLaunchKernelGGL(pib::k_bpred1<DT_F16>, g1, dim3(256), 0, st, L->A, L->rank, L->d, ks, W.xh, W.xl, W.tpart);
   else
     hipLaunchKernelGGL(pib::k_bpred1<DT_F32>, g1, dim3(256), 0, st, L->A, L->rank, L->d, ks, W.xh, W.xl, W.tpart);
+  mark(tr, 2, st);
   hipLaunchKernelGGL(pib::k_bsplit_t, dim3(cdiv(kBatchM * L->rank, 256)), dim3(256), 0, st, W.tpart, ks, L->rank,
                      W.th, W.tl);
+  mark(tr, 3, st);
   const dim3 g2(cdiv(cdiv(L->ffn, kBatchM), 4));
   const float* pb = L->pbias ? L->pbias : L->bias;
   if (L->p_dtype == PI_F16)
@@ -433,39 +456,47 @@ void b_predict(const pi_layer* L, int batch, const Ws& W, float* scores, uint8_t
   else
     hipLaunchKernelGGL(pib::k_bscore<DT_F32>, g2, dim3(256), 0, st, L->B, pb, L->ffn, L->rank, batch, W.th, W.tl,
                        W.mnm, W.mask, W.cnt, scores, mask_out);
+  mark(tr, 4, st);
   hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, ulist, ucount, ucount2);
+  mark(tr, 5, st);
 }
 
 template <int WT, int ACT>
 void b_ffn_t(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, const int32_t* ucount, float* y,
-             hipStream_t st) {
+             hipStream_t st, const pi_trace* tr) {
   hipLaunchKernelGGL((pib::k_bup<WT, ACT>), dim3(cdiv(cdiv(L->ffn, kBatchM), 4)), dim3(256), 0, st, L->gate.w,
                      L->gate.scale, L->up.w, L->up.scale, L->bias, L->ffn, L->d, W.xh, W.xl, ulist, ucount, W.mnm,
                      W.hh, W.hl);
+  mark(tr, 6, st);
   hipLaunchKernelGGL(pib::k_bdown<WT>, dim3(cdiv(L->d, kBatchM)), dim3(256), 0, st, L->downT.w, L->downT.scale,
                      L->ffn, L->d, ulist, ucount, W.hh, W.hl, L->b_down, batch, y);
+  mark(tr, 7, st);
 }
 
 // the FFN over the union list for every sequence: y [batch][d]
 void b_ffn(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, const int32_t* ucount, float* y,
-           hipStream_t st) {
+           hipStream_t st, const pi_trace* tr = nullptr) {
   const bool reglu = L->act == PI_REGLU;
   switch (L->w_dtype) {
     case PI_F32:
-      return reglu ? b_ffn_t<DT_F32, ACT_REGLU>(L, batch, W, ulist, ucount, y, st)
-                   : b_ffn_t<DT_F32, ACT_RELU>(L, batch, W, ulist, ucount, y, st);
+      return reglu ? b_ffn_t<DT_F32, ACT_REGLU>(L, batch, W, ulist, ucount, y, st, tr)
+                   : b_ffn_t<DT_F32, ACT_RELU>(L, batch, W, ulist, ucount, y, st, tr);
     case PI_F16:
-      return reglu ? b_ffn_t<DT_F16, ACT_REGLU>(L, batch, W, ulist, ucount, y, st)
-                   : b_ffn_t<DT_F16, ACT_RELU>(L, batch, W, ulist, ucount, y, st);
+      return reglu ? b_ffn_t<DT_F16, ACT_REGLU>(L, batch, W, ulist, ucount, y, st, tr)
+                   : b_ffn_t<DT_F16, ACT_RELU>(L, batch, W, ulist, ucount, y, st, tr);
     default:
-      return reglu ? b_ffn_t<DT_Q4, ACT_REGLU>(L, batch, W, ulist, ucount, y, st)
-                   : b_ffn_t<DT_Q4, ACT_RELU>(L, batch, W, ulist, ucount, y, st);
+      return reglu ? b_ffn_t<DT_Q4, ACT_REGLU>(L, batch, W, ulist, ucount, y, st, tr)
+                   : b_ffn_t<DT_Q4, ACT_RELU>(L, batch, W, ulist, ucount, y, st, tr);
   }
 }
 
+thread_local hipError_t g_last_hip = hipSuccess;   // behind this thread's last PI_EHIP
+
 pi_status launch_status() {
   const hipError_t e = hipGetLastError();
-  return e == hipSuccess ? PI_OK : PI_EHIP;
+  if (e == hipSuccess) return PI_OK;
+  g_last_hip = e;
+  return PI_EHIP;
 }
 
 }  // namespace
@@ -473,6 +504,8 @@ pi_status launch_status() {
 extern "C" {
 
 int32_t pi_abi_version(void) { return PI_ABI_VERSION; }
+
+const char* pi_last_hip_error(void) { return hipGetErrorString(g_last_hip); }
 
 const char* pi_status_str(pi_status s) {
   switch (s) {
@@ -566,14 +599,16 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
       const pi_layer* L = &layers[l];
       const pi_trace* tr = trace ? &trace[l] : nullptr;
       const int cur = l & 1, prv = cur ^ 1;
+      mark(tr, 0, st);
       b_glue(l == 0 ? x : W.x[prv], l == 0 ? nullptr : W.y[prv], batch, L->d, W.x[cur], tr ? tr->x_in : nullptr,
              W, st);
+      mark(tr, 1, st);
       b_predict(L, batch, W, tr ? tr->scores : nullptr, tr ? tr->mask : nullptr, W.ulist, W.misc,
-                counts ? counts + l : nullptr, st);
+                counts ? counts + l : nullptr, st, tr);
       if (tr && (tr->idx || tr->count))   // the union list and count for the record
         hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, tr->idx ? tr->idx : W.ulist,
                            tr->count ? tr->count : W.misc + 1, nullptr);
-      b_ffn(L, batch, W, W.ulist, W.misc, W.y[cur], st);
+      b_ffn(L, batch, W, W.ulist, W.misc, W.y[cur], st, tr);
     }
     const int last = (n_layers - 1) & 1;
     hipLaunchKernelGGL(pib::k_bglue_out, dim3(batch), dim3(256), sizeof(float) * D.d, st, W.x[last], W.y[last],
@@ -585,10 +620,13 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
     const pi_layer* L = &layers[l];
     const pi_trace* tr = trace ? &trace[l] : nullptr;
     const int cur = l & 1, prv = cur ^ 1;
+    mark(tr, 0, st);
     k1(L, K1Args{l == 0 ? x : W.x[prv], l == 0 ? nullptr : W.y[prv], np_prev, W.x[cur], tr ? tr->x_in : nullptr,
                  W.t}, st);
+    mark(tr, 1, st);
     k2(L, true, K2Args{W.t, W.x[cur], tr ? tr->scores : nullptr, W.mask, tr ? tr->mask : nullptr, W.cnt, W.h},
        st);
+    mark(tr, 2, st);
     int32_t* c1 = counts ? counts + l : nullptr;
     int32_t* c2 = (tr && tr->count && !tr->idx) ? tr->count : nullptr;
     if (tr && tr->idx)   // ascending list for the record; the down projection reads the mask bytes directly
@@ -596,6 +634,7 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
                          tr->count ? tr->count : W.misc, nullptr);
     np_prev = k3<false>(L, K3Args{W.mask, W.h, nullptr, nullptr, nullptr, W.y[cur], W.cnt, k2_blocks(L), c1, c2},
                         st);
+    mark(tr, 3, st);
   }
   {
     const int last = (n_layers - 1) & 1;

@@ -1,29 +1,41 @@
 #!/usr/bin/env python3
 """Decode-time sparse-FFN benchmark on one MI355X.
 
-A step is one decode token (batch 1) through a whole FFN stack: for every
-layer the predictor, threshold and compaction, the gathered up/gate GEMV with
-its activation, the down projection over the active neurons and the residual
-RMS glue -- every step of the hot path, in the library's HIP kernels, behind
-the C ABI.  Token t's input is its own seeded x ~ N(0, I); weights are the
-seeded synthetic workload (Zipf firing probabilities, hot-first storage) at
-the real FFN shapes, generated on the host and resident in HBM before the
-timed region starts.
+A step is one decode token through a whole FFN stack (batch 1), or one decode
+step of B independent sequences (--batch B): for every layer the predictor,
+threshold and compaction, the gathered up/gate projection with its
+activation, the down projection over the active neurons and the residual RMS
+glue -- every step of the hot path, in the library's HIP kernels, behind the
+C ABI.  Token t's input is its own seeded x ~ N(0, I) per sequence; weights
+are the seeded synthetic workload (Zipf firing probabilities, hot-first
+storage) at the real FFN shapes, generated on the host and resident in HBM
+before the timed region starts.
 
 Default workload: the LLaMA(ReLU)-2-7B-shaped ReGLU stack (32 layers, d=4096,
 ffn=11008, predictor rank 1024, fp16 weights and predictor, fp32
 accumulation), 8 warm-up and 128 timed tokens, token-major (weights are
 re-streamed for every token).
 
+Timing: one HIP graph per token slot, replayed on one stream, bracketed by
+events; the median of the repeats is reported.  In every fourth token graph
+the kernels of one layer (rotating over the layers) are bracketed by event
+nodes, so per-kernel durations are sampled live over the timed region on the
+stream the kernels run on.  An event node adds a fixed cost to each interval;
+it is estimated in the same run as (sum of a layer's kernel intervals - the
+uninstrumented time per layer) / kernels per layer, and subtracted.
+
 Prints one JSON line: tokens/s, the HBM roofline of the dominant kernel on
-algorithmic (active) bytes, and the CPU oracle timed on a bounded sample of
-the same tokens.
+algorithmic (active) bytes, the active-byte rate of the whole step, and the
+CPU oracle timed on a bounded sample of the same tokens.
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -44,26 +56,82 @@ def parse():
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--config", type=int, default=1, help="workload index (0..4)")
+    ap.add_argument("--batch", type=int, default=1, help="sequences per decode step (1..32)")
     ap.add_argument("--layers", type=int, default=0, help="override the number of layers (0 = all)")
     ap.add_argument("--order", default="hot_first", choices=["hot_first", "identity"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle budget (a bounded sample of the same tokens); 0 = skip")
     ap.add_argument("--repeats", type=int, default=3, help="timed repeats; the median is reported")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the stack directly instead of replaying graphs (for counter runs)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="first run a plain elementwise copy of this many MiB (counter calibration)")
+    ap.add_argument("--dump-counts", default="", help="write the per-token active counts here (JSON)")
     return ap.parse_args()
 
 
-def layer_bytes(cfg, k):
-    """Algorithmic HBM bytes of one layer for one token at batch 1 with k active neurons.
-
-    Dense predictor (A, B), the predictor bias, the active rows of gate/up and
-    down with their bias, the index list, and the x/y vectors.  Rows of
-    inactive neurons are not counted.
-    """
+def sizes(cfg):
     pb = {"f32": 4, "f16": 2}[cfg.p_dtype]
     wb = {"f32": 4.0, "f16": 2.0, "q4_0": 18.0 / 32.0}[cfg.w_dtype]
     n_mat = 3 if cfg.act == "reglu" else 2
+    return pb, wb, n_mat
+
+
+def kernel_bytes(cfg, batch, k):
+    """Algorithmic HBM bytes of one launch of each kernel of a layer, k active (union) neurons.
+
+    Dense predictor (A, B) and its bias, the active rows of gate/up with their
+    bias, the active rows of W_down^T with their h values, and the x/y vectors
+    of the glue.  Rows of inactive neurons, scratch buffers and re-reads are
+    not counted.  The per-kernel figures sum to the per-layer formula
+    (r*d + f*r)*pb + 4f + k*(n_mat*d*wb + 4) + 4k + 8*d*B.
+    """
+    pb, wb, n_mat = sizes(cfg)
     d, f, r = cfg.d, cfg.ffn, cfg.rank
-    return (r * d + f * r) * pb + 4 * f + k * (n_mat * d * wb + 4) + 4 * k + 8 * d
+    n_up = n_mat - 1
+    if batch == 1:
+        return {"k_predict_t": r * d * pb + 8 * d,
+                "k_score": f * r * pb + 4 * f + k * (n_up * d * wb + 4),
+                "k_down": k * d * wb + 4 * k}
+    return {"k_bglue": 8 * d * batch, "k_bpred1": r * d * pb, "k_bsplit_t": 0,
+            "k_bscore": f * r * pb + 4 * f, "k_compact": 0,
+            "k_bup": k * (n_up * d * wb + 4), "k_bdown": k * d * wb + 4 * k}
+
+
+def layer_bytes(cfg, k, batch=1):
+    return float(sum(kernel_bytes(cfg, batch, k).values()))
+
+
+def source_digest():
+    """sha256 over the HIP sources; counter summaries taken on other sources do not apply."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "activation_sparse_predict_amd", "csrc", "*"))):
+        with open(p, "rb") as fh:
+            h.update(os.path.basename(p).encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(kernel, workload, batch):
+    """HBM bytes per launch from a committed counter summary, or None.
+
+    The summary under profiles/ carries machine-readable lines
+    `kernel:`, `workload:`, `batch:`, `source_sha256:`,
+    `traffic_bytes_per_launch:` and `alg_bytes_per_launch:`; it applies only
+    while the HIP sources hash to the recorded digest.
+    """
+    digest = source_digest()
+    for p in sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md"))):
+        kv = {}
+        with open(p) as fh:
+            for line in fh:
+                m = re.match(r"^- ([a-z_0-9]+): `([^`]+)`$", line.strip())
+                if m:
+                    kv[m.group(1)] = m.group(2)
+        if (kv.get("kernel") == kernel and kv.get("workload") == workload
+                and kv.get("batch") == str(batch) and kv.get("source_sha256") == digest):
+            return {"traffic": float(kv["traffic_bytes_per_launch"]),
+                    "alg": float(kv["alg_bytes_per_launch"]), "file": os.path.relpath(p, ROOT)}
+    return None
 
 
 def main():
@@ -71,6 +139,10 @@ def main():
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); "
               "the sparse FFN is not sharded across GPUs here.", file=sys.stderr)
+        sys.exit(2)
+    B = args.batch
+    if not 1 <= B <= 32:
+        print("bench.py: --batch must be in 1..32", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -89,73 +161,144 @@ def main():
     if args.layers:
         cfg = cfg.with_(n_layers=args.layers)
     nthr = min(16, os.cpu_count() or 1)
-    W, K = args.warmup, args.steps
-    log(f"[bench] {cfg.name}: L={cfg.n_layers} d={cfg.d} f={cfg.ffn} r={cfg.rank} "
-        f"{cfg.w_dtype}/{cfg.p_dtype} {cfg.act}; warmup {W}, steps {K}")
+    W, K, L = args.warmup, args.steps, cfg.n_layers
+    kernels = pi.LAYER_KERNELS[1 if B == 1 else 2]
+    log(f"[bench] {cfg.name}: L={L} d={cfg.d} f={cfg.ffn} r={cfg.rank} "
+        f"{cfg.w_dtype}/{cfg.p_dtype} {cfg.act}; batch {B}; warmup {W}, steps {K}")
 
-    # ---- weights: generated per layer on the host, uploaded, host copy kept
-    # only for the layers the CPU oracle will need (all of them, when it runs)
+    stream = torch.cuda.Stream()
+    if args.calib_copy_mb:
+        # a plain elementwise map (read n bytes, write n bytes) for counter calibration
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: 3 x {args.calib_copy_mb} MiB read + write")
+        del src, dst
+
+    # ---- weights: generated per layer on the host, uploaded; host copies kept
+    # for the CPU oracle only
     t0 = time.time()
     keep_host = args.cpu_seconds > 0
     host, layers = [], []
-    for l in range(cfg.n_layers):
+    for l in range(L):
         lw = workload.make_layer(cfg, l, order=args.order, nthreads=nthr)
         layers.append(pi.DeviceLayer.upload(lw, dev))
         if keep_host:
             host.append(lw)
         del lw
     torch.cuda.synchronize()
-    wbytes = sum(L.nbytes() for L in layers)
+    wbytes = sum(Ld.nbytes() for Ld in layers)
     log(f"[bench] generated + uploaded {wbytes / 1e9:.2f} GB in {time.time() - t0:.1f} s")
 
-    xs_host = workload.make_tokens(cfg, W + K)[:, 0, :]          # [W+K][d] float32
+    xs_host = workload.make_tokens(cfg, W + K, seqs=B)              # [W+K][B][d] float32
     xs = torch.from_numpy(np.ascontiguousarray(xs_host)).to(dev)
     outs = torch.empty_like(xs)
-    counts = torch.zeros((W + K, cfg.n_layers), dtype=torch.int32, device=dev)
+    counts = torch.zeros((W + K, L), dtype=torch.int32, device=dev)
+    stack = pi.Stack(layers, batch=B)
 
-    stream = torch.cuda.Stream()
-    stack = pi.Stack(layers)
+    # ---- every EVERY-th token slot: events around the kernels of one layer
+    n_ev = len(kernels) + 1
+    EVERY = 4
+    events, traces, ev_layer = {}, {}, {}
+    for t in range(W + K):
+        if t % EVERY:
+            traces[t] = None
+            continue
+        l = (t // EVERY) % L
+        evs = [pi.HipEvent() for _ in range(n_ev)]
+        recs = [dict() for _ in range(L)]
+        recs[l] = {"events": [int(e) for e in evs]}
+        events[t], ev_layer[t] = evs, l
+        traces[t] = pi.make_trace(L, recs)
 
-    # ---- one HIP graph per token slot (x_t -> out_t, counts_t), captured once
-    with torch.cuda.stream(stream):
-        stack(xs[0], outs[0], counts[0], stream=stream)          # eager warm-up of the path
+    def run_token(t, s):
+        stack(xs[t], outs[t], counts[t], traces[t], stream=s)
+
+    run_token(0, stream)                                           # eager warm-up of the path
     stream.synchronize()
     graphs = []
-    for t in range(W + K):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            stack(xs[t], outs[t], counts[t], stream=torch.cuda.current_stream())
-        graphs.append(g)
-    torch.cuda.synchronize()
-    log(f"[bench] captured {len(graphs)} token graphs")
+    if not args.eager:
+        for t in range(W + K):
+            graphs.append(pi.HipGraph(stream, lambda s, t=t: run_token(t, s)))
+        torch.cuda.synchronize()
+        log(f"[bench] captured {len(graphs)} token graphs")
+
+    def replay(t):
+        if args.eager:
+            run_token(t, stream)
+        else:
+            graphs[t].replay()
 
     times = []
+    kdur = {k: [] for k in kernels}      # ms per launch
+    kbytes = {k: [] for k in kernels}    # algorithmic bytes of the same launches
+    ev0, ev1 = pi.HipEvent(), pi.HipEvent()
     for rep in range(args.repeats):
-        with torch.cuda.stream(stream):
-            for t in range(W):
-                graphs[t].replay()
-            ev0 = torch.cuda.Event(enable_timing=True)
-            ev1 = torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            ev0.record(stream)
-            for t in range(W, W + K):
-                graphs[t].replay()
-            ev1.record(stream)
+        for t in range(W):
+            replay(t)
         torch.cuda.synchronize()
-        ms = ev0.elapsed_time(ev1)
+        ev0.record(stream)
+        for t in range(W, W + K):
+            replay(t)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_ms(ev1)
         times.append(ms)
-        log(f"[bench] repeat {rep}: {K} tokens in {ms:.3f} ms ({K / ms * 1e3:.1f} tok/s)")
+        cnt_rep = counts.cpu().numpy()
+        for t in range(W, W + K):
+            if t not in events:
+                continue
+            kb = kernel_bytes(cfg, B, int(cnt_rep[t, ev_layer[t]]))
+            evs = events[t]
+            for i, k in enumerate(kernels):
+                kdur[k].append(evs[i].elapsed_ms(evs[i + 1]))
+                kbytes[k].append(kb[k])
+        log(f"[bench] repeat {rep}: {K} steps in {ms:.3f} ms ({B * K / ms * 1e3:.1f} tok/s)")
     ms = float(np.median(times))
     ms_per_step = ms / K
 
     cnt = counts[W:].cpu().numpy().astype(np.int64)                # [K][L]
-    alg_bytes = float(sum(layer_bytes(cfg, int(k)) for k in cnt.ravel())) / K   # per token
-    achieved = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    if args.dump_counts:
+        with open(args.dump_counts, "w") as fh:
+            json.dump({"workload": cfg.name, "config": args.config, "layers": L, "batch": B,
+                       "warmup": W, "steps": K, "repeats": args.repeats,
+                       "counts": counts.cpu().numpy().tolist()}, fh)
+    step_bytes = float(sum(layer_bytes(cfg, int(k), B) for k in cnt.ravel())) / K
+    stack_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     mean_active = float(cnt.mean() / cfg.ffn)
-    log(f"[bench] mean active {mean_active:.4f}, {alg_bytes / 1e6:.2f} MB/token, "
-        f"{achieved:.1f} GB/s ({achieved / HBM_PEAK_GBS:.3f} of peak)")
+    log(f"[bench] mean active {mean_active:.4f}, {step_bytes / 1e6:.2f} MB/step, "
+        f"{stack_gbs:.1f} GB/s over the whole step ({stack_gbs / HBM_PEAK_GBS:.3f} of peak)")
 
-    # ---- CPU oracle on a bounded sample of the same tokens
+    # ---- per-kernel durations sampled over the timed region, less the event-node cost
+    per_kernel = {}
+    layer_plain_us = ms_per_step * 1e3 / L
+    raw_layer_us = sum(float(np.mean(kdur[k])) * 1e3 for k in kernels)
+    node_us = max(0.0, (raw_layer_us - layer_plain_us) / len(kernels))
+    for k in kernels:
+        raw = np.asarray(kdur[k]) * 1e3
+        d_us = np.maximum(raw - node_us, 1e-3)
+        b = np.asarray(kbytes[k], dtype=np.float64)
+        per_kernel[k] = {"avg_us": float(d_us.mean()), "raw_interval_us": float(raw.mean()),
+                         "launches": int(d_us.size), "alg_bytes_per_launch": float(b.mean()),
+                         "gbs": float(b.sum() / (d_us.sum() * 1e-6) / 1e9) if b.sum() else 0.0}
+        log(f"[bench]   {k:12s} {per_kernel[k]['avg_us']:8.2f} us (interval {raw.mean():6.2f})  "
+            f"{per_kernel[k]['alg_bytes_per_launch'] / 1e6:8.3f} MB  {per_kernel[k]['gbs']:8.1f} GB/s")
+    layer_us = sum(v["avg_us"] for v in per_kernel.values())
+    log(f"[bench]   event node cost {node_us:.2f} us per interval (layer: intervals {raw_layer_us:.2f} us, "
+        f"uninstrumented {layer_plain_us:.2f} us)")
+    dom = max(kernels, key=lambda k: per_kernel[k]["avg_us"])
+    dk = per_kernel[dom]
+    tr = counter_traffic(dom, cfg.name, B)
+    traffic = None
+    if tr is not None:
+        # counters are per launch of the profiled run; scale to this run's launches
+        traffic = tr["traffic"] / tr["alg"] * dk["alg_bytes_per_launch"]
+
+    # ---- CPU oracle on a bounded sample of the same tokens (one sequence at a time)
     cpu = None
     if keep_host:
         import oracle
@@ -167,25 +310,32 @@ def main():
         outs_h = outs.cpu().numpy()
         n_done, errs = 0, []
         tc0 = time.perf_counter()
+        done = False
         for t in range(W, W + K):
-            ref = oracle.stack_forward(host, xs_host[t][None, :])
-            n_done += 1
-            y = ref["out"][0]
-            errs.append(float(np.abs(outs_h[t] - y).max() / max(np.abs(y).max(), 1e-30)))
-            if time.perf_counter() - tc0 >= args.cpu_seconds:
+            for b in range(B):
+                ref = oracle.stack_forward(host, xs_host[t][b][None, :])
+                n_done += 1
+                y = ref["out"][0]
+                errs.append(float(np.abs(outs_h[t][b] - y).max() / max(np.abs(y).max(), 1e-30)))
+                if time.perf_counter() - tc0 >= args.cpu_seconds:
+                    done = True
+                    break
+            if done:
                 break
         tc = time.perf_counter() - tc0
         cpu = {"value": n_done / tc, "unit": "tokens/s", "cores": int(blas_threads),
                "kind": "oracle",
-               "sample": f"first {n_done} timed token(s) through all {cfg.n_layers} layers, "
-                         f"float64 NumPy oracle, {tc:.1f} s",
+               "sample": f"{n_done} sequence-token(s) of the timed steps (first step first) through "
+                         f"all {L} layers, float64 NumPy oracle, {tc:.1f} s",
                "max_rel_err_vs_gpu_out": max(errs)}
-        log(f"[bench] oracle: {n_done} tokens in {tc:.1f} s; max rel err of GPU stack output "
-            f"{max(errs):.2e}")
+        log(f"[bench] oracle: {n_done} sequence-tokens in {tc:.1f} s; max rel err of GPU stack "
+            f"output {max(errs):.2e}")
 
+    metric = ("sparse-FFN tokens/s at batch 1 (1 GPU); active-byte HBM GB/s vs peak" if B == 1
+              else f"sparse-FFN tokens/s at batch {B} (1 GPU); active-byte HBM GB/s vs peak")
     res = {
-        "metric": "sparse-FFN tokens/s at batch 1 (1 GPU)",
-        "value": K / (ms * 1e-3),
+        "metric": metric,
+        "value": B * K / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
@@ -196,14 +346,20 @@ def main():
         "vs_baseline": None,
         "dtype": "f16" if cfg.w_dtype == "f16" else cfg.w_dtype,
         "data": "synthetic",
-        "config": {"workload": cfg.name, "layers": cfg.n_layers, "d": cfg.d, "ffn": cfg.ffn,
-                   "rank": cfg.rank, "batch": 1, "act": cfg.act, "w_dtype": cfg.w_dtype,
+        "config": {"workload": cfg.name, "layers": L, "d": cfg.d, "ffn": cfg.ffn,
+                   "rank": cfg.rank, "batch": B, "act": cfg.act, "w_dtype": cfg.w_dtype,
                    "p_dtype": cfg.p_dtype, "order": args.order, "mean_active": mean_active,
-                   "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "pi_ffn_stack, one token (all kernels of all layers)",
-                     "alg_bytes_per_launch": alg_bytes},
+                   "graphs": not args.eager, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": dk["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dk["gbs"] / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": dom, "avg_launch_us": dk["avg_us"],
+                     "alg_bytes_per_launch": dk["alg_bytes_per_launch"],
+                     "launches_timed": dk["launches"], "event_node_us_subtracted": node_us,
+                     "traffic_unit": "HBM bytes per launch (counter summary "
+                                     + (tr["file"] if tr else "absent or stale") + ")"},
+        "stack_hbm": {"achieved": stack_gbs, "frac": stack_gbs / HBM_PEAK_GBS, "unit": "GB/s",
+                      "alg_bytes_per_step": step_bytes},
+        "kernels": per_kernel,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define PI_ABI_VERSION 1
+#define PI_ABI_VERSION 2
 
 typedef enum {
   PI_OK = 0,
@@ -102,6 +102,15 @@ typedef struct {
   uint8_t* mask;    /* [batch][ffn] 1 if score > 0 */
   int32_t* idx;     /* [ffn]        ascending storage ids of the union mask */
   int32_t* count;   /* [1]          number of entries in idx */
+  /* Timing: hipEvent_t handles (as void*) recorded on the stream, events[0]
+   * before the layer's first kernel and events[i] after its i-th kernel, for
+   * i < n_events.  Kernels of a layer, in order -- batch 1: predictor GEMV 1
+   * with the glue, scores with the fused up/gate gather, down projection;
+   * batch > 1: glue, predictor GEMM 1, its split sum, scores and union, union
+   * compaction, up/gate GEMM, down GEMM.  Record-only kernels of the trace
+   * (list compaction) are not counted. */
+  void** events;
+  int32_t n_events;
 } pi_trace;
 
 /* Workspace needed by any entry point for these layers at this batch.
@@ -156,6 +165,9 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
 
 const char* pi_status_str(pi_status s);
 int32_t pi_abi_version(void);
+/* Name of the HIP error behind the calling thread's most recent PI_EHIP
+ * ("no error" before any).  Static string, not to be freed. */
+const char* pi_last_hip_error(void);
 
 #ifdef __cplusplus
 }

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(pi):
 
 
 def test_abi_version_and_status_strings(pi):
-    assert pi.abi_version() == 1
+    assert pi.abi_version() == 2
     assert pi.status_str(0) == "ok"
     assert "workspace" in pi.status_str(3)
 
@@ -144,3 +144,27 @@ def test_batched_validation(pi):
     assert 0 < n1 < n8 < n32
     r = lib.pi_predict(ctypes.byref(L), FAKE, 8, None, FAKE, FAKE, FAKE, FAKE, n8 - 1, None)
     assert r == 3
+
+
+def test_struct_layouts_match_the_header(pi, tmp_path):
+    """ctypes mirrors of pi_mat / pi_layer / pi_trace have the C compiler's sizes and offsets."""
+    src = tmp_path / "layout.c"
+    fields = {"pi_mat": [f for f, _ in pi.PiMat._fields_], "pi_layer": [f for f, _ in pi.PiLayer._fields_],
+              "pi_trace": [f for f, _ in pi.PiTrace._fields_]}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "pi.h"', "int main(void) {"]
+    for st, fs in fields.items():
+        lines.append(f'  printf("{st} %zu\\n", sizeof({st}));')
+        for f in fs:
+            lines.append(f'  printf("{st}.{f} %zu\\n", offsetof({st}, {f}));')
+    lines += ["  return 0;", "}"]
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = dict(line.rsplit(" ", 1) for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                              text=True).stdout.split("\n") if line)
+    for st, cls in (("pi_mat", pi.PiMat), ("pi_layer", pi.PiLayer), ("pi_trace", pi.PiTrace)):
+        assert int(out[st]) == ctypes.sizeof(cls), st
+        for f in fields[st]:
+            assert int(out[f"{st}.{f}"]) == getattr(cls, f).offset, f"{st}.{f}"

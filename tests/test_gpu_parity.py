@@ -289,6 +289,46 @@ def test_stack_deterministic_and_graph_replay():
         _ = (torch.randn(1000, device=DEV) * 2).sum().item()   # unrelated eager work
 
 
+@pytest.mark.parametrize("nb", [1, 8])
+def test_trace_events_in_hip_graph(nb):
+    """Timing events of a trace record, eager and as event nodes of a captured graph (the
+    benchmark's launch setup): every kernel interval is positive, the output is unchanged."""
+    cfg = SMALL["f16-reglu"]
+    say(f"[events] batch {nb}: per-kernel events, eager and in a captured graph")
+    layers = [pi.DeviceLayer.upload(h, DEV) for h in host_layers(cfg)]
+    n, nk = cfg.n_layers, len(pi.LAYER_KERNELS[1 if nb == 1 else 2])
+    stack = pi.Stack(layers, batch=nb)
+    x = dev(workload.make_x(cfg, 5, seqs=nb))
+    ref = torch.empty(nb, cfg.d, device=DEV)
+    stack(x, ref)
+    torch.cuda.synchronize()
+    evs = [[pi.HipEvent() for _ in range(nk + 1)] for _ in range(n)]
+    trace = pi.make_trace(n, [{"events": [int(e) for e in ev]} for ev in evs])
+    s = torch.cuda.Stream()
+    out = torch.full((nb, cfg.d), float("nan"), device=DEV)
+    torch.cuda.synchronize()
+    stack(x, out, None, trace, stream=s)
+    s.synchronize()
+    assert torch.equal(out.cpu(), ref.cpu())
+    eager = [[ev[i].elapsed_ms(ev[i + 1]) for i in range(nk)] for ev in evs]
+    assert all(v > 0 for row in eager for v in row), eager
+    graph = pi.HipGraph(s, lambda st: stack(x, out, None, trace, stream=st))
+    for rep in range(3):
+        for ev in evs:                  # stamp in reverse order: every interval <= 0 until replayed
+            for e in reversed(ev):
+                e.record(s)
+        s.synchronize()
+        assert all(ev[i].elapsed_ms(ev[i + 1]) <= 0 for ev in evs for i in range(nk))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        s.synchronize()
+        assert torch.equal(out.cpu(), ref.cpu()), rep
+        replayed = [[ev[i].elapsed_ms(ev[i + 1]) for i in range(nk)] for ev in evs]
+        assert all(v > 0 for row in replayed for v in row), replayed
+    say(f"  layer 0 kernel intervals (ms), graph: {[round(v, 4) for v in replayed[0]]}")
+
+
 # ------------------------------------------------------------------ full size
 FULL_CASES = [(0, 1, 16), (1, 2, 3), (2, 2, 2), (3, 2, 2), (4, 2, 2)]
 
