@@ -60,7 +60,7 @@ struct Dims {
 };
 
 constexpr int kMaxParts = 4;       // neuron splits of the down projection (partial y vectors)
-constexpr int kMaxK2Blocks = 1 << 16;
+constexpr int kK2Grid = 512;   // two per compute unit of an MI355X
 
 int epl_of(int dt) { return dt == PI_F32 ? 4 : (dt == PI_F16 ? 8 : 32); }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -68,6 +68,8 @@ int cdiv(int a, int b) { return (a + b - 1) / b; }
 // Grid size of the predictor kernel (one active count per block): at most this.
 int k2_blocks_for(int ffn, int rank, int p_dtype);
 int k2_blocks_max(int ffn);
+// blocks of the batched score kernel: 4 waves of 32 neurons each
+int bscore_blocks(int ffn) { return cdiv(cdiv(ffn, pib::BM), 4); }
 
 struct WsLayout {
   size_t t, xbuf, ybuf, mask, h, cnt, misc;
@@ -91,7 +93,7 @@ WsLayout layout(const Dims& D, int batch) {
   w.ybuf = o; o += w.ys * 2;
   w.mask = o; o += align_up(fpad);                       // one byte per neuron (the union when batch > 1)
   w.h = o;    o += align_up(sizeof(float) * (size_t)D.fmax);
-  w.cnt = o;  o += align_up(sizeof(int32_t) * (size_t)k2_blocks_max(D.fmax));
+  w.cnt = o;  o += align_up(sizeof(int32_t) * (size_t)std::max(k2_blocks_max(D.fmax), bscore_blocks(D.fmax)));
   w.misc = o; o += kAlign;
   if (batch > 1) {
     w.xh = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * D.d);
@@ -192,10 +194,14 @@ int k2_wch(const pi_layer* L) {
   return L->w_dtype == PI_F32 ? pick(kWchF32, n) : L->w_dtype == PI_F16 ? pick(kWchF16, n) : pick(kWchQ4, n);
 }
 // about one batch of B rows per wave, and at least ~4 waves per CU when ffn allows
+// K2: two blocks of K2_WAVES waves per CU at most, each wave with one batch
+// of rows of B when the layer is small enough, several batches (in turn) when
+// it is not.  Two blocks on some CUs and one on others would make the CUs with
+// two the kernel's tail.
 int k2_blocks_for(int ffn, int rank, int p_dtype) {
-  const int rb = 16 / k2_pch_of(rank, p_dtype);
-  const int nw = std::max(cdiv(ffn, rb), std::min(1024, cdiv(ffn, 4)));
-  return std::min(kMaxK2Blocks, std::max(1, cdiv(nw, K2_WAVES)));
+  (void)rank;
+  (void)p_dtype;
+  return std::max(1, std::min(kK2Grid, cdiv(ffn, 2 * K2_WAVES)));   // at least two rows per wave
 }
 int k2_blocks(const pi_layer* L) { return k2_blocks_for(L->ffn, L->rank, L->p_dtype); }
 int k2_blocks_max(int ffn) { return std::max(k2_blocks_for(ffn, 64, PI_F32), k2_blocks_for(ffn, 1 << 20, PI_F32)); }
@@ -265,7 +271,7 @@ struct K2Args {
 
 template <int PT, int WT, int ACT, bool FUSE, int PCH, int WCH>
 void launch_k2_t(const pi_layer* L, const K2Args& a, hipStream_t st) {
-  const size_t lds = sizeof(float) * ((size_t)L->rank + (FUSE ? (size_t)L->d : 0));
+  const size_t lds = sizeof(float) * ((size_t)K2_WAVES * dma_pad(L->rank) + (FUSE ? (size_t)dma_pad(L->d) : 0));
   hipLaunchKernelGGL((k_score<PT, WT, ACT, FUSE, PCH, WCH>), dim3(k2_blocks(L)), dim3(K2_WAVES * WAVE), lds, st,
                      L->B, L->pbias ? L->pbias : L->bias, L->bias, a.t, L->ffn, L->rank, L->gate.w, L->gate.scale,
                      L->up.w, L->up.scale, a.xcur, L->d, a.scores, a.mask, a.mask2, a.cnt, a.h);
@@ -448,7 +454,7 @@ void b_predict(const pi_layer* L, int batch, const Ws& W, float* scores, uint8_t
   hipLaunchKernelGGL(pib::k_bsplit_t, dim3(cdiv(kBatchM * L->rank, 256)), dim3(256), 0, st, W.tpart, ks, L->rank,
                      W.th, W.tl);
   mark(tr, 3, st);
-  const dim3 g2(cdiv(cdiv(L->ffn, kBatchM), 4));
+  const dim3 g2(bscore_blocks(L->ffn));
   const float* pb = L->pbias ? L->pbias : L->bias;
   if (L->p_dtype == PI_F16)
     hipLaunchKernelGGL(pib::k_bscore<DT_F16>, g2, dim3(256), 0, st, L->B, pb, L->ffn, L->rank, batch, W.th, W.tl,

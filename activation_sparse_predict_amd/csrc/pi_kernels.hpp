@@ -221,20 +221,41 @@ __device__ __forceinline__ void stage_f32(float* __restrict__ lds, const float* 
   }
 }
 
-// The two halves of stage_f32's first round, so that other loads can be
-// issued between them.
-template <int MAXV>
-__device__ __forceinline__ void load_f32(float4 (&v)[MAXV], const float* __restrict__ g, int n, int tid, int nthr) {
-  const int nv = n / 4;
-#pragma unroll
-  for (int j = 0; j < MAXV; ++j) v[j] = reinterpret_cast<const float4*>(g)[min(j * nthr + tid, nv - 1)];
+// ------------------------------------------------------------- LDS-DMA
+// A value the compiler cannot see through (an SGPR set by inline asm).  Adding
+// it to the addresses of a batch of loads makes them depend on this point of
+// the program, so they cannot be hoisted above it.
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+  return z;
 }
-template <int MAXV>
-__device__ __forceinline__ void store_f32(float* __restrict__ lds, const float4 (&v)[MAXV], int n, int tid,
-                                          int nthr) {
-  const int nv = n / 4;
-#pragma unroll
-  for (int j = 0; j < MAXV; ++j) reinterpret_cast<float4*>(lds)[min(j * nthr + tid, nv - 1)] = v[j];
+
+// Wait until at most N vector-memory loads of this wave are outstanding and
+// all its LDS operations are done.  Loads complete in issue order, so this
+// waits for everything issued before the last N.
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+// LDS floats that dma_f32 writes for n floats: whole 1 KB pieces.
+__host__ __device__ constexpr int dma_pad(int n) { return (n + 255) / 256 * 256; }
+
+// Copy n floats (n % 4 == 0, g 16-byte aligned) from global memory straight
+// into lds[0, dma_pad(n)) with LDS-DMA loads (global_load_lds_dwordx4): lane i
+// of a wave-wide load lands at 16 i bytes past the piece's base.  Wave w of nw
+// issues 1 KB pieces w, w + nw, ...; lanes past n read the last vector again
+// and write the padding.  No registers hold the data, so the loads cannot be
+// sunk to a later use; the data is in LDS once this wave's vmcnt has passed
+// them, and visible to the other waves after a barrier that follows that wait.
+__device__ __forceinline__ void dma_f32(float* lds, const float* g, int n, int w, int nw, int lane) {
+  const int nv = n / 4, npc = (nv + 63) / 64;
+  for (int c = w; c < npc; c += nw)
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(g + 4 * min(c * 64 + lane, nv - 1)),
+        (__attribute__((address_space(3))) void*)(lds + c * 256), 16, 0, 0);
 }
 
 // v = x + sum_{p < np} y[p] (np <= 4 partial vectors of n floats, added in the
@@ -411,21 +432,25 @@ k_predict_t(const void* __restrict__ A, int r, int d, const float* __restrict__ 
 // ----------------------------------------------------------------------- K2
 // Scores s_i = c_i + B[i] . t, threshold s_i > 0, one mask byte per neuron,
 // and -- if FUSE -- the gathered up/gate GEMV with ReLU or ReGLU for the active
-// neurons.  Global wave g owns neurons i = g + NW m (interleaved, so the
-// hot-first order spreads the frequently active rows over all waves).  A wave
+// neurons.  The neurons are dealt to the blocks round-robin (so the hot-first
+// order spreads the frequently active rows evenly over the blocks).  Each
+// wave copies t into its own LDS slice and the block copies x' into LDS, both
+// by LDS-DMA issued ahead of the rows of B, so no barrier and no register
+// staging stands between the rows' arrival and the first multiply.  A wave
 // loads RB = 16 / PCH rows of B (PCH 16-byte chunks per lane each) before its
-// first multiply and reduces the RB dot products with one transposed
-// butterfly.  The block's active neurons then go to a list in LDS and its
-// waves take them two at a time (gate and up rows of both, WCH chunks per lane
-// per row, in one HBM round trip): the number of actives per wave varies a
-// lot, per block much less, and the slowest wave sets the kernel's time.
+// first multiply and reduces the RB dot products with one butterfly each.
+// The waves' active neurons then go to per-wave lists in LDS (ballot order,
+// no atomics) and the block's waves take the concatenated list two at a time
+// (gate and up rows of both, WCH chunks per lane per row, in one HBM round
+// trip): the number of actives per wave varies a lot, per block much less,
+// and the slowest wave sets the kernel's time.
 // The block's active count goes to cnt_blk[block] (summed over batches).
 // Global stores come after the block barrier so that the barrier does not wait
 // for them.
 constexpr int K2_WAVES = 4;
 
 template <int PT, int WT, int ACT, bool FUSE, int PCH, int WCH>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(K2_WAVES * WAVE) __attribute__((amdgpu_waves_per_eu(2)))
 k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const float* __restrict__ bias,
         const float* __restrict__ t, int f, int r,
         const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc,
@@ -436,21 +461,24 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
   constexpr int RB = 16 / PCH;                               // rows of B per batch
   constexpr int PEPL = Tr<PT>::EPL, PTW = WAVE * PEPL;
   extern __shared__ float smem[];
-  float* ts = smem;          // [r]
-  float* xs = smem + r;      // [d] (FUSE only)
-  // per-batch active lists and counters, three in rotation: batch b appends to
-  // slot b % 3 before its barrier and reads it after; slot (b + 2) % 3, last
-  // read before barrier b by every wave, is cleared after it for batch b + 2
-  __shared__ int act[3][K2_WAVES * RB];
-  __shared__ int nact[3];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  const int NW = gridDim.x * K2_WAVES, g = blockIdx.x * K2_WAVES + w;
+  float* ts = smem + w * dma_pad(r);               // this wave's own copy of t [dma_pad(r)]
+  float* xs = smem + K2_WAVES * dma_pad(r);        // x' [dma_pad(d)] (FUSE only)
+  // per-batch active lists, one per wave (in row order) with its length, two
+  // slots in rotation: batch b writes slot b % 2 before its barrier and reads
+  // it after; batch b + 2 writes it again only after barrier b + 1, which no
+  // wave passes before every wave is done reading batch b's lists
+  __shared__ int act[2][K2_WAVES][RB];
+  __shared__ int nact[2][K2_WAVES];
+  // wave w of block b owns neurons i = b + nb (w + K2_WAVES m), m = 0, 1, ...:
+  // the block index runs fastest, so every block gets an equal share of each
+  // stretch of the hot-first order and the blocks' active counts are alike
+  const int nb = gridDim.x, b = blockIdx.x, NW = nb * K2_WAVES;
+  const int g = b + nb * w;                                  // the wave's first neuron
   const int M = g < f ? (f - 1 - g) / NW + 1 : 0;            // neurons of this wave
-  const int g0 = blockIdx.x * K2_WAVES;                      // the block's first wave has the most
-  const int Mb = g0 < f ? (f - 1 - g0) / NW + 1 : 0;         // block-uniform trip count
+  const int Mb = b < f ? (f - 1 - b) / NW + 1 : 0;           // wave 0 has the most: block-uniform trip count
   const int pch = (r + PTW - 1) / PTW;
   const int my_u = min(lane, RB - 1);                        // lane u < RB reports row u of the batch
-  if (tid < 3) nact[tid] = 0;
 
   // Rows past the wave's last neuron (all rows, for a wave without neurons)
   // and chunks past the row end load a clamped, valid address and are
@@ -458,31 +486,26 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
   uint4 bc[RB][PCH];
   float pb = 0.f;
   auto nrow = [&](int m) __attribute__((always_inline)) { return min(g + NW * max(min(m, M - 1), 0), f - 1); };
-  auto issue = [&](int m0, int q0) __attribute__((always_inline)) {
+  auto issue = [&](int m0, int q0, int z) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
-      const size_t row = (size_t)nrow(m0 + u);
+      const size_t row = (size_t)(nrow(m0 + u) + z);
 #pragma unroll
       for (int q = 0; q < PCH; ++q)
         bc[u][q] = ld_chunk<PT>(Bm, row, r, min(min(q0 + q, pch - 1) * PTW + lane * PEPL, r - PEPL));
     }
-    if (q0 == 0) pb = pbias[nrow(m0 + my_u)];
+    if (q0 == 0) pb = pbias[nrow(m0 + my_u) + z];
     PI_ISSUE_FENCE();
   };
 
-  // t and x' are staged in LDS; their first rounds are issued unconditionally
-  // ahead of the rows of B, longer vectors finish after
-  const int nthr = blockDim.x;
-  float4 tv[1], xv[8];
-  load_f32<1>(tv, t, r, tid, nthr);
-  if constexpr (FUSE) load_f32<8>(xv, xcur, d, tid, nthr);
-  PI_ISSUE_FENCE();
-  issue(0, 0);
-  store_f32<1>(ts, tv, r, tid, nthr);
-  if constexpr (FUSE) store_f32<8>(xs, xv, d, tid, nthr);
-  if (r > 4 * nthr) stage_f32<4>(ts, t, r, tid, nthr, nthr);
-  if (FUSE && d > 32 * nthr) stage_f32<8>(xs, xcur, d, tid, nthr, 8 * nthr);
-  __syncthreads();
+  // t (a copy per wave, so that no barrier stands between it and the first
+  // dot products) and x' (shared; first read after the score barrier) go to
+  // LDS by LDS-DMA ahead of the first rows of B.  The rows' addresses depend on
+  // an opaque zero taken after the copies are issued, so the rows stay behind
+  // them and t arrives while the rows are still in flight.
+  dma_f32(ts, t, r, 0, 1, lane);
+  if constexpr (FUSE) dma_f32(xs, xcur, d, w, K2_WAVES, lane);
+  issue(0, 0, opaque_zero());
 
   int block_count = 0;
   for (int m0 = 0, batch = 0; m0 < Mb; m0 += RB, ++batch) {
@@ -490,7 +513,7 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
 #pragma unroll
     for (int u = 0; u < RB; ++u) acc[u] = 0.f;
     for (int q0 = 0; q0 < pch; q0 += PCH) {
-      if (q0 > 0) issue(m0, q0);
+      if (q0 > 0) issue(m0, q0, 0);
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
 #pragma unroll
@@ -514,14 +537,27 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
     const float s = dot + pb;
     const bool on = rep && s > 0.f;
 
-    const int par = batch % 3;
-    if (on) act[par][atomicAdd(&nact[par], 1)] = i;          // LDS atomic
+    const int par = batch & 1;
+    const uint64_t bal = __ballot(on);                       // lanes u < RB: rows in order
+    if (on) act[par][w][__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = i;
+    if (lane == 0) nact[par][w] = __popcll(bal);
     __syncthreads();
-    const int n = nact[par];
-    if (tid == 0) {
-      nact[(batch + 2) % 3] = 0;
-      block_count += n;
-    }
+    // the block's list is the waves' lists one after another; entry a is in
+    // the list of the wave whose prefix bounds it
+    int pre[K2_WAVES + 1];
+    pre[0] = 0;
+#pragma unroll
+    for (int v = 0; v < K2_WAVES; ++v) pre[v + 1] = pre[v] + nact[par][v];
+    const int n = pre[K2_WAVES];
+    auto entry = [&](int a) __attribute__((always_inline)) {
+      int ww = 0, base = 0;
+#pragma unroll
+      for (int v = 1; v < K2_WAVES; ++v)
+        if (a >= pre[v]) { ww = v; base = pre[v]; }
+      return act[par][ww][a - base];
+    };
+    if (tid == 0) block_count += n;
+    if (m0 + RB < Mb) issue(m0 + RB, 0, 0);    // the next batch's rows of B, in flight during the gather
     if (rep) {
       if (scores) scores[i] = s;
       mask[i] = on ? 1 : 0;
@@ -536,7 +572,7 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
       constexpr bool PAIR = NMAT * WCH <= 16;
       for (int a = w; a < n; a += (PAIR ? 2 : 1) * K2_WAVES) {
         if (PAIR && a + K2_WAVES < n) {
-          const int rows[2] = {act[par][a], act[par][a + K2_WAVES]};
+          const int rows[2] = {entry(a), entry(a + K2_WAVES)};
           const float b0 = bias[rows[0]], b1 = bias[rows[1]];
           float z[2][NMAT];
           gather_rows<WT, WCH, NMAT, 2>(w0, s0, up_w, up_sc, rows, d, xs, lane, z);
@@ -545,7 +581,7 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
             h_full[rows[1]] = (ACT == ACT_RELU) ? fmaxf(z[1][0] + b1, 0.f) : fmaxf(z[1][0] + b1, 0.f) * z[1][NMAT - 1];
           }
         } else {
-          const int rows[1] = {act[par][a]};
+          const int rows[1] = {entry(a)};
           const float b0 = bias[rows[0]];
           float z[1][NMAT];
           gather_rows<WT, WCH, NMAT, 1>(w0, s0, up_w, up_sc, rows, d, xs, lane, z);
@@ -554,7 +590,6 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
         }
       }
     }
-    if (m0 + RB < Mb) issue(m0 + RB, 0);       // the next batch's rows of B
   }
   if (tid == 0 && cnt_blk) cnt_blk[blockIdx.x] = block_count;
 }

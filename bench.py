@@ -21,8 +21,8 @@ events; the median of the repeats is reported.  In every fourth token graph
 the kernels of one layer (rotating over the layers) are bracketed by event
 nodes, so per-kernel durations are sampled live over the timed region on the
 stream the kernels run on.  An event node adds a fixed cost to each interval;
-it is estimated in the same run as (sum of a layer's kernel intervals - the
-uninstrumented time per layer) / kernels per layer, and subtracted.
+it is measured in the same run by pairing each such slot with one that
+brackets only the whole layer, and subtracted.
 
 Prints one JSON line: tokens/s, the HBM roofline of the dominant kernel on
 algorithmic (active) bytes, the active-byte rate of the whole step, and the
@@ -190,6 +190,8 @@ def main():
         if keep_host:
             host.append(lw)
         del lw
+        if (l + 1) % 8 == 0 and l + 1 < L:
+            log(f"[bench]   layer {l + 1}/{L} generated ({time.time() - t0:.0f} s)")
     torch.cuda.synchronize()
     wbytes = sum(Ld.nbytes() for Ld in layers)
     log(f"[bench] generated + uploaded {wbytes / 1e9:.2f} GB in {time.time() - t0:.1f} s")
@@ -200,19 +202,25 @@ def main():
     counts = torch.zeros((W + K, L), dtype=torch.int32, device=dev)
     stack = pi.Stack(layers, batch=B)
 
-    # ---- every EVERY-th token slot: events around the kernels of one layer
+    # ---- every EVERY-th token slot carries events on one layer, in pairs of
+    # slots on the same layer: a "full" slot brackets each kernel of the layer,
+    # the next an "ends" slot brackets only the whole layer.  An event node adds
+    # a cost c to each interval, so (sum of full intervals - ends interval) =
+    # (kernels - 1) c.
     n_ev = len(kernels) + 1
     EVERY = 4
-    events, traces, ev_layer = {}, {}, {}
+    events, traces, ev_layer, ev_full = {}, {}, {}, {}
     for t in range(W + K):
         if t % EVERY:
             traces[t] = None
             continue
-        l = (t // EVERY) % L
-        evs = [pi.HipEvent() for _ in range(n_ev)]
+        pidx = t // EVERY
+        l = (7 * (pidx // 2)) % L
+        full = pidx % 2 == 0
+        evs = [pi.HipEvent() if (full or i in (0, n_ev - 1)) else None for i in range(n_ev)]
         recs = [dict() for _ in range(L)]
-        recs[l] = {"events": [int(e) for e in evs]}
-        events[t], ev_layer[t] = evs, l
+        recs[l] = {"events": [int(e) if e is not None else 0 for e in evs]}
+        events[t], ev_layer[t], ev_full[t] = evs, l, full
         traces[t] = pi.make_trace(L, recs)
 
     def run_token(t, s):
@@ -236,6 +244,7 @@ def main():
     times = []
     kdur = {k: [] for k in kernels}      # ms per launch
     kbytes = {k: [] for k in kernels}    # algorithmic bytes of the same launches
+    pair_full, pair_ends = {}, {}        # per (repeat, pair): sum of kernel intervals / whole layer
     ev0, ev1 = pi.HipEvent(), pi.HipEvent()
     for rep in range(args.repeats):
         for t in range(W):
@@ -252,10 +261,15 @@ def main():
         for t in range(W, W + K):
             if t not in events:
                 continue
+            evs, key = events[t], (rep, t // (2 * EVERY))
+            if not ev_full[t]:
+                pair_ends[key] = evs[0].elapsed_ms(evs[n_ev - 1])
+                continue
             kb = kernel_bytes(cfg, B, int(cnt_rep[t, ev_layer[t]]))
-            evs = events[t]
+            iv = [evs[i].elapsed_ms(evs[i + 1]) for i in range(len(kernels))]
+            pair_full[key] = sum(iv)
             for i, k in enumerate(kernels):
-                kdur[k].append(evs[i].elapsed_ms(evs[i + 1]))
+                kdur[k].append(iv[i])
                 kbytes[k].append(kb[k])
         log(f"[bench] repeat {rep}: {K} steps in {ms:.3f} ms ({B * K / ms * 1e3:.1f} tok/s)")
     ms = float(np.median(times))
@@ -275,9 +289,10 @@ def main():
 
     # ---- per-kernel durations sampled over the timed region, less the event-node cost
     per_kernel = {}
-    layer_plain_us = ms_per_step * 1e3 / L
-    raw_layer_us = sum(float(np.mean(kdur[k])) * 1e3 for k in kernels)
-    node_us = max(0.0, (raw_layer_us - layer_plain_us) / len(kernels))
+    pairs = sorted(set(pair_full) & set(pair_ends))
+    raw_layer_us = float(np.mean([pair_full[p] for p in pairs])) * 1e3 if pairs else 0.0
+    ends_layer_us = float(np.mean([pair_ends[p] for p in pairs])) * 1e3 if pairs else 0.0
+    node_us = max(0.0, (raw_layer_us - ends_layer_us) / (len(kernels) - 1)) if pairs else 0.0
     for k in kernels:
         raw = np.asarray(kdur[k]) * 1e3
         d_us = np.maximum(raw - node_us, 1e-3)
@@ -288,8 +303,8 @@ def main():
         log(f"[bench]   {k:12s} {per_kernel[k]['avg_us']:8.2f} us (interval {raw.mean():6.2f})  "
             f"{per_kernel[k]['alg_bytes_per_launch'] / 1e6:8.3f} MB  {per_kernel[k]['gbs']:8.1f} GB/s")
     layer_us = sum(v["avg_us"] for v in per_kernel.values())
-    log(f"[bench]   event node cost {node_us:.2f} us per interval (layer: intervals {raw_layer_us:.2f} us, "
-        f"uninstrumented {layer_plain_us:.2f} us)")
+    log(f"[bench]   event node cost {node_us:.2f} us per interval ({len(pairs)} layer pairs: kernel intervals "
+        f"{raw_layer_us:.2f} us, whole layer {ends_layer_us:.2f} us; step/L {ms_per_step * 1e3 / L:.2f} us)")
     dom = max(kernels, key=lambda k: per_kernel[k]["avg_us"])
     dk = per_kernel[dom]
     tr = counter_traffic(dom, cfg.name, B)
