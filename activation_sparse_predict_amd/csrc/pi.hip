@@ -30,6 +30,9 @@ pi_status check_mat(const pi_mat& m, int32_t dtype) {
   return PI_OK;
 }
 
+constexpr int kMaxD = 16384;
+constexpr int kMaxRank = 4096;
+
 pi_status check_layer(const pi_layer* L) {
   if (!L) return PI_EINVAL;
   if (L->d <= 0 || L->ffn <= 0 || L->rank <= 0) return PI_EINVAL;
@@ -37,6 +40,7 @@ pi_status check_layer(const pi_layer* L) {
   if (L->act != PI_RELU && L->act != PI_REGLU) return PI_EINVAL;
   if (L->w_dtype != PI_F32 && L->w_dtype != PI_F16 && L->w_dtype != PI_Q4_0) return PI_EINVAL;
   if (L->p_dtype == PI_Q4_0) return PI_EUNSUPPORTED;
+  if (L->d > kMaxD || L->rank > kMaxRank) return PI_EUNSUPPORTED;   // vectors staged whole in LDS
   if (L->p_dtype != PI_F32 && L->p_dtype != PI_F16) return PI_EINVAL;
   if (!L->A || !L->B || !L->bias) return PI_EINVAL;
   if (!aligned(L->A, 16) || !aligned(L->B, 16) || !aligned(L->bias, 16)) return PI_EINVAL;
@@ -220,7 +224,9 @@ K3Shape k3_shape(int d, int dt) {
   K3Shape s;
   s.twc = nchunks >= 64 ? 4 : nchunks >= 32 ? 2 : 1;
   s.ct = cdiv(nchunks, s.twc);
-  s.nc = std::max(1, std::min(kMaxParts, cdiv(256, s.ct)));
+  // the next layer's predictor kernel stages x and the NC partials in LDS
+  const int lds_parts = 147456 / (4 * dma_pad(d)) - 1;
+  s.nc = std::max(1, std::min(std::min(kMaxParts, lds_parts), cdiv(256, s.ct)));
   return s;
 }
 
@@ -237,7 +243,7 @@ struct K1Args {
 template <int PT, int NCH>
 void launch_k1_t(const pi_layer* L, const K1Args& a, hipStream_t st) {
   hipLaunchKernelGGL((k_predict_t<PT, NCH>), dim3(k1_blocks(L->rank)), dim3(K1_WAVES * WAVE),
-                     sizeof(float) * L->d, st, L->A, L->rank, L->d, a.x_prev, a.y_prev, a.y_np, a.x_out,
+                     sizeof(float) * (size_t)dma_pad(L->d) * (1 + a.y_np), st, L->A, L->rank, L->d, a.x_prev, a.y_prev, a.y_np, a.x_out,
                      a.x_trace, a.t);
 }
 

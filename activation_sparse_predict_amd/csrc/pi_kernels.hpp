@@ -357,11 +357,14 @@ __device__ __forceinline__ void gather_rows(const void* __restrict__ w0, const u
 // ----------------------------------------------------------------------- K1
 // t = A x', x' = glue(x_prev, y_prev) if y_np > 0 else x_prev, with glue
 // v = x_prev + y_prev, x' = v / sqrt(mean(v^2) + 1e-6) and y_prev given as y_np
-// partial vectors that are added in order.  One wave per row of A; the wave
-// issues the loads of its row (NCH chunks per lane per round) before the block
-// computes x', so the glue hides under the HBM latency.  Every block computes
-// the same x' with the same operation order, so all agree bit for bit.
-// Blocks also write their slice of x'.
+// partial vectors that are added in order.  One wave per row of A.  x_prev
+// and the partials go to LDS by LDS-DMA first; the row of A (NCH chunks per
+// lane per round) is issued after them, its addresses depending on an opaque
+// zero, so the glue waits only for the copies and runs while the row is in
+// flight.  The dot product takes v and the row's result is scaled by
+// 1 / sqrt(mean(v^2) + 1e-6).  Every block computes the same v and scale with
+// the same operation order, so all agree bit for bit; each block writes its
+// slice of x'.
 constexpr int K1_WAVES = 4;
 
 template <int PT, int NCH>
@@ -369,38 +372,72 @@ __global__ void __launch_bounds__(256)
 k_predict_t(const void* __restrict__ A, int r, int d, const float* __restrict__ x_prev,
             const float* __restrict__ y_prev, int y_np, float* __restrict__ x_out, float* __restrict__ x_trace,
             float* __restrict__ t) {
-  extern __shared__ float xs[];
+  extern __shared__ float smem[];
   __shared__ float red[K1_WAVES];
   constexpr int EPL = Tr<PT>::EPL, TW = WAVE * EPL;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int row = blockIdx.x * K1_WAVES + w;
   const size_t rowc = (size_t)min(row, r - 1);       // a wave without a row reads row r-1 and discards it
   const int nch = (d + TW - 1) / TW;
+  const int dp = dma_pad(d);
+  float* xs = smem;                                   // x_prev, then v [dp]
+  float* ys = smem + dp;                              // the y partials [y_np][dp]
 
+  dma_f32(xs, x_prev, d, w, K1_WAVES, lane);
+  for (int p = 0; p < y_np; ++p) dma_f32(ys + (size_t)p * dp, y_prev + (size_t)p * d, d, w, K1_WAVES, lane);
+  const int z = opaque_zero();
   uint4 c[NCH];
 #pragma unroll
-  for (int q = 0; q < NCH; ++q) c[q] = ld_chunk<PT>(A, rowc, d, min(min(q, nch - 1) * TW + lane * EPL, d - EPL));
+  for (int q = 0; q < NCH; ++q)
+    c[q] = ld_chunk<PT>(A, rowc + z, d, min(min(q, nch - 1) * TW + lane * EPL, d - EPL));
   PI_ISSUE_FENCE();
+  wait_vm_lds<NCH>();                                 // the copies, not the row
+  __builtin_amdgcn_s_barrier();
 
-  float ss = stage_residual<4>(xs, x_prev, y_prev, y_np, d, tid, blockDim.x);
+  const int nv = d / 4;
   if (y_np > 0) {
+    float ss = 0.f;
+    float4* x4 = reinterpret_cast<float4*>(xs);
+    const float4* y4p = reinterpret_cast<const float4*>(ys);
+    for (int k = tid; k < nv; k += blockDim.x) {
+      float4 y4 = y4p[k];
+      for (int p = 1; p < y_np; ++p) {
+        const float4 u = y4p[(size_t)p * (dp / 4) + k];
+        y4.x += u.x;
+        y4.y += u.y;
+        y4.z += u.z;
+        y4.w += u.w;
+      }
+      float4 v = x4[k];
+      v.x += y4.x;
+      v.y += y4.y;
+      v.z += y4.z;
+      v.w += y4.w;
+      x4[k] = v;
+      ss = fmaf(v.x, v.x, ss);
+      ss = fmaf(v.y, v.y, ss);
+      ss = fmaf(v.z, v.z, ss);
+      ss = fmaf(v.w, v.w, ss);
+    }
     ss = wave_sum(ss);
     if (lane == 0) red[w] = ss;
-    __syncthreads();
+  }
+  __syncthreads();
+  float inv = 1.f;
+  if (y_np > 0) {
     float tot = 0.f;
 #pragma unroll
     for (int i = 0; i < K1_WAVES; ++i) tot += red[i];
-    const float inv = 1.0f / sqrtf(tot / (float)d + 1e-6f);
-    for (int k = tid; k < d; k += blockDim.x) xs[k] *= inv;
+    inv = 1.0f / sqrtf(tot / (float)d + 1e-6f);
   }
-  __syncthreads();
 
   {
     const int nb = gridDim.x, b = blockIdx.x;
     const int cx = (d + nb - 1) / nb;
     for (int k = b * cx + tid; k < min(d, (b + 1) * cx); k += blockDim.x) {
-      if (x_out) x_out[k] = xs[k];
-      if (x_trace) x_trace[k] = xs[k];
+      const float xk = y_np > 0 ? xs[k] * inv : xs[k];
+      if (x_out) x_out[k] = xk;
+      if (x_trace) x_trace[k] = xk;
     }
   }
 
@@ -426,7 +463,7 @@ k_predict_t(const void* __restrict__ A, int r, int d, const float* __restrict__ 
     }
   }
   a = wave_sum(a);
-  if (row < r && lane == 0) t[row] = a;
+  if (row < r && lane == 0) t[row] = y_np > 0 ? a * inv : a;
 }
 
 // ----------------------------------------------------------------------- K2

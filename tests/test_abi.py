@@ -92,6 +92,7 @@ def test_workspace_bytes(pi):
     (dict(A=FAKE + 4), 1), (dict(B=None), 1),          # misaligned / missing predictor
     (dict(pbias=FAKE + 4), 1),
     (dict(w_dtype=2), 1),                              # Q4_0 without scales
+    (dict(d=16384 + 64), 2), (dict(rank=4096 + 64), 2),  # beyond the LDS staging limits
 ])
 def test_predict_rejects_bad_layers(pi, kw, status):
     assert predict(pi, make_layer(pi, **kw)) == status
