@@ -58,6 +58,11 @@ pi_status check_batch(int32_t batch) {
   return PI_OK;
 }
 
+// the batched path keeps a split of the union list in LDS
+pi_status check_batched_ffn(const pi_layer* L, int32_t batch) {
+  return (batch > 1 && L->ffn > pib::BD_MAXF) ? PI_EUNSUPPORTED : PI_OK;
+}
+
 // -------------------------------------------------------------- workspace
 struct Dims {
   int d = 0, fmax = 0, rmax = 0;
@@ -72,8 +77,8 @@ int cdiv(int a, int b) { return (a + b - 1) / b; }
 // Grid size of the predictor kernel (one active count per block): at most this.
 int k2_blocks_for(int ffn, int rank, int p_dtype);
 int k2_blocks_max(int ffn);
-// blocks of the batched score kernel: 4 waves of 32 neurons each
-int bscore_blocks(int ffn) { return cdiv(cdiv(ffn, pib::BM), 4); }
+// blocks of the batched score kernel: one tile of 32 neurons each
+int bscore_blocks(int ffn) { return cdiv(ffn, pib::BM); }
 
 struct WsLayout {
   size_t t, xbuf, ybuf, mask, h, cnt, misc;
@@ -91,7 +96,7 @@ WsLayout layout(const Dims& D, int batch) {
   size_t o = 0;
   const size_t fpad = (size_t)cdiv(D.fmax, 16) * 16;
   w.xs = align_up(sizeof(float) * (size_t)D.d * batch);
-  w.ys = align_up(sizeof(float) * (size_t)D.d * std::max(kMaxParts * batch, batch > 1 ? kBatchM : 0));
+  w.ys = align_up(sizeof(float) * (size_t)D.d * (batch > 1 ? pib::BD_SPLIT * kBatchM : kMaxParts));
   w.t = o;    o += align_up(sizeof(float) * (size_t)D.rmax * batch);
   w.xbuf = o; o += w.xs * 2;
   w.ybuf = o; o += w.ys * 2;
@@ -107,8 +112,8 @@ WsLayout layout(const Dims& D, int batch) {
     w.tl = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * D.rmax);
     w.mnm = o;   o += align_up((size_t)kBatchM * D.fmax);
     w.ulist = o; o += align_up(sizeof(int32_t) * (size_t)D.fmax);
-    w.hh = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * D.fmax);
-    w.hl = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * D.fmax);
+    w.hh = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * pib::h_stride(D.fmax));
+    w.hl = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * pib::h_stride(D.fmax));
   }
   w.total = o;
   return w;
@@ -422,8 +427,8 @@ int bksplit(int r) { return std::max(1, std::min(kMaxKSplit, cdiv(256, cdiv(r, k
 // y_prev is NULL) to x_out / x_trace and as fp16 hi/lo operands.
 void b_glue(const float* x_prev, const float* y_prev, int batch, int d, float* x_out, float* x_trace, const Ws& W,
             hipStream_t st) {
-  hipLaunchKernelGGL(pib::k_bglue, dim3(kBatchM), dim3(256), sizeof(float) * d, st, x_prev, y_prev,
-                     y_prev ? 1 : 0, batch, d, x_out, x_trace, W.xh, W.xl);
+  hipLaunchKernelGGL(pib::k_bglue, dim3(kBatchM), dim3(pib::BG_T), 0, st, x_prev, y_prev,
+                     y_prev ? pib::BD_SPLIT : 0, batch, d, x_out, x_trace, W.xh, W.xl);
 }
 
 // per-sequence scores and masks, the union and its ascending list
@@ -476,16 +481,17 @@ void b_predict(const pi_layer* L, int batch, const Ws& W, float* scores, uint8_t
 template <int WT, int ACT>
 void b_ffn_t(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, const int32_t* ucount, float* y,
              hipStream_t st, const pi_trace* tr) {
-  hipLaunchKernelGGL((pib::k_bup<WT, ACT>), dim3(cdiv(cdiv(L->ffn, kBatchM), 4)), dim3(256), 0, st, L->gate.w,
+  hipLaunchKernelGGL((pib::k_bup<WT, ACT>), dim3(cdiv(L->ffn, kBatchM)), dim3(pib::BUP_W * WAVE), 0, st, L->gate.w,
                      L->gate.scale, L->up.w, L->up.scale, L->bias, L->ffn, L->d, W.xh, W.xl, ulist, ucount, W.mnm,
                      W.hh, W.hl);
   mark(tr, 6, st);
-  hipLaunchKernelGGL(pib::k_bdown<WT>, dim3(cdiv(L->d, kBatchM)), dim3(256), 0, st, L->downT.w, L->downT.scale,
-                     L->ffn, L->d, ulist, ucount, W.hh, W.hl, L->b_down, batch, y);
+  hipLaunchKernelGGL(pib::k_bdown<WT>, dim3(cdiv(L->d, kBatchM) * pib::BD_SPLIT), dim3(256), 0, st, L->downT.w,
+                     L->downT.scale, L->ffn, L->d, ulist, ucount, W.hh, W.hl, L->b_down, batch, y);
   mark(tr, 7, st);
 }
 
-// the FFN over the union list for every sequence: y [batch][d]
+// the FFN over the union list for every sequence: BD_SPLIT partial vectors
+// y_part [BD_SPLIT][32][d] (rows b < batch written)
 void b_ffn(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, const int32_t* ucount, float* y,
            hipStream_t st, const pi_trace* tr = nullptr) {
   const bool reglu = L->act == PI_REGLU;
@@ -566,6 +572,7 @@ pi_status pi_sparse_ffn(const pi_layer* layer, const float* x, int32_t batch, co
   pi_status s;
   if ((s = check_layer(layer)) != PI_OK) return s;
   if ((s = check_batch(batch)) != PI_OK) return s;
+  if ((s = check_batched_ffn(layer, batch)) != PI_OK) return s;
   if (!x || !aligned(x, 16) || !idx || !count || !y) return PI_EINVAL;
   if ((batch == 1) != (mask == nullptr)) return PI_EINVAL;
   Dims D{layer->d, layer->ffn, layer->rank};
@@ -581,7 +588,9 @@ pi_status pi_sparse_ffn(const pi_layer* layer, const float* x, int32_t batch, co
     hipLaunchKernelGGL(pib::k_blist, dim3(cdiv(layer->ffn, 256)), dim3(256), 0, st, idx, count, layer->ffn, mask,
                        batch, W.mask, W.mnm);
     hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, layer->ffn, W.ulist, W.misc, nullptr);
-    b_ffn(layer, batch, W, W.ulist, W.misc, y, st);
+    b_ffn(layer, batch, W, W.ulist, W.misc, W.y[0], st);
+    hipLaunchKernelGGL(pib::k_bsum_y, dim3(cdiv(batch * layer->d, 256)), dim3(256), 0, st, W.y[0], batch, layer->d,
+                       y);
     return launch_status();
   }
   up_list(layer, x, idx, count, W.h, st);
@@ -598,6 +607,8 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
   for (int l = 0; l < n_layers; ++l)
     if ((s = check_layer(&layers[l])) != PI_OK) return s;
   if ((s = check_batch(batch)) != PI_OK) return s;
+  for (int l = 0; l < n_layers; ++l)
+    if ((s = check_batched_ffn(&layers[l], batch)) != PI_OK) return s;
   if (!x || !aligned(x, 16) || !out) return PI_EINVAL;
   Dims D;
   if (!dims_of(layers, n_layers, &D)) return PI_EINVAL;
@@ -624,7 +635,7 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
     }
     const int last = (n_layers - 1) & 1;
     hipLaunchKernelGGL(pib::k_bglue_out, dim3(batch), dim3(256), sizeof(float) * D.d, st, W.x[last], W.y[last],
-                       D.d, out);
+                       pib::BD_SPLIT, D.d, out);
     return launch_status();
   }
   int np_prev = 0;

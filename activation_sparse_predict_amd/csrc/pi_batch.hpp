@@ -67,13 +67,16 @@ __device__ __forceinline__ h8v q4_h8(uint4 c, int b0, bool hi_nib) {
 // sum of np partials y[p][b]) (np = 0: x' = x_prev[b]); x' goes to x_out[b]
 // (and x_trace[b]) in fp32 and to xh/xl[b] as fp16 hi/lo.  Rows b >= B are
 // written as zeros in xh/xl so that they contribute nothing to any product.
-__global__ void __launch_bounds__(256)
+constexpr int BG_T = 1024;               // threads of a glue block
+constexpr int BG_V = 4;                  // float4 per thread held at once (d <= 16384)
+
+__global__ void __launch_bounds__(BG_T)
 k_bglue(const float* __restrict__ x_prev, const float* __restrict__ y_part, int np, int B, int d,
         float* __restrict__ x_out, float* __restrict__ x_trace, _Float16* __restrict__ xh,
         _Float16* __restrict__ xl) {
-  extern __shared__ float vs[];
-  __shared__ float red[4];
+  __shared__ float red[BG_T / WAVE];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const int nv = d / 4;
   if (b >= B) {
     for (int k = tid; k < d; k += blockDim.x) {
       xh[(size_t)b * d + k] = (_Float16)0.f;
@@ -82,34 +85,73 @@ k_bglue(const float* __restrict__ x_prev, const float* __restrict__ y_part, int 
     return;
   }
   const size_t ystride = (size_t)BM * d;   // partial p of row b is at y_part + p*32*d + b*d
-  float ss = 0.f;
-  for (int k = tid; k < d; k += blockDim.x) {
-    float v = x_prev[(size_t)b * d + k];
-    if (np > 0) {
-      float yv = y_part[(size_t)b * d + k];
-      for (int p = 1; p < np; ++p) yv += y_part[p * ystride + (size_t)b * d + k];
-      v += yv;
+  const float4* x4 = reinterpret_cast<const float4*>(x_prev + (size_t)b * d);
+  // this thread's float4 elements k = tid + BG_T j; every load is issued before
+  // the first add (indices past the row read its last vector and are dropped)
+  float4 v[BG_V];
+#pragma unroll
+  for (int j = 0; j < BG_V; ++j) v[j] = x4[min(tid + BG_T * j, nv - 1)];
+  if (np > 0) {
+    float4 y[BG_V];
+#pragma unroll
+    for (int j = 0; j < BG_V; ++j)
+      y[j] = reinterpret_cast<const float4*>(y_part + (size_t)b * d)[min(tid + BG_T * j, nv - 1)];
+    for (int p = 1; p < np; ++p) {
+      float4 u[BG_V];
+#pragma unroll
+      for (int j = 0; j < BG_V; ++j)
+        u[j] = reinterpret_cast<const float4*>(y_part + p * ystride + (size_t)b * d)[min(tid + BG_T * j, nv - 1)];
+#pragma unroll
+      for (int j = 0; j < BG_V; ++j) {
+        y[j].x += u[j].x;
+        y[j].y += u[j].y;
+        y[j].z += u[j].z;
+        y[j].w += u[j].w;
+      }
     }
-    vs[k] = v;
-    ss = fmaf(v, v, ss);
+#pragma unroll
+    for (int j = 0; j < BG_V; ++j) {
+      v[j].x += y[j].x;
+      v[j].y += y[j].y;
+      v[j].z += y[j].z;
+      v[j].w += y[j].w;
+    }
   }
   float inv = 1.f;
   if (np > 0) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < BG_V; ++j) {
+      if (tid + BG_T * j < nv) {
+        ss = fmaf(v[j].x, v[j].x, ss);
+        ss = fmaf(v[j].y, v[j].y, ss);
+        ss = fmaf(v[j].z, v[j].z, ss);
+        ss = fmaf(v[j].w, v[j].w, ss);
+      }
+    }
     ss = wave_sum(ss);
     if (lane == 0) red[w] = ss;
     __syncthreads();
-    const float tot = red[0] + red[1] + red[2] + red[3];
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < BG_T / WAVE; ++i) tot += red[i];
     inv = 1.0f / sqrtf(tot / (float)d + 1e-6f);
   }
-  __syncthreads();
-  for (int k = tid; k < d; k += blockDim.x) {
-    const float v = vs[k] * inv;
-    if (x_out) x_out[(size_t)b * d + k] = v;
-    if (x_trace) x_trace[(size_t)b * d + k] = v;
-    _Float16 hh, ll;
-    split_f16(v, &hh, &ll);
-    xh[(size_t)b * d + k] = hh;
-    xl[(size_t)b * d + k] = ll;
+#pragma unroll
+  for (int j = 0; j < BG_V; ++j) {
+    const int k4 = tid + BG_T * j;
+    if (k4 >= nv) continue;
+    const float o[4] = {v[j].x * inv, v[j].y * inv, v[j].z * inv, v[j].w * inv};
+    if (x_out) reinterpret_cast<float4*>(x_out + (size_t)b * d)[k4] = make_float4(o[0], o[1], o[2], o[3]);
+    if (x_trace) reinterpret_cast<float4*>(x_trace + (size_t)b * d)[k4] = make_float4(o[0], o[1], o[2], o[3]);
+    _Float16 hh[4], ll[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split_f16(o[e], &hh[e], &ll[e]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xh[(size_t)b * d + 4 * k4 + e] = hh[e];
+      xl[(size_t)b * d + 4 * k4 + e] = ll[e];
+    }
   }
 }
 
@@ -136,8 +178,9 @@ __device__ __forceinline__ void split8(const float* __restrict__ p, h8v* hi, h8v
 
 // acc += X[rows of this lane][K window] * W[row][K window] over KU steps of 16,
 // starting at k; X given as hi/lo fp16 [32][ldx], W rows contiguous along K.
-// All loads of the window are issued before the first MFMA.  Steps at or past
-// kend load a clamped address and are skipped.
+// All loads of the window are issued before the first MFMA, with no branch
+// among them: steps at or past kend load a clamped address and multiply a
+// zero X operand instead.
 template <int WT>
 __device__ __forceinline__ void mfma_window(f16v& acc, const _Float16* __restrict__ xh,
                                             const _Float16* __restrict__ xl, size_t ldx, const void* __restrict__ W,
@@ -157,13 +200,14 @@ __device__ __forceinline__ void mfma_window(f16v& acc, const _Float16* __restric
     }
   }
   PI_ISSUE_FENCE();
+  const h8v z8 = {};
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
-    if (k + u * kstride < kend) {
-      acc = mfma(ah[u], bw[u], acc);
-      acc = mfma(al[u], bw[u], acc);
-      if constexpr (WT == DT_F32) acc = mfma(ah[u], bl[u], acc);
-    }
+    const bool ok = k + u * kstride < kend;
+    const h8v a = ok ? ah[u] : z8, b = ok ? al[u] : z8;
+    acc = mfma(a, bw[u], acc);
+    acc = mfma(b, bw[u], acc);
+    if constexpr (WT == DT_F32) acc = mfma(a, bl[u], acc);
   }
 }
 
@@ -209,88 +253,118 @@ k_bsplit_t(const float* __restrict__ t_part, int ksplit, int r, _Float16* __rest
 }
 
 // ------------------------------------------------------------ predictor 2
-// s[b][i] = c_i + sum_k t[b][k] B[i][k], one tile of 32 neurons per wave;
-// mask m[i][b] = (s > 0) for b < batch (0 for padded rows), one byte each in
-// neuron-major layout [ffn][32]; union u[i] = OR_b m[i][b]; the block's union
-// count to cnt_blk[block].  Optional outputs in sequence-major layout:
-// scores[b][i] and mask_out[b][i].
+// s[b][i] = c_i + sum_k t[b][k] B[i][k] for one tile of 32 neurons per block,
+// its 4 waves splitting K into contiguous ranges (partials summed through LDS
+// in wave order); mask m[i][b] = (s > 0) for b < batch (0 for padded rows),
+// one byte each in neuron-major layout [ffn][32]; union u[i] = OR_b m[i][b];
+// the tile's union count to cnt_blk[block].  Optional outputs in
+// sequence-major layout: scores[b][i] and mask_out[b][i].
+constexpr int BS_W = 4;
+
 template <int PT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(BS_W * WAVE)
 k_bscore(const void* __restrict__ Bm, const float* __restrict__ pbias, int f, int r, int batch,
          const _Float16* __restrict__ th, const _Float16* __restrict__ tl, uint8_t* __restrict__ m_nm,
          uint8_t* __restrict__ u, int32_t* __restrict__ cnt_blk, float* __restrict__ scores,
          uint8_t* __restrict__ mask_out) {
-  __shared__ int cnt_w[4];
+  __shared__ float red[BS_W][BM * BM];
+  __shared__ int cnt_w;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int col = lane % 32, half = lane / 32;
-  const int tile = blockIdx.x * 4 + w;
-  const int i_raw = tile * BM + col;
-  const int i = min(i_raw, f - 1);
+  const int i0 = blockIdx.x * BM;
+  const int i = min(i0 + col, f - 1);
   f16v acc = {};
-  for (int k = 0; k < r; k += 16 * KU) mfma_window<PT>(acc, th, tl, r, Bm, (size_t)i, r, k, r, 16, lane);
-  const float c = pbias[i];
-  const bool col_ok = i_raw < f;
-  uint32_t on_bits = 0;     // bit 4g+v: row 8g + 4*half + v is active
+  const int ns = r / 16, kbeg = 16 * (w * ns / BS_W), kend = 16 * ((w + 1) * ns / BS_W);
+  for (int k = kbeg; k < kend; k += 16 * KU) mfma_window<PT>(acc, th, tl, r, Bm, (size_t)i, r, k, kend, 16, lane);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    uint32_t word = 0;
+  for (int g = 0; g < 4; ++g)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int b = 8 * g + 4 * half + v;
-      const float s = acc[4 * g + v] + c;
-      const bool on = col_ok && b < batch && s > 0.f;
-      word |= (on ? 1u : 0u) << (8 * v);
-      on_bits |= (on ? 1u : 0u) << (4 * g + v);
-      if (col_ok && b < batch) {
-        if (scores) scores[(size_t)b * f + i] = s;
-        if (mask_out) mask_out[(size_t)b * f + i] = on ? 1 : 0;
+    for (int v = 0; v < 4; ++v) red[w][(8 * g + 4 * half + v) * BM + col] = acc[4 * g + v];
+  if (tid == 0) cnt_w = 0;
+  __syncthreads();
+  // thread (neuron c = tid % 32, batch rows bq = tid / 32 .. step 8): 256 threads
+  // cover the 32 x 32 tile four rows each
+  const int c = tid % BM, ii = i0 + c;
+  const bool col_ok = ii < f;
+  const float cb = pbias[min(ii, f - 1)];
+  uint32_t on_rows = 0;
+#pragma unroll
+  for (int q = 0; q < BM / 8; ++q) {
+    const int b = tid / BM + 8 * q;
+    const int e = b * BM + c;
+    float sacc = red[0][e];
+#pragma unroll
+    for (int v = 1; v < BS_W; ++v) sacc += red[v][e];
+    const float sv = sacc + cb;
+    const bool on = col_ok && b < batch && sv > 0.f;
+    on_rows |= (on ? 1u : 0u) << b;
+    if (col_ok) {
+      m_nm[(size_t)ii * BM + b] = on ? 1 : 0;
+      if (b < batch) {
+        if (scores) scores[(size_t)b * f + ii] = sv;
+        if (mask_out) mask_out[(size_t)b * f + ii] = on ? 1 : 0;
       }
     }
-    if (col_ok) *reinterpret_cast<uint32_t*>(m_nm + (size_t)i * BM + 8 * g + 4 * half) = word;
   }
-  const uint32_t other = (uint32_t)__shfl_xor((int)on_bits, 32, WAVE);
-  const bool un = (on_bits | other) != 0;
-  if (col_ok && half == 0) u[i] = un ? 1 : 0;
-  const int cw = wave_sum((col_ok && half == 0 && un) ? 1 : 0);
-  if (lane == 0) cnt_w[w] = cw;
+  __syncthreads();                          // red is reused below for the union bits
+  reinterpret_cast<uint32_t*>(red[0])[tid] = on_rows;
   __syncthreads();
-  if (tid == 0 && cnt_blk) cnt_blk[blockIdx.x] = cnt_w[0] + cnt_w[1] + cnt_w[2] + cnt_w[3];
+  if (tid < BM) {
+    uint32_t all = 0;
+#pragma unroll
+    for (int q = 0; q < (BS_W * WAVE) / BM; ++q) all |= reinterpret_cast<const uint32_t*>(red[0])[tid + BM * q];
+    const bool un = all != 0;
+    if (col_ok) u[ii] = un ? 1 : 0;
+    if (col_ok && un) atomicAdd(&cnt_w, 1);   // LDS atomic
+  }
+  __syncthreads();
+  if (tid == 0 && cnt_blk) cnt_blk[blockIdx.x] = cnt_w;
 }
 
 // ------------------------------------------------------------ up / gate
-// z = X W^T over the union rows: wave tile q covers union list entries
-// [32 q, 32 q + 32) (blocks past the union's end return).  Epilogue:
-// h[b] = m[i][b] ? act(z + bias) : 0, written as fp16 hi/lo to hh/hl[i][b]
-// (neuron-major, 32 per neuron).
+// z = X W^T over the union rows.  Block q covers union list entries [32 q,
+// 32 q + 32) (blocks past the union's end return); its BUP_W waves split K
+// into contiguous ranges and their partial tiles are summed through LDS in
+// wave order.  Epilogue: h[b] = m[i][b] ? act(z + bias) : 0, written as fp16
+// hi/lo to hh/hl[b][j] (batch-major, j = the neuron's position in the union
+// list), the layout in which the down projection reads it as an MFMA operand.
+constexpr int BUP_W = 8;
+constexpr int BD_CH = 256;               // union positions per chunk of the down projection
+
+// row stride (halves) of the batch-major h: whole chunks, so that a chunk's
+// reads stay inside the row
+__host__ __device__ constexpr int h_stride(int f) { return (f + BD_CH - 1) / BD_CH * BD_CH; }
+
 template <int WT, int ACT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(BUP_W * WAVE)
 k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, const void* __restrict__ up_w,
       const uint16_t* __restrict__ up_sc, const float* __restrict__ bias, int f, int d,
       const _Float16* __restrict__ xh, const _Float16* __restrict__ xl, const int32_t* __restrict__ ulist,
       const int32_t* __restrict__ ucount, const uint8_t* __restrict__ m_nm, _Float16* __restrict__ hh_out,
       _Float16* __restrict__ hl_out) {
+  constexpr int NMAT = (ACT == ACT_RELU) ? 1 : 2;
+  __shared__ float red[BUP_W][NMAT][BM * BM];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int col = lane % 32, half = lane / 32;
   const int n = min(max(*ucount, 0), f);
-  const int t0 = (blockIdx.x * 4 + w) * BM;
-  if (t0 >= n) return;
-  const bool row_ok = t0 + col < n;
+  const int t0 = blockIdx.x * BM;
+  if (t0 >= n) return;                                        // block-uniform
   const int row = ulist[min(t0 + col, n - 1)];
-  constexpr int NMAT = (ACT == ACT_RELU) ? 1 : 2;
   f16v acc[NMAT];
 #pragma unroll
   for (int mt = 0; mt < NMAT; ++mt) acc[mt] = f16v{};
   if constexpr (WT == DT_Q4) {
     // one Q4_0 block (32 k) per step pair: low nibbles give k 0..15, high nibbles k 16..31;
-    // KU / 2 blocks per batch of loads
+    // KU / 2 blocks per batch of loads; this wave's blocks [kb0, kb1)
     constexpr int QB = KU / 2;
-    for (int k = 0; k < d; k += 32 * QB) {
+    const int nq = d / 32, kbeg = 32 * (w * nq / BUP_W), kend = 32 * ((w + 1) * nq / BUP_W);
+    for (int k = kbeg; k < kend; k += 32 * QB) {
       uint4 cq[NMAT][QB];
       float sc[NMAT][QB];
       h8v ah[QB][2], al[QB][2];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int kb = min(k + 32 * qb, d - 32);
+        const int kb = min(k + 32 * qb, kend - 32);
 #pragma unroll
         for (int mt = 0; mt < NMAT; ++mt) {
           const void* wp = (NMAT == 2 && mt == 0) ? gate_w : up_w;
@@ -308,7 +382,7 @@ k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, con
       PI_ISSUE_FENCE();
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        if (k + 32 * qb >= d) continue;
+        if (k + 32 * qb >= kend) continue;
 #pragma unroll
         for (int mt = 0; mt < NMAT; ++mt) {
           f16v p = {};
@@ -325,146 +399,198 @@ k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, con
       }
     }
   } else {
-    for (int k = 0; k < d; k += 16 * KU) {
+    const int ns = d / 16, kbeg = 16 * (w * ns / BUP_W), kend = 16 * ((w + 1) * ns / BUP_W);
+    for (int k = kbeg; k < kend; k += 16 * KU) {
 #pragma unroll
       for (int mt = 0; mt < NMAT; ++mt)
-        mfma_window<WT>(acc[mt], xh, xl, d, (NMAT == 2 && mt == 0) ? gate_w : up_w, (size_t)row, d, k, d, 16,
+        mfma_window<WT>(acc[mt], xh, xl, d, (NMAT == 2 && mt == 0) ? gate_w : up_w, (size_t)row, d, k, kend, 16,
                         lane);
     }
   }
-  // epilogue: lane holds neuron `row`, batch rows 8g + 4*half + v
-  if (row_ok) {
-    const float bi = bias[row];
-    const uint8_t* mrow = m_nm + (size_t)row * BM;
+  // the waves' partial tiles: lane holds neuron column col, batch rows 8g + 4*half + v
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t mw = *reinterpret_cast<const uint32_t*>(mrow + 8 * g + 4 * half);
-      const size_t o = (size_t)row * BM + 8 * g + 4 * half;
+  for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float h;
-        if constexpr (ACT == ACT_RELU) h = fmaxf(acc[0][4 * g + v] + bi, 0.f);
-        else h = fmaxf(acc[0][4 * g + v] + bi, 0.f) * acc[NMAT - 1][4 * g + v];
-        if (((mw >> (8 * v)) & 0xFFu) == 0) h = 0.f;
-        _Float16 a, b;
-        split_f16(h, &a, &b);
-        hh_out[o + v] = a;
-        hl_out[o + v] = b;
-      }
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[w][mt][(8 * g + 4 * half + v) * BM + col] = acc[mt][4 * g + v];
+  __syncthreads();
+  for (int e = tid; e < BM * BM; e += blockDim.x) {
+    const int b = e / BM, c = e % BM;
+    if (t0 + c >= n) continue;
+    float z[NMAT];
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt) {
+      float s = 0.f;
+#pragma unroll
+      for (int v = 0; v < BUP_W; ++v) s += red[v][mt][e];
+      z[mt] = s;
     }
+    const int rw = ulist[t0 + c];
+    float h;
+    if constexpr (ACT == ACT_RELU) h = fmaxf(z[0] + bias[rw], 0.f);
+    else h = fmaxf(z[0] + bias[rw], 0.f) * z[NMAT - 1];
+    if (m_nm[(size_t)rw * BM + b] == 0) h = 0.f;
+    _Float16 a, l;
+    split_f16(h, &a, &l);
+    hh_out[(size_t)b * h_stride(f) + t0 + c] = a;
+    hl_out[(size_t)b * h_stride(f) + t0 + c] = l;
   }
 }
 
 // ------------------------------------------------------------------ down
-// y[b][c] = sum over union neurons i of h[i][b] downT[i][c].  Block = one
-// column tile of 32 columns.  The union list is taken in chunks of 64 rows;
-// each chunk is staged through LDS -- the weight tile transposed to [column]
-// [neuron] (fp32 weights as hi/lo), h to [batch][neuron] as hi/lo (Q4_0: h
-// times the row's block scale, the weights as q - 8) -- and each wave runs
-// one 16-row K step of it.  The global loads of the next KBD_P chunks are in
-// flight while a chunk is processed.  Wave partials are summed in a fixed
-// order; one block writes each y element.
-constexpr int KBD_CH = 64;               // union rows per chunk
-constexpr int KBD_PAD = KBD_CH + 8;      // padded neuron stride (halves) of a transposed row
-constexpr int KBD_P = 4;                 // chunks in flight
+// y[b][c] = sum over union positions j of h[b][j] downT[u_j][c].  Block = one
+// column tile of 32 columns and one of BD_SPLIT splits of the union list,
+// whose partial sums go to y_part[split][b][c] (b < batch; the consumer adds
+// the splits in order, b_down rides on split 0).  A split's share of the
+// list is taken in chunks of BD_CH positions.  The weights of a chunk are
+// staged through LDS transposed to [column][position] -- each thread writes
+// four consecutive positions of a column at once -- as fp16 (fp32 weights
+// and Q4_0 weights times their block scale as hi + lo pairs); h is read
+// straight from its batch-major layout as the A operand.  Wave w runs K steps
+// 4w .. 4w + 3 of a chunk.  The next chunk's global loads are in flight while
+// a chunk is processed; wave partials are summed in a fixed order.
+constexpr int BD_PAD = BD_CH + 8;        // padded position stride (halves) of a transposed column
+constexpr int BD_SPLIT = 8;              // splits of the union list (partial y vectors)
+constexpr int BD_MAXF = 65536;           // largest ffn of the batched path: a split's list fits in LDS
+constexpr int BD_ROWS = BD_MAXF / BD_SPLIT;
 
 template <int WT>
 __global__ void __launch_bounds__(256)
 k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int f, int d,
         const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount, const _Float16* __restrict__ hh_in,
-        const _Float16* __restrict__ hl_in, const float* __restrict__ b_down, int batch, float* __restrict__ y) {
-  constexpr int NW = (WT == DT_F32) ? 2 : 1;      // weight tiles: hi (and lo for fp32)
-  __shared__ _Float16 wt[NW][BM][KBD_PAD];        // [column][neuron]
-  __shared__ _Float16 ht[BM][KBD_PAD];            // [batch][neuron] hi
-  __shared__ _Float16 lt[BM][KBD_PAD];            // [batch][neuron] lo
+        const _Float16* __restrict__ hl_in, const float* __restrict__ b_down, int batch,
+        float* __restrict__ y_part) {
+  constexpr int NW = (WT == DT_F16) ? 1 : 2;      // weight tiles: hi (and lo for fp32 and Q4_0)
+  __shared__ _Float16 wt[NW][BM][BD_PAD];         // [column][position]
   __shared__ float red[4][BM * BM];
+  __shared__ int rows_l[BD_ROWS];                 // this split's share of the union list
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  const int c0 = blockIdx.x * BM;
+  const int ntile = (d + BM - 1) / BM;
+  const int c0 = (blockIdx.x % ntile) * BM, split = blockIdx.x / ntile;
   const int n = min(max(*ucount, 0), f);
-  const int nch = (n + KBD_CH - 1) / KBD_CH;
-  const int rr = tid / 4, cq = tid % 4;           // staging: row rr of the chunk, 8 columns / batch rows 8cq..
+  const int nch_all = (n + BD_CH - 1) / BD_CH, cps = (nch_all + BD_SPLIT - 1) / BD_SPLIT;
+  const int ch0 = split * cps;                     // this split's chunks [ch0, ch0 + nch)
+  const int nch = max(0, min(nch_all, ch0 + cps) - ch0);
+  const int rg = tid / 4, cq = tid % 4;            // staging: positions 4 rg .. 4 rg + 3, columns 8 cq ..
+  const int row_a = lane % 32, kh = 8 * (lane / 32);
+  const int hs = h_stride(f);
   f16v acc = {};
+  // the split's list entries, so that no weight load waits for a list load
+  {
+    const int p0 = ch0 * BD_CH, np_ = min(n, (ch0 + nch) * BD_CH) - p0;
+    for (int q = tid; q < np_; q += blockDim.x) rows_l[q] = ulist[p0 + q];
+    __syncthreads();
+  }
 
   struct Stage {
-    uint4 wv, wv2;
-    h8v hv, lv;
-    float scale;
-    bool ok;
+    uint4 wv[4], wv2[4];     // four rows' 16-byte pieces (fp32: two each)
+    float scale[4];
+    h8v ah[4], al[4];        // this wave's four K steps of h (hi, lo)
   };
   auto fetch = [&](int c, Stage& st) __attribute__((always_inline)) {
-    const int e = c * KBD_CH + rr;
-    st.ok = e < n;
-    const int row = ulist[min(e, n - 1)];
-    st.scale = 1.f;
-    if constexpr (WT == DT_F16) {
-      st.wv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(downT) + (size_t)row * d + c0 + 8 * cq);
-    } else if constexpr (WT == DT_F32) {
-      const float* fp = static_cast<const float*>(downT) + (size_t)row * d + c0 + 8 * cq;
-      st.wv = *reinterpret_cast<const uint4*>(fp);
-      st.wv2 = *reinterpret_cast<const uint4*>(fp + 4);
-    } else {
-      st.wv = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(downT) + (size_t)row * (d / 2) + c0 / 2);
-      st.scale = (float)__builtin_bit_cast(_Float16, down_sc[(size_t)row * (d / 32) + c0 / 32]);
+    const int base = (ch0 + c) * BD_CH;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = min(base + 4 * rg + q, n - 1);
+      const int row = rows_l[e - ch0 * BD_CH];
+      st.scale[q] = 1.f;
+      if constexpr (WT == DT_F16) {
+        st.wv[q] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(downT) + (size_t)row * d + c0 + 8 * cq);
+      } else if constexpr (WT == DT_F32) {
+        const float* fp = static_cast<const float*>(downT) + (size_t)row * d + c0 + 8 * cq;
+        st.wv[q] = *reinterpret_cast<const uint4*>(fp);
+        st.wv2[q] = *reinterpret_cast<const uint4*>(fp + 4);
+      } else {
+        st.wv[q] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(downT) + (size_t)row * (d / 2) + c0 / 2);
+        st.scale[q] = (float)__builtin_bit_cast(_Float16, down_sc[(size_t)row * (d / 32) + c0 / 32]);
+      }
     }
-    st.hv = *reinterpret_cast<const h8v*>(hh_in + (size_t)row * BM + 8 * cq);
-    st.lv = *reinterpret_cast<const h8v*>(hl_in + (size_t)row * BM + 8 * cq);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int jj = base + 16 * (4 * w + s4) + kh;
+      st.ah[s4] = *reinterpret_cast<const h8v*>(hh_in + (size_t)row_a * hs + jj);
+      st.al[s4] = *reinterpret_cast<const h8v*>(hl_in + (size_t)row_a * hs + jj);
+    }
   };
-  auto stage_lds = [&](const Stage& st) __attribute__((always_inline)) {
-    h8v wh, wl;
-    if constexpr (WT == DT_F16) {
-      wh = as_h8(st.wv);
-    } else if constexpr (WT == DT_F32) {
-      const float v[8] = {__uint_as_float(st.wv.x), __uint_as_float(st.wv.y), __uint_as_float(st.wv.z),
-                          __uint_as_float(st.wv.w), __uint_as_float(st.wv2.x), __uint_as_float(st.wv2.y),
-                          __uint_as_float(st.wv2.z), __uint_as_float(st.wv2.w)};
+  // h at positions past the list end is whatever an earlier call left there:
+  // zero it (the weights there are zero, but 0 * NaN is not)
+  auto clip_h = [&](Stage& st, int c) __attribute__((always_inline)) {
+    const int base = (ch0 + c) * BD_CH;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int jj = base + 16 * (4 * w + s4) + kh;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        _Float16 a, b;
-        split_f16(v[e], &a, &b);
-        wh[e] = a;
-        wl[e] = b;
+        if (jj + e >= n) {
+          st.ah[s4][e] = (_Float16)0.f;
+          st.al[s4][e] = (_Float16)0.f;
+        }
       }
-    } else {
-      // columns 8cq..8cq+7 of the 32-weight block: low nibbles of bytes 0..15 are
-      // weights 0..15, high nibbles weights 16..31
-      wh = q4_h8(st.wv, 8 * (cq & 1), cq >= 2);
+    }
+  };
+  auto stage_lds = [&](const Stage& st, int c) __attribute__((always_inline)) {
+    const int base = (ch0 + c) * BD_CH;
+    float v[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = base + 4 * rg + q < n;
+      if constexpr (WT == DT_F16) {
+        const h8v hv = as_h8(st.wv[q]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[q][e] = ok ? (float)hv[e] : 0.f;
+      } else if constexpr (WT == DT_F32) {
+        const float a[8] = {__uint_as_float(st.wv[q].x), __uint_as_float(st.wv[q].y), __uint_as_float(st.wv[q].z),
+                            __uint_as_float(st.wv[q].w), __uint_as_float(st.wv2[q].x), __uint_as_float(st.wv2[q].y),
+                            __uint_as_float(st.wv2[q].z), __uint_as_float(st.wv2[q].w)};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[q][e] = ok ? a[e] : 0.f;
+      } else {
+        // columns 8cq..8cq+7 of the 32-weight block: low nibbles of bytes 0..15 are
+        // weights 0..15, high nibbles weights 16..31
+        const h8v qv = q4_h8(st.wv[q], 8 * (cq & 1), cq >= 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[q][e] = ok ? st.scale[q] * (float)qv[e] : 0.f;
+      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      wt[0][8 * cq + e][rr] = st.ok ? wh[e] : (_Float16)0.f;
-      if constexpr (NW == 2) wt[NW - 1][8 * cq + e][rr] = st.ok ? wl[e] : (_Float16)0.f;
-      float h = st.ok ? ((float)st.hv[e] + (float)st.lv[e]) * st.scale : 0.f;
-      _Float16 a, b;
-      split_f16(h, &a, &b);
-      ht[8 * cq + e][rr] = a;
-      lt[8 * cq + e][rr] = b;
+      _Float16 hi[4], lo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) split_f16(v[q][e], &hi[q], &lo[q]);
+      typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+      *reinterpret_cast<h4v*>(&wt[0][8 * cq + e][4 * rg]) = h4v{hi[0], hi[1], hi[2], hi[3]};
+      if constexpr (NW == 2) *reinterpret_cast<h4v*>(&wt[1][8 * cq + e][4 * rg]) = h4v{lo[0], lo[1], lo[2], lo[3]};
     }
   };
 
-  Stage ring[KBD_P];
+  // chunk c: stage its weights, start the next chunk's loads, multiply
+  auto step = [&](Stage& cur, Stage& nxt, int c) __attribute__((always_inline)) {
+    stage_lds(cur, c);
+    clip_h(cur, c);
+    if (c + 1 < nch) fetch(c + 1, nxt);
+    __syncthreads();
+    const int base = (ch0 + c) * BD_CH;
 #pragma unroll
-  for (int p = 0; p < KBD_P; ++p)
-    if (p < nch) fetch(p, ring[p]);
-  for (int c0ch = 0; c0ch < nch; c0ch += KBD_P) {
-#pragma unroll
-    for (int p = 0; p < KBD_P; ++p) {
-      const int c = c0ch + p;
-      if (c >= nch) break;                         // block-uniform
-      stage_lds(ring[p]);
-      if (c + KBD_P < nch) fetch(c + KBD_P, ring[p]);
-      __syncthreads();
-      const int kb = 16 * w + 8 * (lane / 32);
-      const h8v ah = *reinterpret_cast<const h8v*>(&ht[lane % 32][kb]);
-      const h8v al = *reinterpret_cast<const h8v*>(&lt[lane % 32][kb]);
-      const h8v bw = *reinterpret_cast<const h8v*>(&wt[0][lane % 32][kb]);
-      acc = mfma(ah, bw, acc);
-      acc = mfma(al, bw, acc);
-      if constexpr (NW == 2) {
-        const h8v bl = *reinterpret_cast<const h8v*>(&wt[NW - 1][lane % 32][kb]);
-        acc = mfma(ah, bl, acc);
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int kb = 16 * (4 * w + s4) + kh;
+      if (base + 16 * (4 * w + s4) < n) {         // wave-uniform: a step wholly past the end is skipped
+        const h8v bw = *reinterpret_cast<const h8v*>(&wt[0][row_a][kb]);
+        acc = mfma(cur.ah[s4], bw, acc);
+        acc = mfma(cur.al[s4], bw, acc);
+        if constexpr (NW == 2) {
+          const h8v bl = *reinterpret_cast<const h8v*>(&wt[1][row_a][kb]);
+          acc = mfma(cur.ah[s4], bl, acc);
+        }
       }
-      __syncthreads();
     }
+    __syncthreads();
+  };
+  Stage s0, s1;
+  if (nch > 0) fetch(0, s0);
+  for (int c = 0; c < nch; c += 2) {
+    step(s0, s1, c);
+    if (c + 1 < nch) step(s1, s0, c + 1);
   }
   const int col = lane % 32, half = lane / 32;
 #pragma unroll
@@ -476,9 +602,18 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
     const int b = e / BM, c = e % BM, cg = c0 + c;
     if (b >= batch || cg >= d) continue;
     float v = red[0][e] + red[1][e] + red[2][e] + red[3][e];
-    if (b_down) v += b_down[cg];
-    y[(size_t)b * d + cg] = v;
+    if (b_down && split == 0) v += b_down[cg];
+    y_part[((size_t)split * BM + b) * d + cg] = v;
   }
+}
+
+// y[b] = the BD_SPLIT partial vectors of k_bdown added in order (b < batch)
+__global__ void k_bsum_y(const float* __restrict__ y_part, int batch, int d, float* __restrict__ y) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= batch * d) return;
+  float v = y_part[e];
+  for (int p = 1; p < BD_SPLIT; ++p) v += y_part[(size_t)p * BM * d + e];
+  y[e] = v;
 }
 
 // Explicit-list input of the batched FFN: u[i] = 1 for listed i (others 0,
@@ -499,15 +634,18 @@ __global__ void k_blist(const int32_t* __restrict__ idx, const int32_t* __restri
   for (int b = 0; b < BM; ++b) m_nm[(size_t)i * BM + b] = (b < batch && mask[(size_t)b * f + i]) ? 1 : 0;
 }
 
-// out[b] = glue(x[b], y[b]) for b < batch (one block per sequence)
+// out[b] = glue(x[b], sum of the np partials y[p][b]) for b < batch (one
+// block per sequence); partial p of row b is at y_part + (p * 32 + b) * d
 __global__ void __launch_bounds__(256)
-k_bglue_out(const float* __restrict__ x, const float* __restrict__ y, int d, float* __restrict__ out) {
+k_bglue_out(const float* __restrict__ x, const float* __restrict__ y_part, int np, int d, float* __restrict__ out) {
   extern __shared__ float vs[];
   __shared__ float red[4];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   float ss = 0.f;
   for (int k = tid; k < d; k += blockDim.x) {
-    const float v = x[(size_t)b * d + k] + y[(size_t)b * d + k];
+    float yv = y_part[(size_t)b * d + k];
+    for (int p = 1; p < np; ++p) yv += y_part[((size_t)p * BM + b) * d + k];
+    const float v = x[(size_t)b * d + k] + yv;
     vs[k] = v;
     ss = fmaf(v, v, ss);
   }

@@ -29,7 +29,9 @@
  *    16-byte aligned, Q4_0 scales 4-byte aligned; 1 <= batch <= 32;
  *    act REGLU needs `gate`; predictor dtype F32 or F16 (Q4_0 predictor:
  *    PI_EUNSUPPORTED); d <= 16384 and rank <= 4096 (vectors are staged whole
- *    in LDS; larger: PI_EUNSUPPORTED); every layer of a stack has the same d.
+ *    in LDS; larger: PI_EUNSUPPORTED); the FFN at batch > 1 needs
+ *    ffn <= 65536 (PI_EUNSUPPORTED otherwise); every layer of a stack has the
+ *    same d.
  *  - Calls on distinct workspaces are independent; calls sharing a workspace
  *    must be ordered on one stream.
  *  - Batch 1 runs GEMV kernels over the active rows.  Batch 2..32 runs each
