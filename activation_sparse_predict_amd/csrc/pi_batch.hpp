@@ -37,6 +37,14 @@ __device__ __forceinline__ f16v mfma(h8v a, h8v b, f16v c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// A operands ([32][K] fp16: x, t and h, K a multiple of 16) are stored in
+// operand order: the 32 x 16 block of K step s is 512 contiguous halves, lane
+// l's 8 values (row l % 32, k = 16 s + 8 (l / 32) + e) at 8 l.  A wave then
+// reads one K step as 1 KB of contiguous memory instead of 32 rows x 32 B.
+__host__ __device__ constexpr size_t aop(int row, int k) {
+  return (size_t)(k >> 4) * 512 + (size_t)((k >> 3) & 1) * 256 + (size_t)row * 8 + (k & 7);
+}
+
 // fp32 value -> (hi, lo) fp16 pair with hi + lo ~ v to about 22 bits
 __device__ __forceinline__ void split_f16(float v, _Float16* hi, _Float16* lo) {
   const _Float16 h = (_Float16)v;
@@ -65,7 +73,7 @@ __device__ __forceinline__ h8v q4_h8(uint4 c, int b0, bool hi_nib) {
 // ------------------------------------------------------------------- glue
 // One block per padded sequence row b < 32.  Rows b < B: x' = glue(x_prev[b],
 // sum of np partials y[p][b]) (np = 0: x' = x_prev[b]); x' goes to x_out[b]
-// (and x_trace[b]) in fp32 and to xh/xl[b] as fp16 hi/lo.  Rows b >= B are
+// (and x_trace[b]) in fp32 and to xh/xl row b (operand order) as fp16 hi/lo.  Rows b >= B are
 // written as zeros in xh/xl so that they contribute nothing to any product.
 constexpr int BG_T = 1024;               // threads of a glue block
 constexpr int BG_V = 4;                  // float4 per thread held at once (d <= 16384)
@@ -79,8 +87,8 @@ k_bglue(const float* __restrict__ x_prev, const float* __restrict__ y_part, int 
   const int nv = d / 4;
   if (b >= B) {
     for (int k = tid; k < d; k += blockDim.x) {
-      xh[(size_t)b * d + k] = (_Float16)0.f;
-      xl[(size_t)b * d + k] = (_Float16)0.f;
+      xh[aop(b, k)] = (_Float16)0.f;
+      xl[aop(b, k)] = (_Float16)0.f;
     }
     return;
   }
@@ -149,8 +157,8 @@ k_bglue(const float* __restrict__ x_prev, const float* __restrict__ y_part, int 
     for (int e = 0; e < 4; ++e) split_f16(o[e], &hh[e], &ll[e]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      xh[(size_t)b * d + 4 * k4 + e] = hh[e];
-      xl[(size_t)b * d + 4 * k4 + e] = ll[e];
+      xh[aop(b, 4 * k4 + e)] = hh[e];
+      xl[aop(b, 4 * k4 + e)] = ll[e];
     }
   }
 }
@@ -177,20 +185,21 @@ __device__ __forceinline__ void split8(const float* __restrict__ p, h8v* hi, h8v
 }
 
 // acc += X[rows of this lane][K window] * W[row][K window] over KU steps of 16,
-// starting at k; X given as hi/lo fp16 [32][ldx], W rows contiguous along K.
+// starting at k; X given as hi/lo fp16 [32][K] in operand order, W rows
+// contiguous along K.
 // All loads of the window are issued before the first MFMA, with no branch
 // among them: steps at or past kend load a clamped address and multiply a
 // zero X operand instead.
 template <int WT>
 __device__ __forceinline__ void mfma_window(f16v& acc, const _Float16* __restrict__ xh,
-                                            const _Float16* __restrict__ xl, size_t ldx, const void* __restrict__ W,
+                                            const _Float16* __restrict__ xl, const void* __restrict__ W,
                                             size_t row, size_t ldw, int k, int kend, int kstride, int lane) {
   const int half = lane / 32;
   h8v ah[KU], al[KU], bw[KU], bl[KU];
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
-    const int kk = min(k + u * kstride, kend - 16) + 8 * half;
-    const size_t xo = (size_t)(lane % 32) * ldx + kk;
+    const int ks = min(k + u * kstride, kend - 16), kk = ks + 8 * half;
+    const size_t xo = (size_t)(ks >> 4) * 512 + 8 * lane;
     ah[u] = *reinterpret_cast<const h8v*>(xh + xo);
     al[u] = *reinterpret_cast<const h8v*>(xl + xo);
     if constexpr (WT == DT_F16) {
@@ -225,7 +234,7 @@ k_bpred1(const void* __restrict__ A, int r, int d, int ksplit, const _Float16* _
   const int k0 = ks * kper, k1 = min(d, k0 + kper);
   f16v acc = {};
   for (int k = k0 + 16 * w; k < k1; k += 4 * 16 * KU)
-    mfma_window<PT>(acc, xh, xl, d, A, (size_t)j, d, k, k1, 4 * 16, lane);
+    mfma_window<PT>(acc, xh, xl, A, (size_t)j, d, k, k1, 4 * 16, lane);
 #pragma unroll
   for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -238,7 +247,7 @@ k_bpred1(const void* __restrict__ A, int r, int d, int ksplit, const _Float16* _
   }
 }
 
-// t = sum of the K-split partials (in order), as fp16 hi/lo [32][r]
+// t = sum of the K-split partials (in order), as fp16 hi/lo [32][r] in operand order
 __global__ void __launch_bounds__(256)
 k_bsplit_t(const float* __restrict__ t_part, int ksplit, int r, _Float16* __restrict__ th,
            _Float16* __restrict__ tl) {
@@ -248,8 +257,8 @@ k_bsplit_t(const float* __restrict__ t_part, int ksplit, int r, _Float16* __rest
   for (int ks = 1; ks < ksplit; ++ks) v += t_part[(size_t)ks * BM * r + e];
   _Float16 hh, ll;
   split_f16(v, &hh, &ll);
-  th[e] = hh;
-  tl[e] = ll;
+  th[aop(e / r, e % r)] = hh;
+  tl[aop(e / r, e % r)] = ll;
 }
 
 // ------------------------------------------------------------ predictor 2
@@ -275,7 +284,7 @@ k_bscore(const void* __restrict__ Bm, const float* __restrict__ pbias, int f, in
   const int i = min(i0 + col, f - 1);
   f16v acc = {};
   const int ns = r / 16, kbeg = 16 * (w * ns / BS_W), kend = 16 * ((w + 1) * ns / BS_W);
-  for (int k = kbeg; k < kend; k += 16 * KU) mfma_window<PT>(acc, th, tl, r, Bm, (size_t)i, r, k, kend, 16, lane);
+  for (int k = kbeg; k < kend; k += 16 * KU) mfma_window<PT>(acc, th, tl, Bm, (size_t)i, r, k, kend, 16, lane);
 #pragma unroll
   for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -326,13 +335,14 @@ k_bscore(const void* __restrict__ Bm, const float* __restrict__ pbias, int f, in
 // 32 q + 32) (blocks past the union's end return); its BUP_W waves split K
 // into contiguous ranges and their partial tiles are summed through LDS in
 // wave order.  Epilogue: h[b] = m[i][b] ? act(z + bias) : 0, written as fp16
-// hi/lo to hh/hl[b][j] (batch-major, j = the neuron's position in the union
-// list), the layout in which the down projection reads it as an MFMA operand.
+// hi/lo to hh/hl as a [32][h_stride] operand-order matrix (row b, column j =
+// the neuron's position in the union list), in which the down projection
+// reads it as its A operand.
 constexpr int BUP_W = 8;
 constexpr int BD_CH = 256;               // union positions per chunk of the down projection
 
-// row stride (halves) of the batch-major h: whole chunks, so that a chunk's
-// reads stay inside the row
+// K extent (halves) of the h operand: whole chunks, so that a chunk's
+// reads stay inside the buffer
 __host__ __device__ constexpr int h_stride(int f) { return (f + BD_CH - 1) / BD_CH * BD_CH; }
 
 template <int WT, int ACT>
@@ -374,7 +384,7 @@ k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, con
         }
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const size_t xo = (size_t)(lane % 32) * d + kb + 16 * st + 8 * half;
+          const size_t xo = (size_t)((kb + 16 * st) >> 4) * 512 + 8 * lane;
           ah[qb][st] = *reinterpret_cast<const h8v*>(xh + xo);
           al[qb][st] = *reinterpret_cast<const h8v*>(xl + xo);
         }
@@ -403,8 +413,7 @@ k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, con
     for (int k = kbeg; k < kend; k += 16 * KU) {
 #pragma unroll
       for (int mt = 0; mt < NMAT; ++mt)
-        mfma_window<WT>(acc[mt], xh, xl, d, (NMAT == 2 && mt == 0) ? gate_w : up_w, (size_t)row, d, k, kend, 16,
-                        lane);
+        mfma_window<WT>(acc[mt], xh, xl, (NMAT == 2 && mt == 0) ? gate_w : up_w, (size_t)row, d, k, kend, 16, lane);
     }
   }
   // the waves' partial tiles: lane holds neuron column col, batch rows 8g + 4*half + v
@@ -433,8 +442,8 @@ k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, con
     if (m_nm[(size_t)rw * BM + b] == 0) h = 0.f;
     _Float16 a, l;
     split_f16(h, &a, &l);
-    hh_out[(size_t)b * h_stride(f) + t0 + c] = a;
-    hl_out[(size_t)b * h_stride(f) + t0 + c] = l;
+    hh_out[aop(b, t0 + c)] = a;
+    hl_out[aop(b, t0 + c)] = l;
   }
 }
 
@@ -447,7 +456,7 @@ k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, con
 // staged through LDS transposed to [column][position] -- each thread writes
 // four consecutive positions of a column at once -- as fp16 (fp32 weights
 // and Q4_0 weights times their block scale as hi + lo pairs); h is read
-// straight from its batch-major layout as the A operand.  Wave w runs K steps
+// straight from its operand-order layout as the A operand.  Wave w runs K steps
 // 4w .. 4w + 3 of a chunk.  The next chunk's global loads are in flight while
 // a chunk is processed; wave partials are summed in a fixed order.
 constexpr int BD_PAD = BD_CH + 8;        // padded position stride (halves) of a transposed column
@@ -474,7 +483,6 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
   const int nch = max(0, min(nch_all, ch0 + cps) - ch0);
   const int rg = tid / 4, cq = tid % 4;            // staging: positions 4 rg .. 4 rg + 3, columns 8 cq ..
   const int row_a = lane % 32, kh = 8 * (lane / 32);
-  const int hs = h_stride(f);
   f16v acc = {};
   // the split's list entries, so that no weight load waits for a list load
   {
@@ -508,9 +516,9 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
     }
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const int jj = base + 16 * (4 * w + s4) + kh;
-      st.ah[s4] = *reinterpret_cast<const h8v*>(hh_in + (size_t)row_a * hs + jj);
-      st.al[s4] = *reinterpret_cast<const h8v*>(hl_in + (size_t)row_a * hs + jj);
+      const int ks = base + 16 * (4 * w + s4);
+      st.ah[s4] = *reinterpret_cast<const h8v*>(hh_in + (size_t)(ks >> 4) * 512 + 8 * lane);
+      st.al[s4] = *reinterpret_cast<const h8v*>(hl_in + (size_t)(ks >> 4) * 512 + 8 * lane);
     }
   };
   // h at positions past the list end is whatever an earlier call left there:
