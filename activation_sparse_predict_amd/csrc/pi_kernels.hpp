@@ -173,6 +173,34 @@ __device__ __forceinline__ float chunk_dot(uint4 c, float scale, const float* __
   }
 }
 
+// Q4_0 activations in LDS for the gathered dot products, pair-transposed:
+// element 32 b + j (block b, 0 <= j < 32) is half j / 16 of the float2 at
+// xq[(j % 16) * nb + b], nb = d / 32.  A lane that owns block b reads its 16
+// pairs at stride nb, so the 64 lanes of a wave read 64 consecutive 8-byte
+// words per access: no LDS bank conflicts (the linear layout puts the lanes
+// 128 bytes apart, all on the same banks).
+__host__ __device__ constexpr int q4t_pos(int k, int d) { return ((k & 15) * (d >> 5) + (k >> 5)) * 2 + ((k >> 4) & 1); }
+
+// sum_j w_j * x_j over Q4_0 block `blk`, x in the pair-transposed layout; the
+// same operation order as chunk_dot<DT_Q4>.
+__device__ __forceinline__ float chunk_dot_q4t(uint4 c, float scale, const float2* __restrict__ xq, int blk, int nb) {
+  const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
+  float a = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    // the nibbles of four bytes as bytes: each (x >> 8 b) & 0xFF becomes one
+    // byte-to-float conversion
+    const uint32_t lo = wd[k] & 0x0F0F0F0Fu, hi = (wd[k] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float2 xv = xq[(4 * k + b) * nb + blk];
+      a = fmaf((float)((lo >> (8 * b)) & 0xFFu) - 8.f, xv.x, a);
+      a = fmaf((float)((hi >> (8 * b)) & 0xFFu) - 8.f, xv.y, a);
+    }
+  }
+  return a * scale;
+}
+
 // acc[j] += h * w_j over one chunk (acc has EPL entries).
 template <int DT>
 __device__ __forceinline__ void chunk_axpy(uint4 c, float scale, float h, float* __restrict__ acc) {
@@ -190,12 +218,14 @@ __device__ __forceinline__ void chunk_axpy(uint4 c, float scale, float h, float*
     const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
+      // the nibbles of four bytes as bytes: each (x >> 8 b) & 0xFF becomes one
+      // byte-to-float conversion
+      const uint32_t lo = wd[k] & 0x0F0F0F0Fu, hi = (wd[k] >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const uint32_t byte = (wd[k] >> (8 * b)) & 0xFFu;
         const int j = 4 * k + b;
-        acc[j] = fmaf(hs, (float)((int)(byte & 15u) - 8), acc[j]);
-        acc[j + 16] = fmaf(hs, (float)((int)(byte >> 4) - 8), acc[j + 16]);
+        acc[j] = fmaf(hs, (float)((lo >> (8 * b)) & 0xFFu) - 8.f, acc[j]);
+        acc[j + 16] = fmaf(hs, (float)((hi >> (8 * b)) & 0xFFu) - 8.f, acc[j + 16]);
       }
     }
   }
@@ -310,7 +340,7 @@ __device__ __forceinline__ float stage_residual(float* __restrict__ lds, const f
 }
 
 // Dot products of rows rows[0..NN) of NMAT matrices (NMAT = 2: gate, up) with
-// the LDS vector xs[d]: all NN * NMAT * NCH chunk loads of a round are issued
+// the LDS vector xs[d] (pair-transposed for Q4_0, see q4t_pos): all NN * NMAT * NCH chunk loads of a round are issued
 // before the first multiply, one HBM round trip per round.  z[n][m] is row
 // rows[n] of matrix m dotted with xs, in every lane.  Chunks past the row
 // (ragged tail, or beyond the row's chunk count) load a clamped, valid address
@@ -345,7 +375,11 @@ __device__ __forceinline__ void gather_rows(const void* __restrict__ w0, const u
       const bool ok = (q0 + q < nch) && (e < d);
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        const float p = chunk_dot<WT>(c[v][q], fs[v][q], xs + (ok ? e : 0));
+        float p;
+        if constexpr (WT == DT_Q4)
+          p = chunk_dot_q4t(c[v][q], fs[v][q], reinterpret_cast<const float2*>(xs), ok ? e / 32 : 0, d / 32);
+        else
+          p = chunk_dot<WT>(c[v][q], fs[v][q], xs + (ok ? e : 0));
         a[v] += ok ? p : 0.f;
       }
     }
@@ -364,14 +398,14 @@ __device__ __forceinline__ void gather_rows(const void* __restrict__ w0, const u
 // flight.  The dot product takes v and the row's result is scaled by
 // 1 / sqrt(mean(v^2) + 1e-6).  Every block computes the same v and scale with
 // the same operation order, so all agree bit for bit; each block writes its
-// slice of x'.
+// slice of x' (and, if xq_out is given, of its pair-transposed Q4_0 copy).
 constexpr int K1_WAVES = 4;
 
 template <int PT, int NCH>
 __global__ void __launch_bounds__(256)
 k_predict_t(const void* __restrict__ A, int r, int d, const float* __restrict__ x_prev,
-            const float* __restrict__ y_prev, int y_np, float* __restrict__ x_out, float* __restrict__ x_trace,
-            float* __restrict__ t) {
+            const float* __restrict__ y_prev, int y_np, float* __restrict__ x_out, float* __restrict__ xq_out,
+            float* __restrict__ x_trace, float* __restrict__ t) {
   extern __shared__ float smem[];
   __shared__ float red[K1_WAVES];
   constexpr int EPL = Tr<PT>::EPL, TW = WAVE * EPL;
@@ -437,6 +471,7 @@ k_predict_t(const void* __restrict__ A, int r, int d, const float* __restrict__ 
     for (int k = b * cx + tid; k < min(d, (b + 1) * cx); k += blockDim.x) {
       const float xk = y_np > 0 ? xs[k] * inv : xs[k];
       if (x_out) x_out[k] = xk;
+      if (xq_out) xq_out[q4t_pos(k, d)] = xk;
       if (x_trace) x_trace[k] = xk;
     }
   }
@@ -644,7 +679,11 @@ k_up_list(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc,
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE, W = blockDim.x / WAVE;
   const int cnt = min(max(*count, 0), f);
   if ((int)blockIdx.x * W >= cnt) return;
-  stage_f32<8>(xs, x, d, tid, blockDim.x);
+  if constexpr (WT == DT_Q4) {
+    for (int k = tid; k < d; k += blockDim.x) xs[q4t_pos(k, d)] = x[k];
+  } else {
+    stage_f32<8>(xs, x, d, tid, blockDim.x);
+  }
   __syncthreads();
   constexpr int NMAT = (ACT == ACT_RELU) ? 1 : 2;
   const void* w0 = (ACT == ACT_RELU) ? up_w : gate_w;
