@@ -9,7 +9,7 @@ Entry points (same names and meaning as the C functions):
   workspace_bytes(layers, batch)
   predict(layer, x, idx, count, scores=None, mask=None, ws=None)
   sparse_ffn(layer, x, idx, count, y, mask=None, ws=None)
-  ffn_stack(layers, x, out, counts=None, trace=None, ws=None)
+  ffn_stack(layers, x, out, counts=None, trace=None, ws=None, nz_counts=None)
 """
 from __future__ import annotations
 
@@ -77,7 +77,7 @@ def lib():
         L.pi_predict.restype = ctypes.c_int
         L.pi_sparse_ffn.argtypes = [P, P, I32, P, P, P, P, P, SZ, P]
         L.pi_sparse_ffn.restype = ctypes.c_int
-        L.pi_ffn_stack.argtypes = [P, I32, P, I32, P, P, P, P, SZ, P]
+        L.pi_ffn_stack.argtypes = [P, I32, P, I32, P, P, P, P, P, SZ, P]
         L.pi_ffn_stack.restype = ctypes.c_int
         L.pi_last_hip_error.restype = ctypes.c_char_p
         _lib = L
@@ -237,16 +237,16 @@ class Stack:
         self.arr = _layer_array(self.layers)
         self.ws = alloc_workspace(self.layers, batch) if ws is None else ws
 
-    def __call__(self, x, out, counts=None, trace=None, stream=None):
+    def __call__(self, x, out, counts=None, trace=None, stream=None, nz_counts=None):
         tr = None if trace is None else ctypes.cast(trace, ctypes.c_void_p)
         st = lib().pi_ffn_stack(ctypes.cast(self.arr, ctypes.c_void_p), len(self.layers), _p(x),
-                                self.batch, _p(out), _p(counts), tr, _p(self.ws), self.ws.numel(),
-                                _stream(stream))
+                                self.batch, _p(out), _p(counts), _p(nz_counts), tr, _p(self.ws),
+                                self.ws.numel(), _stream(stream))
         _check(st, "pi_ffn_stack")
 
 
-def ffn_stack(layers, x, out, counts=None, trace=None, ws=None, batch: int = 1, stream=None):
-    Stack(layers, batch, ws)(x, out, counts, trace, stream)
+def ffn_stack(layers, x, out, counts=None, trace=None, ws=None, batch: int = 1, stream=None, nz_counts=None):
+    Stack(layers, batch, ws)(x, out, counts, trace, stream, nz_counts)
 
 
 # ------------------------------------------------------- HIP runtime plumbing

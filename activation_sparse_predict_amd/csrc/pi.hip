@@ -81,7 +81,7 @@ int k2_blocks_max(int ffn);
 int bscore_blocks(int ffn) { return cdiv(ffn, pib::BM); }
 
 struct WsLayout {
-  size_t t, xbuf, ybuf, xq, mask, h, cnt, misc;
+  size_t t, xbuf, ybuf, xq, mask, pmask, h, cnt, misc;
   // batched path (batch > 1)
   size_t xh, xl, tpart, th, tl, mnm, ulist, hh, hl;
   size_t total;
@@ -102,8 +102,10 @@ WsLayout layout(const Dims& D, int batch) {
   w.ybuf = o; o += w.ys * 2;
   w.xq = o;   o += align_up(sizeof(float) * (size_t)D.d);   // x' pair-transposed for Q4_0 gathers (batch 1)
   w.mask = o; o += align_up(fpad);                       // one byte per neuron (the union when batch > 1)
+  w.pmask = o; o += align_up(fpad);                      // the predictor's mask for a trace list (batch 1)
   w.h = o;    o += align_up(sizeof(float) * (size_t)D.fmax);
-  w.cnt = o;  o += align_up(sizeof(int32_t) * (size_t)std::max(k2_blocks_max(D.fmax), bscore_blocks(D.fmax)));
+  // per-block counts: active neurons, then those with h != 0 (batch 1)
+  w.cnt = o;  o += align_up(sizeof(int32_t) * (size_t)std::max(2 * k2_blocks_max(D.fmax), bscore_blocks(D.fmax)));
   w.misc = o; o += kAlign;
   if (batch > 1) {
     w.xh = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * D.d);
@@ -126,6 +128,7 @@ struct Ws {
   float* y[2];
   float* xq;
   uint8_t* mask;
+  uint8_t* pmask;
   float* h;
   int32_t* cnt;
   int32_t* misc;
@@ -145,6 +148,7 @@ Ws carve(void* base, const WsLayout& L) {
   w.y[1] = reinterpret_cast<float*>(b + L.ybuf + L.ys);
   w.xq = reinterpret_cast<float*>(b + L.xq);
   w.mask = reinterpret_cast<uint8_t*>(b + L.mask);
+  w.pmask = reinterpret_cast<uint8_t*>(b + L.pmask);
   w.h = reinterpret_cast<float*>(b + L.h);
   w.cnt = reinterpret_cast<int32_t*>(b + L.cnt);
   w.misc = reinterpret_cast<int32_t*>(b + L.misc);
@@ -347,6 +351,7 @@ struct K3Args {
   int n_cnt_blk;
   int32_t* count_out;
   int32_t* count_out2;
+  int32_t* nz_out;           // active neurons with h != 0, or NULL
 };
 
 template <int WT, int TWC, bool EXPL>
@@ -355,7 +360,7 @@ void launch_k3_t(const pi_layer* L, const K3Shape& sh, const K3Args& a, hipStrea
   const int xcd = (nblk % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((k_down<WT, TWC, EXPL>), dim3(nblk), dim3(K3_WAVES * WAVE), 0, st, L->downT.w,
                      L->downT.scale, L->ffn, L->d, sh.ct, sh.nc, xcd, a.mask, a.h_full, a.idx, a.count, a.h_list,
-                     L->b_down, a.y_part, a.cnt_blk, a.n_cnt_blk, a.count_out, a.count_out2);
+                     L->b_down, a.y_part, a.cnt_blk, a.n_cnt_blk, a.count_out, a.count_out2, a.nz_out);
 }
 
 template <int WT, bool EXPL>
@@ -460,7 +465,7 @@ void mark(const pi_trace* tr, int i, hipStream_t st) {
 }
 
 void b_predict(const pi_layer* L, int batch, const Ws& W, float* scores, uint8_t* mask_out, int32_t* ulist,
-               int32_t* ucount, int32_t* ucount2, hipStream_t st, const pi_trace* tr = nullptr) {
+               int32_t* ucount, int32_t* ucount2, int32_t* ucount3, hipStream_t st, const pi_trace* tr = nullptr) {
   const int ks = bksplit(L->rank);
   const dim3 g1(cdiv(L->rank, kBatchM) * ks);
   if (L->p_dtype == PI_F16)
@@ -480,7 +485,7 @@ void b_predict(const pi_layer* L, int batch, const Ws& W, float* scores, uint8_t
     hipLaunchKernelGGL(pib::k_bscore<DT_F32>, g2, dim3(256), 0, st, L->B, pb, L->ffn, L->rank, batch, W.th, W.tl,
                        W.mnm, W.mask, W.cnt, scores, mask_out);
   mark(tr, 4, st);
-  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, ulist, ucount, ucount2);
+  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, ulist, ucount, ucount2, ucount3);
   mark(tr, 5, st);
 }
 
@@ -563,12 +568,12 @@ pi_status pi_predict(const pi_layer* layer, const float* x, int32_t batch, float
   (void)hipGetLastError();
   if (batch > 1) {
     b_glue(x, nullptr, batch, layer->d, nullptr, nullptr, W, st);
-    b_predict(layer, batch, W, scores, mask, idx, count, nullptr, st);
+    b_predict(layer, batch, W, scores, mask, idx, count, nullptr, nullptr, st);
     return launch_status();
   }
   k1(layer, K1Args{x, nullptr, 0, nullptr, nullptr, nullptr, W.t}, st);
   k2(layer, false, K2Args{W.t, nullptr, scores, W.mask, mask, nullptr, nullptr}, st);
-  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, layer->ffn, idx, count, nullptr);
+  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, layer->ffn, idx, count, nullptr, nullptr);
   return launch_status();
 }
 
@@ -593,21 +598,22 @@ pi_status pi_sparse_ffn(const pi_layer* layer, const float* x, int32_t batch, co
     hipLaunchKernelGGL(pib::k_bclear, dim3(cdiv(layer->ffn, 256)), dim3(256), 0, st, W.mask, layer->ffn);
     hipLaunchKernelGGL(pib::k_blist, dim3(cdiv(layer->ffn, 256)), dim3(256), 0, st, idx, count, layer->ffn, mask,
                        batch, W.mask, W.mnm);
-    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, layer->ffn, W.ulist, W.misc, nullptr);
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, layer->ffn, W.ulist, W.misc, nullptr, nullptr);
     b_ffn(layer, batch, W, W.ulist, W.misc, W.y[0], st);
     hipLaunchKernelGGL(pib::k_bsum_y, dim3(cdiv(batch * layer->d, 256)), dim3(256), 0, st, W.y[0], batch, layer->d,
                        y);
     return launch_status();
   }
   up_list(layer, x, idx, count, W.h, st);
-  const int np = k3<true>(layer, K3Args{nullptr, nullptr, idx, count, W.h, W.y[0], nullptr, 0, nullptr, nullptr},
+  const int np = k3<true>(layer, K3Args{nullptr, nullptr, idx, count, W.h, W.y[0], nullptr, 0, nullptr, nullptr, nullptr},
                           st);
   hipLaunchKernelGGL(k_finalize, dim3(cdiv(layer->d, 256)), dim3(256), 0, st, W.y[0], np, y, layer->d);
   return launch_status();
 }
 
 pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x, int32_t batch, float* out,
-                       int32_t* counts, const pi_trace* trace, void* ws, size_t ws_bytes, void* stream) {
+                       int32_t* counts, int32_t* nz_counts, const pi_trace* trace, void* ws, size_t ws_bytes,
+                       void* stream) {
   if (!layers || n_layers <= 0) return PI_EINVAL;
   pi_status s;
   for (int l = 0; l < n_layers; ++l)
@@ -616,6 +622,9 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
   for (int l = 0; l < n_layers; ++l)
     if ((s = check_batched_ffn(&layers[l], batch)) != PI_OK) return s;
   if (!x || !aligned(x, 16) || !out) return PI_EINVAL;
+  if (trace)
+    for (int l = 0; l < n_layers; ++l)
+      if (trace[l].mask && !aligned(trace[l].mask, 16)) return PI_EINVAL;
   Dims D;
   if (!dims_of(layers, n_layers, &D)) return PI_EINVAL;
   const WsLayout WL = layout(D, batch);
@@ -633,10 +642,10 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
              W, st);
       mark(tr, 1, st);
       b_predict(L, batch, W, tr ? tr->scores : nullptr, tr ? tr->mask : nullptr, W.ulist, W.misc,
-                counts ? counts + l : nullptr, st, tr);
+                counts ? counts + l : nullptr, nz_counts ? nz_counts + l : nullptr, st, tr);
       if (tr && (tr->idx || tr->count))   // the union list and count for the record
         hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, tr->idx ? tr->idx : W.ulist,
-                           tr->count ? tr->count : W.misc + 1, nullptr);
+                           tr->count ? tr->count : W.misc + 1, nullptr, nullptr);
       b_ffn(L, batch, W, W.ulist, W.misc, W.y[cur], st, tr);
     }
     const int last = (n_layers - 1) & 1;
@@ -654,16 +663,19 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
     k1(L, K1Args{l == 0 ? x : W.x[prv], l == 0 ? nullptr : W.y[prv], np_prev, W.x[cur], q4 ? W.xq : nullptr,
                  tr ? tr->x_in : nullptr, W.t}, st);
     mark(tr, 1, st);
-    k2(L, true, K2Args{W.t, q4 ? W.xq : W.x[cur], tr ? tr->scores : nullptr, W.mask, tr ? tr->mask : nullptr, W.cnt, W.h},
-       st);
+    // W.mask marks the active neurons with h != 0 (the rows the down projection
+    // reads); the predictor's own mask goes to the record, or to W.pmask when
+    // only the record's list asks for it
+    uint8_t* pmask = tr ? (tr->mask ? tr->mask : (tr->idx ? W.pmask : nullptr)) : nullptr;
+    k2(L, true, K2Args{W.t, q4 ? W.xq : W.x[cur], tr ? tr->scores : nullptr, W.mask, pmask, W.cnt, W.h}, st);
     mark(tr, 2, st);
     int32_t* c1 = counts ? counts + l : nullptr;
     int32_t* c2 = (tr && tr->count && !tr->idx) ? tr->count : nullptr;
-    if (tr && tr->idx)   // ascending list for the record; the down projection reads the mask bytes directly
-      hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, tr->idx,
-                         tr->count ? tr->count : W.misc, nullptr);
-    np_prev = k3<false>(L, K3Args{W.mask, W.h, nullptr, nullptr, nullptr, W.y[cur], W.cnt, k2_blocks(L), c1, c2},
-                        st);
+    if (tr && tr->idx)   // ascending list of the predictor's mask, for the record
+      hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, pmask, L->ffn, tr->idx,
+                         tr->count ? tr->count : W.misc, nullptr, nullptr);
+    np_prev = k3<false>(L, K3Args{W.mask, W.h, nullptr, nullptr, nullptr, W.y[cur], W.cnt, k2_blocks(L), c1, c2,
+                                  nz_counts ? nz_counts + l : nullptr}, st);
     mark(tr, 3, st);
   }
   {

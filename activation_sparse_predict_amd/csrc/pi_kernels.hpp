@@ -516,7 +516,11 @@ k_predict_t(const void* __restrict__ A, int r, int d, const float* __restrict__ 
 // (gate and up rows of both, WCH chunks per lane per row, in one HBM round
 // trip): the number of actives per wave varies a lot, per block much less,
 // and the slowest wave sets the kernel's time.
-// The block's active count goes to cnt_blk[block] (summed over batches).
+// The block's active count goes to cnt_blk[block] (summed over batches) and
+// the count of its active neurons with h != 0 to cnt_blk[nb + block].
+// With FUSE, `mask` marks only the neurons whose h is nonzero: a neuron the
+// predictor marks but whose ReLU output is 0 adds nothing to y, so the down
+// projection does not read its row; `mask2` (if given) is the predictor's mask.
 // Global stores come after the block barrier so that the barrier does not wait
 // for them.
 constexpr int K2_WAVES = 4;
@@ -580,6 +584,7 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
   issue(0, 0, opaque_zero());
 
   int block_count = 0;
+  int nz = 0;                                                // this wave's gathered neurons with h != 0
   for (int m0 = 0, batch = 0; m0 < Mb; m0 += RB, ++batch) {
     float acc[RB];
 #pragma unroll
@@ -632,7 +637,9 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
     if (m0 + RB < Mb) issue(m0 + RB, 0, 0);    // the next batch's rows of B, in flight during the gather
     if (rep) {
       if (scores) scores[i] = s;
-      mask[i] = on ? 1 : 0;
+      // fused: mask marks the neurons whose h is nonzero (the rows the down
+      // projection reads); inactive ones here, active ones when h is known
+      if (!FUSE || !on) mask[i] = on ? 1 : 0;
       if (mask2) mask2[i] = on ? 1 : 0;
     }
     if constexpr (FUSE) {
@@ -648,22 +655,43 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
           const float b0 = bias[rows[0]], b1 = bias[rows[1]];
           float z[2][NMAT];
           gather_rows<WT, WCH, NMAT, 2>(w0, s0, up_w, up_sc, rows, d, xs, lane, z);
+          const float h0 = (ACT == ACT_RELU) ? fmaxf(z[0][0] + b0, 0.f) : fmaxf(z[0][0] + b0, 0.f) * z[0][NMAT - 1];
+          const float h1 = (ACT == ACT_RELU) ? fmaxf(z[1][0] + b1, 0.f) : fmaxf(z[1][0] + b1, 0.f) * z[1][NMAT - 1];
+          nz += (h0 != 0.f) + (h1 != 0.f);
           if (lane == 0) {
-            h_full[rows[0]] = (ACT == ACT_RELU) ? fmaxf(z[0][0] + b0, 0.f) : fmaxf(z[0][0] + b0, 0.f) * z[0][NMAT - 1];
-            h_full[rows[1]] = (ACT == ACT_RELU) ? fmaxf(z[1][0] + b1, 0.f) : fmaxf(z[1][0] + b1, 0.f) * z[1][NMAT - 1];
+            h_full[rows[0]] = h0;
+            h_full[rows[1]] = h1;
+            mask[rows[0]] = h0 != 0.f;
+            mask[rows[1]] = h1 != 0.f;
           }
         } else {
           const int rows[1] = {entry(a)};
           const float b0 = bias[rows[0]];
           float z[1][NMAT];
           gather_rows<WT, WCH, NMAT, 1>(w0, s0, up_w, up_sc, rows, d, xs, lane, z);
-          if (lane == 0)
-            h_full[rows[0]] = (ACT == ACT_RELU) ? fmaxf(z[0][0] + b0, 0.f) : fmaxf(z[0][0] + b0, 0.f) * z[0][NMAT - 1];
+          const float h0 = (ACT == ACT_RELU) ? fmaxf(z[0][0] + b0, 0.f) : fmaxf(z[0][0] + b0, 0.f) * z[0][NMAT - 1];
+          nz += (h0 != 0.f);
+          if (lane == 0) {
+            h_full[rows[0]] = h0;
+            mask[rows[0]] = h0 != 0.f;
+          }
         }
       }
     }
   }
-  if (tid == 0 && cnt_blk) cnt_blk[blockIdx.x] = block_count;
+  if (cnt_blk) {
+    // cnt_blk[block]: active neurons; cnt_blk[nb + block]: those with h != 0
+    __shared__ int nz_w[K2_WAVES];
+    if (lane == 0) nz_w[w] = nz;
+    __syncthreads();
+    if (tid == 0) {
+      cnt_blk[blockIdx.x] = block_count;
+      int tot = 0;
+#pragma unroll
+      for (int v = 0; v < K2_WAVES; ++v) tot += nz_w[v];
+      cnt_blk[nb + blockIdx.x] = tot;
+    }
+  }
 }
 
 // Up/gate over an explicit list (pi_sparse_ffn): h_list[j] for j < count, one
@@ -707,8 +735,9 @@ k_up_list(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc,
 // neuron split nc of NC.  With the XCD-aware order, the blocks that the
 // hardware places on one XCD (block ids congruent mod 8) own adjacent tiles,
 // so the tiles that share a 128-byte line of a row share that XCD's L2.
-// Each wave builds, in LDS, the list of active neurons among its share of the
-// mask (16-neuron groups g = nc*8 + w + S*k, S = 8*NC) or of an explicit list,
+// Each wave builds, in LDS, the list of neurons that its share of the mask
+// marks (16-neuron groups g = nc*8 + w + S*k, S = 8*NC; the mask marks active
+// neurons with h != 0) or of an explicit list (entries with h != 0),
 // then gathers the tile's segments of those rows, RPW = 64 / TWC rows per
 // wave-wide load and K3_LOADS loads per HBM round trip, accumulating in fp32
 // in list order.  Lanes of one chunk column are summed with a transposed
@@ -724,7 +753,8 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
        int xcd_order, const uint8_t* __restrict__ mask, const float* __restrict__ h_full,
        const int32_t* __restrict__ idx, const int32_t* __restrict__ count, const float* __restrict__ h_list,
        const float* __restrict__ b_down, float* __restrict__ y_part, const int32_t* __restrict__ cnt_blk,
-       int n_cnt_blk, int32_t* __restrict__ count_out, int32_t* __restrict__ count_out2) {
+       int n_cnt_blk, int32_t* __restrict__ count_out, int32_t* __restrict__ count_out2,
+       int32_t* __restrict__ nz_out) {
   constexpr int EPL = Tr<WT>::EPL;
   constexpr int RPW = WAVE / TWC;                 // rows per wave-wide load
   constexpr int TCOL = TWC * EPL;                 // columns per tile
@@ -742,11 +772,16 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
   const int col = tile * TCOL + q * EPL;
   const int colc = min(col, d - EPL);             // lanes past d read a valid chunk, unused
 
-  // block 0 also adds up the predictor kernel's per-block active counts
-  __shared__ int cnt_red[K3_WAVES];
-  int cpart = 0;
-  if (blockIdx.x == 0 && (count_out || count_out2))
-    for (int k = tid; k < n_cnt_blk; k += blockDim.x) cpart += cnt_blk[k];
+  // block 0 also adds up the predictor kernel's per-block counts: active
+  // neurons in cnt_blk[0, n), those with h != 0 in cnt_blk[n, 2n)
+  __shared__ int cnt_red[2][K3_WAVES];
+  const bool do_cnt = blockIdx.x == 0 && (count_out || count_out2 || nz_out);
+  int cpart = 0, zpart = 0;
+  if (do_cnt)
+    for (int k = tid; k < n_cnt_blk; k += blockDim.x) {
+      cpart += cnt_blk[k];
+      zpart += cnt_blk[n_cnt_blk + k];
+    }
 
   float acc[EPL];
 #pragma unroll
@@ -816,7 +851,7 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
       const int p = min(p0 + S * lane, cnt - 1);
       const int id = idx[p];
       const float hl = h_list[p];
-      const bool on = p0 + S * lane < cnt && id >= 0 && id < f;
+      const bool on = p0 + S * lane < cnt && id >= 0 && id < f && hl != 0.f;   // h = 0 adds nothing
       const uint64_t bal = __ballot(on);
       if (bal == 0) continue;
       if (n > K3_CAP - WAVE) flush();
@@ -838,16 +873,24 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
     const float v = group_sum<TWC>(acc[j], lane);
     if (lane < TWC) red[w][lane * EPL + j] = v;
   }
-  if (blockIdx.x == 0 && (count_out || count_out2)) {
+  if (do_cnt) {
     cpart = wave_sum(cpart);
-    if (lane == 0) cnt_red[w] = cpart;
+    zpart = wave_sum(zpart);
+    if (lane == 0) {
+      cnt_red[0][w] = cpart;
+      cnt_red[1][w] = zpart;
+    }
   }
   __syncthreads();
-  if (blockIdx.x == 0 && tid == 0 && (count_out || count_out2)) {
-    int tot = 0;
-    for (int i = 0; i < K3_WAVES; ++i) tot += cnt_red[i];
+  if (do_cnt && tid == 0) {
+    int tot = 0, tz = 0;
+    for (int i = 0; i < K3_WAVES; ++i) {
+      tot += cnt_red[0][i];
+      tz += cnt_red[1][i];
+    }
     if (count_out) *count_out = tot;
     if (count_out2) *count_out2 = tot;
+    if (nz_out) *nz_out = tz;
   }
   for (int cc = tid; cc < TCOL; cc += blockDim.x) {
     const int cg = tile * TCOL + cc;
@@ -863,13 +906,13 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
 
 // --------------------------------------------------------------- small ones
 // Ascending list of the neurons whose mask byte is set (single block of 1024
-// threads): idx[0..count), *count (and *count2 if not NULL).  The mask buffer
-// is padded to a multiple of 16 bytes and holds 0 or 1.  Each thread takes 16
+// threads): idx[0..count), *count (and *count2, *count3 if not NULL).  The mask holds
+// 0 or 1 per neuron and is read 16 bytes at a time, the ragged tail bytewise.  Each thread takes 16
 // bytes per round; a DPP scan of the per-thread counts inside each wave and a
 // scan of the wave totals give each thread its output position.
 __global__ void __launch_bounds__(1024)
 k_compact(const uint8_t* __restrict__ mask, int f, int32_t* __restrict__ idx, int32_t* __restrict__ count,
-          int32_t* __restrict__ count2) {
+          int32_t* __restrict__ count2, int32_t* __restrict__ count3) {
   __shared__ int wsum[16];
   __shared__ int base_s;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE, W = blockDim.x / WAVE;
@@ -879,11 +922,12 @@ k_compact(const uint8_t* __restrict__ mask, int f, int32_t* __restrict__ idx, in
   for (int g0 = 0; g0 < ngrp; g0 += blockDim.x) {
     const int grp = g0 + tid;
     uint32_t bits = 0;
-    if (grp < ngrp) {
+    if (grp * 16 + 16 <= f) {
       const uint4 v = reinterpret_cast<const uint4*>(mask)[grp];
       auto b4 = [](uint32_t x) __attribute__((always_inline)) { return ((x & 0x01010101u) * 0x01020408u) >> 24; };
       bits = b4(v.x) | (b4(v.y) << 4) | (b4(v.z) << 8) | (b4(v.w) << 12);
-      if (grp * 16 + 16 > f) bits &= (1u << (f - grp * 16)) - 1u;
+    } else if (grp < ngrp) {
+      for (int j = 0; j < f - grp * 16; ++j) bits |= (mask[grp * 16 + j] ? 1u : 0u) << j;   // ragged tail, bytewise
     }
     const int c = __popc(bits);
     const int inc = wave_scan(c);
@@ -908,6 +952,7 @@ k_compact(const uint8_t* __restrict__ mask, int f, int32_t* __restrict__ idx, in
   if (tid == 0) {
     *count = base_s;
     if (count2) *count2 = base_s;
+    if (count3) *count3 = base_s;
   }
 }
 

@@ -77,29 +77,33 @@ def sizes(cfg):
     return pb, wb, n_mat
 
 
-def kernel_bytes(cfg, batch, k):
+def kernel_bytes(cfg, batch, k, k_nz=None):
     """Algorithmic HBM bytes of one launch of each kernel of a layer, k active (union) neurons.
 
     Dense predictor (A, B) and its bias, the active rows of gate/up with their
-    bias, the active rows of W_down^T with their h values, and the x/y vectors
-    of the glue.  Rows of inactive neurons, scratch buffers and re-reads are
-    not counted.  The per-kernel figures sum to the per-layer formula
-    (r*d + f*r)*pb + 4f + k*(n_mat*d*wb + 4) + 4k + 8*d*B.
+    bias, the rows of W_down^T that are read with their h values, and the x/y
+    vectors of the glue.  At batch 1 the down projection reads only the k_nz
+    active neurons whose h is nonzero; at batch > 1 every union row.  Rows of
+    inactive neurons, scratch buffers and re-reads are not counted.  The
+    per-kernel figures sum to the per-layer formula
+    (r*d + f*r)*pb + 4f + k*((n_mat-1)*d*wb + 4) + k_nz*(d*wb + 4) + 8*d*B.
     """
     pb, wb, n_mat = sizes(cfg)
     d, f, r = cfg.d, cfg.ffn, cfg.rank
     n_up = n_mat - 1
+    if k_nz is None:
+        k_nz = k
     if batch == 1:
         return {"k_predict_t": r * d * pb + 8 * d,
                 "k_score": f * r * pb + 4 * f + k * (n_up * d * wb + 4),
-                "k_down": k * d * wb + 4 * k}
+                "k_down": k_nz * d * wb + 4 * k_nz}
     return {"k_bglue": 8 * d * batch, "k_bpred1": r * d * pb, "k_bsplit_t": 0,
             "k_bscore": f * r * pb + 4 * f, "k_compact": 0,
             "k_bup": k * (n_up * d * wb + 4), "k_bdown": k * d * wb + 4 * k}
 
 
-def layer_bytes(cfg, k, batch=1):
-    return float(sum(kernel_bytes(cfg, batch, k).values()))
+def layer_bytes(cfg, k, batch=1, k_nz=None):
+    return float(sum(kernel_bytes(cfg, batch, k, k_nz).values()))
 
 
 def source_digest():
@@ -200,6 +204,7 @@ def main():
     xs = torch.from_numpy(np.ascontiguousarray(xs_host)).to(dev)
     outs = torch.empty_like(xs)
     counts = torch.zeros((W + K, L), dtype=torch.int32, device=dev)
+    nz_counts = torch.zeros((W + K, L), dtype=torch.int32, device=dev)   # rows of W_down^T read
     stack = pi.Stack(layers, batch=B)
 
     # ---- every EVERY-th token slot carries events on one layer, in pairs of
@@ -224,7 +229,7 @@ def main():
         traces[t] = pi.make_trace(L, recs)
 
     def run_token(t, s):
-        stack(xs[t], outs[t], counts[t], traces[t], stream=s)
+        stack(xs[t], outs[t], counts[t], traces[t], stream=s, nz_counts=nz_counts[t])
 
     run_token(0, stream)                                           # eager warm-up of the path
     stream.synchronize()
@@ -258,6 +263,7 @@ def main():
         ms = ev0.elapsed_ms(ev1)
         times.append(ms)
         cnt_rep = counts.cpu().numpy()
+        nz_rep = nz_counts.cpu().numpy()
         for t in range(W, W + K):
             if t not in events:
                 continue
@@ -265,7 +271,7 @@ def main():
             if not ev_full[t]:
                 pair_ends[key] = evs[0].elapsed_ms(evs[n_ev - 1])
                 continue
-            kb = kernel_bytes(cfg, B, int(cnt_rep[t, ev_layer[t]]))
+            kb = kernel_bytes(cfg, B, int(cnt_rep[t, ev_layer[t]]), int(nz_rep[t, ev_layer[t]]))
             iv = [evs[i].elapsed_ms(evs[i + 1]) for i in range(len(kernels))]
             pair_full[key] = sum(iv)
             for i, k in enumerate(kernels):
@@ -276,15 +282,18 @@ def main():
     ms_per_step = ms / K
 
     cnt = counts[W:].cpu().numpy().astype(np.int64)                # [K][L]
+    cnt_nz = nz_counts[W:].cpu().numpy().astype(np.int64)
     if args.dump_counts:
         with open(args.dump_counts, "w") as fh:
             json.dump({"workload": cfg.name, "config": args.config, "layers": L, "batch": B,
                        "warmup": W, "steps": K, "repeats": args.repeats,
-                       "counts": counts.cpu().numpy().tolist()}, fh)
-    step_bytes = float(sum(layer_bytes(cfg, int(k), B) for k in cnt.ravel())) / K
+                       "counts": counts.cpu().numpy().tolist(),
+                       "nz_counts": nz_counts.cpu().numpy().tolist()}, fh)
+    step_bytes = float(sum(layer_bytes(cfg, int(k), B, int(z)) for k, z in zip(cnt.ravel(), cnt_nz.ravel()))) / K
     stack_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     mean_active = float(cnt.mean() / cfg.ffn)
-    log(f"[bench] mean active {mean_active:.4f}, {step_bytes / 1e6:.2f} MB/step, "
+    nz_share = float(cnt_nz.sum() / max(cnt.sum(), 1))
+    log(f"[bench] mean active {mean_active:.4f} (h != 0: {nz_share:.3f} of them), {step_bytes / 1e6:.2f} MB/step, "
         f"{stack_gbs:.1f} GB/s over the whole step ({stack_gbs / HBM_PEAK_GBS:.3f} of peak)")
 
     # ---- per-kernel durations sampled over the timed region, less the event-node cost
@@ -364,6 +373,7 @@ def main():
         "config": {"workload": cfg.name, "layers": L, "d": cfg.d, "ffn": cfg.ffn,
                    "rank": cfg.rank, "batch": B, "act": cfg.act, "w_dtype": cfg.w_dtype,
                    "p_dtype": cfg.p_dtype, "order": args.order, "mean_active": mean_active,
+                   "down_rows_read_share": nz_share,
                    "graphs": not args.eager, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": dk["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": dk["gbs"] / HBM_PEAK_GBS, "traffic": traffic,

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define PI_ABI_VERSION 2
+#define PI_ABI_VERSION 3
 
 typedef enum {
   PI_OK = 0,
@@ -102,7 +102,7 @@ typedef struct {
 typedef struct {
   float* x_in;      /* [batch][d]   input of the layer */
   float* scores;    /* [batch][ffn] predictor scores */
-  uint8_t* mask;    /* [batch][ffn] 1 if score > 0 */
+  uint8_t* mask;    /* [batch][ffn] 1 if score > 0; 16-byte aligned (PI_EINVAL) */
   int32_t* idx;     /* [ffn]        ascending storage ids of the union mask */
   int32_t* count;   /* [1]          number of entries in idx */
   /* Timing: hipEvent_t handles (as void*) recorded on the stream, events[0]
@@ -159,12 +159,17 @@ pi_status pi_sparse_ffn(const pi_layer* layer, const float* x, int32_t batch, co
  * joined by a residual with a parameter-free RMS norm (not on the pages; it
  * keeps firing rates stable through the stack):
  *   x_0 = x;  x_{l+1} = v / sqrt(mean(v^2) + 1e-6),  v = x_l + y_l;  out = x_L
+ * At batch 1 the down projection reads only the rows of the active neurons
+ * whose h is nonzero (a zero term adds nothing to y; ReLU zeroes every
+ * marked neuron whose pre-activation turns out <= 0).
  * counts: [n_layers] int32 active count per layer (union when batch > 1), or
- * NULL.  trace: array of n_layers records, or NULL.
+ * NULL.  nz_counts: [n_layers] int32, or NULL: rows of downT read per layer
+ * (batch 1: active neurons with h != 0; batch > 1: the union count).
+ * trace: array of n_layers records, or NULL.
  */
 pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x, int32_t batch,
-                       float* out, int32_t* counts, const pi_trace* trace, void* ws,
-                       size_t ws_bytes, void* stream);
+                       float* out, int32_t* counts, int32_t* nz_counts, const pi_trace* trace,
+                       void* ws, size_t ws_bytes, void* stream);
 
 const char* pi_status_str(pi_status s);
 int32_t pi_abi_version(void);

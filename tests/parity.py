@@ -57,6 +57,26 @@ def check_list(mask, idx, count):
     assert np.array_equal(np.asarray(idx)[:count], np.flatnonzero(m))
 
 
+def check_nz_count(layer, act, x_in, mask, nz, rel_band=1e-5):
+    """Rows of W_down^T read at batch 1: active neurons whose h is nonzero.
+
+    h != 0 exactly when the gate (ReGLU) or up (ReLU) pre-activation is > 0
+    (and, for ReGLU, the up product is nonzero).  The pre-activation z is
+    recomputed in float64 on the GPU's own layer input; neurons with |z|
+    within rel_band of max |z| may go either way."""
+    rows = np.flatnonzero(np.asarray(mask).astype(bool))
+    x = np.asarray(x_in, np.float64)
+    w = layer.gate if act == "reglu" else layer.up
+    z = oracle.decode_rows(w, rows) @ x + np.asarray(layer.bias, np.float64)[rows]
+    if act == "reglu":
+        zu = oracle.decode_rows(layer.up, rows) @ x
+        z = np.where(zu == 0.0, -np.abs(z), z)
+    tol = rel_band * (float(np.abs(z).max()) if z.size else 0.0)
+    lo, hi = int((z > tol).sum()), int((z > -tol).sum())
+    assert lo <= int(nz) <= hi, (int(nz), lo, hi)
+    return hi - lo
+
+
 def rel_err(y, y_ref):
     y = np.asarray(y, np.float64)
     y_ref = np.asarray(y_ref, np.float64)

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(pi):
 
 
 def test_abi_version_and_status_strings(pi):
-    assert pi.abi_version() == 2
+    assert pi.abi_version() == 3
     assert pi.status_str(0) == "ok"
     assert "workspace" in pi.status_str(3)
 
@@ -124,11 +124,18 @@ def test_sparse_ffn_and_stack_validation(pi):
     r = lib.pi_sparse_ffn(ctypes.byref(L), FAKE, 1, None, FAKE, None, FAKE, FAKE, 1 << 30, None)
     assert r == 1
     arr = (pi.PiLayer * 2)(L, make_layer(pi, d=1024))
-    r = lib.pi_ffn_stack(ctypes.cast(arr, ctypes.c_void_p), 2, FAKE, 1, FAKE, None, None, FAKE,
+    r = lib.pi_ffn_stack(ctypes.cast(arr, ctypes.c_void_p), 2, FAKE, 1, FAKE, None, None, None, FAKE,
                          1 << 30, None)
     assert r == 1                                      # layers of a stack share d
-    r = lib.pi_ffn_stack(ctypes.cast(arr, ctypes.c_void_p), 0, FAKE, 1, FAKE, None, None, FAKE,
+    r = lib.pi_ffn_stack(ctypes.cast(arr, ctypes.c_void_p), 0, FAKE, 1, FAKE, None, None, None, FAKE,
                          1 << 30, None)
+    assert r == 1
+    # a trace record's mask must be 16-byte aligned
+    one = (pi.PiLayer * 1)(L)
+    tr = (pi.PiTrace * 1)()
+    tr[0].mask = FAKE + 1
+    r = lib.pi_ffn_stack(ctypes.cast(one, ctypes.c_void_p), 1, FAKE, 1, FAKE, None, None,
+                         ctypes.cast(tr, ctypes.c_void_p), FAKE, 1 << 30, None)
     assert r == 1
 
 

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import workload
-from parity import BAND, TOL, check_list, check_scores_masks, check_y, compare_stack, rel_err
+from parity import BAND, TOL, check_list, check_nz_count, check_scores_masks, check_y, compare_stack, rel_err
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -221,10 +221,11 @@ def run_stack_traced(layers, x, cfg):
                          count=with_canary(1, torch.int32, -1)))
     out = with_canary(d, torch.float32)
     counts = with_canary(n, torch.int32, -1)
+    nz = with_canary(n, torch.int32, -1)
     trace = pi.make_trace(n, recs)
-    pi.ffn_stack(layers, dev(x), out, counts, trace)
+    pi.ffn_stack(layers, dev(x), out, counts, trace, nz_counts=nz)
     torch.cuda.synchronize()
-    assert canary_ok(out, d) and canary_ok(counts, n)
+    assert canary_ok(out, d) and canary_ok(counts, n) and canary_ok(nz, n)
     res = []
     for r in recs:
         sizes = dict(x_in=d, scores=f, mask=f, idx=f, count=1)
@@ -235,6 +236,9 @@ def run_stack_traced(layers, x, cfg):
                         count=int(r["count"][0].item())))
     cts = counts[:n].cpu().numpy()
     assert [r["count"] for r in res] == cts.tolist()
+    for r, v in zip(res, nz[:n].cpu().numpy().tolist()):
+        assert 0 <= v <= r["count"]
+        r["nz"] = v
     return out[:d].cpu().numpy(), res
 
 
@@ -249,7 +253,9 @@ def test_stack_small(name):
         out, trace = run_stack_traced(layers, x[0], cfg)
         ref = oracle.stack_forward(host, x)
         st = compare_stack(ref, trace, out, cfg.w_dtype)
-        say(f"  tok {tok}: {st}")
+        amb = [check_nz_count(h, cfg.act, t["x_in"], t["mask"], t["nz"]) for h, t in zip(host, trace)]
+        say(f"  tok {tok}: {st}; rows read {[t['nz'] for t in trace]} of {[t['count'] for t in trace]} "
+            f"(ambiguous {sum(amb)})")
 
 
 def test_stack_deterministic_and_graph_replay():
@@ -350,8 +356,11 @@ def test_full_size_stack(ci, n_layers, n_tok):
         worst = max(worst, st["out_err"])
         flips += st["band_flips"]
         rate = np.mean([t["count"] / cfg.ffn for t in trace])
-        say(f"  tok {tok}: active {rate:.3f} band {st['band']} flips {st['band_flips']} "
-            f"score err {st['max_score_err']:.2e} out err {st['out_err']:.2e}")
+        for h, t in zip(host, trace):
+            check_nz_count(h, cfg.act, t["x_in"], t["mask"], t["nz"])
+        nzr = np.mean([t["nz"] / max(t["count"], 1) for t in trace])
+        say(f"  tok {tok}: active {rate:.3f} (h != 0: {nzr:.3f} of them) band {st['band']} "
+            f"flips {st['band_flips']} score err {st['max_score_err']:.2e} out err {st['out_err']:.2e}")
     say(f"  worst out err {worst:.2e}, band flips {flips}")
     del layers
     torch.cuda.empty_cache()
