@@ -173,6 +173,21 @@ __device__ __forceinline__ float chunk_dot(uint4 c, float scale, const float* __
   }
 }
 
+// A value the compiler cannot see through (an SGPR set by inline asm).  Adding
+// it to the addresses of a batch of loads makes them depend on this point of
+// the program, so they cannot be hoisted above it.
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+  return z;
+}
+
+// 8.0f that the compiler cannot see as a constant.  With a literal 8, it
+// rewrites (float)q - 8 as (float)(int)(q - 8) and extracts every nibble with
+// a separate bit-field instruction; with this, each nibble costs one
+// byte-to-float conversion (v_cvt_f32_ubyte*) and one subtract.
+__device__ __forceinline__ float q4_offset() { return __int_as_float(0x41000000 + opaque_zero()); }
+
 // Q4_0 activations in LDS for the gathered dot products, pair-transposed:
 // element 32 b + j (block b, 0 <= j < 32) is half j / 16 of the float2 at
 // xq[(j % 16) * nb + b], nb = d / 32.  A lane that owns block b reads its 16
@@ -183,7 +198,8 @@ __host__ __device__ constexpr int q4t_pos(int k, int d) { return ((k & 15) * (d 
 
 // sum_j w_j * x_j over Q4_0 block `blk`, x in the pair-transposed layout; the
 // same operation order as chunk_dot<DT_Q4>.
-__device__ __forceinline__ float chunk_dot_q4t(uint4 c, float scale, const float2* __restrict__ xq, int blk, int nb) {
+__device__ __forceinline__ float chunk_dot_q4t(uint4 c, float scale, const float2* __restrict__ xq, int blk, int nb,
+                                               float off) {
   const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
   float a = 0.f;
 #pragma unroll
@@ -194,16 +210,17 @@ __device__ __forceinline__ float chunk_dot_q4t(uint4 c, float scale, const float
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const float2 xv = xq[(4 * k + b) * nb + blk];
-      a = fmaf((float)((lo >> (8 * b)) & 0xFFu) - 8.f, xv.x, a);
-      a = fmaf((float)((hi >> (8 * b)) & 0xFFu) - 8.f, xv.y, a);
+      a = fmaf((float)((lo >> (8 * b)) & 0xFFu) - off, xv.x, a);
+      a = fmaf((float)((hi >> (8 * b)) & 0xFFu) - off, xv.y, a);
     }
   }
   return a * scale;
 }
 
-// acc[j] += h * w_j over one chunk (acc has EPL entries).
+// acc[j] += h * w_j over one chunk (acc has EPL entries); off = q4_offset()
+// (Q4_0 only).
 template <int DT>
-__device__ __forceinline__ void chunk_axpy(uint4 c, float scale, float h, float* __restrict__ acc) {
+__device__ __forceinline__ void chunk_axpy(uint4 c, float scale, float h, float* __restrict__ acc, float off) {
   if constexpr (DT == DT_F32) {
     acc[0] = fmaf(h, __uint_as_float(c.x), acc[0]);
     acc[1] = fmaf(h, __uint_as_float(c.y), acc[1]);
@@ -224,8 +241,8 @@ __device__ __forceinline__ void chunk_axpy(uint4 c, float scale, float h, float*
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int j = 4 * k + b;
-        acc[j] = fmaf(hs, (float)((lo >> (8 * b)) & 0xFFu) - 8.f, acc[j]);
-        acc[j + 16] = fmaf(hs, (float)((hi >> (8 * b)) & 0xFFu) - 8.f, acc[j + 16]);
+        acc[j] = fmaf(hs, (float)((lo >> (8 * b)) & 0xFFu) - off, acc[j]);
+        acc[j + 16] = fmaf(hs, (float)((hi >> (8 * b)) & 0xFFu) - off, acc[j + 16]);
       }
     }
   }
@@ -252,14 +269,6 @@ __device__ __forceinline__ void stage_f32(float* __restrict__ lds, const float* 
 }
 
 // ------------------------------------------------------------- LDS-DMA
-// A value the compiler cannot see through (an SGPR set by inline asm).  Adding
-// it to the addresses of a batch of loads makes them depend on this point of
-// the program, so they cannot be hoisted above it.
-__device__ __forceinline__ int opaque_zero() {
-  int z;
-  asm volatile("s_mov_b32 %0, 0" : "=s"(z));
-  return z;
-}
 
 // Wait until at most N vector-memory loads of this wave are outstanding and
 // all its LDS operations are done.  Loads complete in issue order, so this
@@ -352,6 +361,7 @@ __device__ __forceinline__ void gather_rows(const void* __restrict__ w0, const u
                                             float (&z)[NN][NMAT]) {
   constexpr int EPL = Tr<WT>::EPL, TW = WAVE * EPL, NV = NN * NMAT;
   const int nch = (d + TW - 1) / TW;
+  const float off = WT == DT_Q4 ? q4_offset() : 0.f;
   float a[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) a[v] = 0.f;
@@ -377,7 +387,7 @@ __device__ __forceinline__ void gather_rows(const void* __restrict__ w0, const u
       for (int v = 0; v < NV; ++v) {
         float p;
         if constexpr (WT == DT_Q4)
-          p = chunk_dot_q4t(c[v][q], fs[v][q], reinterpret_cast<const float2*>(xs), ok ? e / 32 : 0, d / 32);
+          p = chunk_dot_q4t(c[v][q], fs[v][q], reinterpret_cast<const float2*>(xs), ok ? e / 32 : 0, d / 32, off);
         else
           p = chunk_dot<WT>(c[v][q], fs[v][q], xs + (ok ? e : 0));
         a[v] += ok ? p : 0.f;
@@ -745,7 +755,8 @@ k_up_list(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc,
 // are written to y_part[nc][cols] with plain stores.
 constexpr int K3_WAVES = 8;
 constexpr int K3_CAP = 2048;     // list entries per wave
-constexpr int K3_LOADS = 16;     // row segments per lane per HBM round trip
+constexpr int K3_LOADS = 16;     // row segments per lane per HBM round trip (8 for Q4_0, whose
+                                 // 32 values per segment need more registers to decode)
 
 template <int WT, int TWC, bool EXPLICIT>
 __global__ void __launch_bounds__(512)
@@ -786,6 +797,7 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
   float acc[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
+  const float off = WT == DT_Q4 ? q4_offset() : 0.f;
 
   int n = 0;                                      // entries in this wave's list
   // gather the listed rows' segments: entry e = e0 + k*RPW + rl for wave-load
@@ -806,14 +818,15 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
     }
     PI_ISSUE_FENCE();
 #pragma unroll
-    for (int k = 0; k < NL; ++k) chunk_axpy<WT>(c[k], sc[k], (e0 + k * RPW + rl < n) ? hv[k] : 0.f, acc);
+    for (int k = 0; k < NL; ++k) chunk_axpy<WT>(c[k], sc[k], (e0 + k * RPW + rl < n) ? hv[k] : 0.f, acc, off);
   };
   auto flush = [&]() __attribute__((always_inline)) {
-    for (int e0 = 0; e0 < n; e0 += K3_LOADS * RPW) {
+    constexpr int NLMAX = WT == DT_Q4 ? 8 : K3_LOADS;
+    for (int e0 = 0; e0 < n; e0 += NLMAX * RPW) {
       const int nl = (n - e0 + RPW - 1) / RPW;   // wave-uniform
       if (nl <= 4) batch(std::integral_constant<int, 4>{}, e0);
       else if (nl <= 8) batch(std::integral_constant<int, 8>{}, e0);
-      else batch(std::integral_constant<int, K3_LOADS>{}, e0);
+      else batch(std::integral_constant<int, NLMAX>{}, e0);
     }
     n = 0;
   };
