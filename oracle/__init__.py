@@ -29,6 +29,7 @@ What it computes (per layer, per sequence b, x_b in R^d):
       format (unite.ai, "Neuronenbewusster Operator").
   activation  ReLU:  h_i = max(b_i + W_up[i] . x, 0)
               ReGLU: h_i = max(b_i + W_gate[i] . x, 0) * (W_up[i] . x)
+              Squared ReLU: h_i = max(b_i + W_up[i] . x, 0)^2
       (GeekNews summary: ReLU / ReGLU / Squared ReLU models), computed only for
       listed neurons with m_{b,i} = 1; a neuron in the union but not in
       sequence b's own mask contributes h = 0 for b.
@@ -122,18 +123,33 @@ def union_mask(masks) -> np.ndarray:
 
 # ------------------------------------------------------------------------ FFN
 def _act(act: str, zg: np.ndarray, zu: np.ndarray | None) -> np.ndarray:
+    """The activation of a neuron from its pre-activation(s).
+
+    The GeekNews summary's model list names ReLU, ReGLU and Squared ReLU
+    (ReLU-family activations, the ones with exact zeros).  Their textbook
+    forms: ReLU max(z, 0); ReGLU max(z_gate, 0) * z_up; Squared ReLU
+    max(z, 0)^2, which is zero exactly where ReLU is."""
     if act == "relu":
         return np.maximum(zg, 0.0)
     if act == "reglu":
         return np.maximum(zg, 0.0) * zu
+    if act == "relu2":
+        r = np.maximum(zg, 0.0)
+        return r * r
     raise ValueError(act)
+
+
+def _uses_gate(act: str) -> bool:
+    """ReGLU gates with its own matrix; ReLU and Squared ReLU use the up matrix alone."""
+    return act == "reglu"
 
 
 def sparse_ffn(act, gate, up, downT, bias, X, masks, b_down=None) -> np.ndarray:
     """y[b] from the rows of the neurons in sequence b's own mask only, float64 [nb][d].
 
-    ReLU uses ``up`` with ``bias``; ReGLU uses ``gate`` with ``bias`` and ``up``
-    without bias.  Contributions are summed in ascending neuron id.
+    ReLU and Squared ReLU use ``up`` with ``bias``; ReGLU uses ``gate`` with
+    ``bias`` and ``up`` without bias.  Contributions are summed in ascending
+    neuron id.
     """
     X = np.atleast_2d(np.asarray(X, dtype=np.float64))
     masks = np.atleast_2d(np.asarray(masks, dtype=bool))
@@ -144,7 +160,7 @@ def sparse_ffn(act, gate, up, downT, bias, X, masks, b_down=None) -> np.ndarray:
         idx = active_list(masks[b])
         if idx.size:
             x = X[b]
-            if act == "relu":
+            if not _uses_gate(act):
                 zg = decode_rows(up, idx) @ x + bias[idx]
                 zu = None
             else:
@@ -167,7 +183,7 @@ def dense_ffn(act, gate, up, downT, bias, X, masks=None, b_down=None) -> np.ndar
     bias = np.asarray(bias, dtype=np.float64)
     U = decode(up)
     D = decode(downT)
-    if act == "relu":
+    if not _uses_gate(act):
         ZG = X @ U.T + bias[None, :]
         ZU = None
     else:

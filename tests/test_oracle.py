@@ -47,9 +47,11 @@ def frac_layer(L, x):
     for i in range(f):
         if not m[i]:
             continue
-        if L["act"] == "relu":
+        if L["act"] in ("relu", "relu2"):
             z = Fraction(float(bias[i])) + sum(Fraction(float(L["up"][i, k])) * X[k] for k in range(d))
             h = max(z, Fraction(0))
+            if L["act"] == "relu2":       # Squared ReLU
+                h = h * h
         else:
             g = Fraction(float(bias[i])) + sum(Fraction(float(L["gate"][i, k])) * X[k] for k in range(d))
             u = sum(Fraction(float(L["up"][i, k])) * X[k] for k in range(d))
@@ -59,7 +61,7 @@ def frac_layer(L, x):
     return s, m, y
 
 
-@pytest.mark.parametrize("act", ["relu", "reglu"])
+@pytest.mark.parametrize("act", ["relu", "reglu", "relu2"])
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_layer_matches_exact_rationals(act, seed):
     rng = np.random.default_rng(seed)
@@ -120,7 +122,7 @@ def test_union_list():
 
 
 # ------------------------------------------------------------------------- FFN
-@pytest.mark.parametrize("act", ["relu", "reglu"])
+@pytest.mark.parametrize("act", ["relu", "reglu", "relu2"])
 def test_sparse_equals_dense_masked_and_all_ones_equals_dense(act):
     rng = np.random.default_rng(6)
     d, f = 64, 96
@@ -169,6 +171,9 @@ def test_identity_closed_forms():
     b = np.full(d, 0.25, np.float32)
     y = oracle.sparse_ffn("relu", None, I, I, b, x, M)
     assert np.array_equal(y, M * np.maximum(x + 0.25, 0))
+    # Squared ReLU: the square of the ReLU closed form
+    y = oracle.sparse_ffn("relu2", None, I, I, np.zeros(d, np.float32), x, M)
+    assert np.array_equal(y, M * np.maximum(x, 0) ** 2)
 
 
 def test_permutation_invariance(gen):
@@ -306,7 +311,13 @@ def _mutants():
         return np.flatnonzero(np.asarray(mask_1d, bool)[1:]) + 1
 
     def relu_on_up(act, zg, zu):
-        return np.maximum(zg, 0.0) if act == "relu" else zg * np.maximum(zu, 0.0)
+        if act == "reglu":
+            return zg * np.maximum(zu, 0.0)
+        r = np.maximum(zg, 0.0)
+        return r * r if act == "relu2" else r
+
+    def relu2_not_squared(act, zg, zu):
+        return np.maximum(zg, 0.0) if act in ("relu", "relu2") else np.maximum(zg, 0.0) * zu
 
     def glue_no_residual(X, Y, eps=1e-6):
         V = np.atleast_2d(np.asarray(Y, dtype=np.float64))
@@ -314,7 +325,8 @@ def _mutants():
 
     return [("predictor_scores", no_bias), ("predictor_scores", transposed_A),
             ("threshold", nonstrict_threshold), ("threshold", wrong_sign_threshold),
-            ("active_list", off_by_one_list), ("_act", relu_on_up), ("rms_glue", glue_no_residual)]
+            ("active_list", off_by_one_list), ("_act", relu_on_up), ("_act", relu2_not_squared),
+            ("rms_glue", glue_no_residual)]
 
 
 @pytest.mark.parametrize("name,fn", _mutants(), ids=lambda v: getattr(v, "__name__", str(v)))
@@ -322,6 +334,7 @@ def test_planted_mistake_is_caught(monkeypatch, gen, name, fn):
     monkeypatch.setattr(oracle, name, fn)
     pins = [lambda: test_layer_matches_exact_rationals("relu", 0),
             lambda: test_layer_matches_exact_rationals("reglu", 1),
+            lambda: test_layer_matches_exact_rationals("relu2", 2),
             test_predictor_zero_weights_gives_bias,
             test_threshold_is_strict_and_nan_inactive,
             test_active_list_matches_library,
