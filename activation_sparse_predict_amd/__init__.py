@@ -22,10 +22,10 @@ LIB_PATH = os.path.join(_HERE, "libpi.so")
 
 PI_OK, PI_EINVAL, PI_EUNSUPPORTED, PI_EWORKSPACE, PI_EHIP = 0, 1, 2, 3, 4
 PI_F32, PI_F16, PI_Q4_0 = 0, 1, 2
-PI_RELU, PI_REGLU = 0, 1
+PI_RELU, PI_REGLU, PI_RELU2 = 0, 1, 2
 
 _DTYPE = {"f32": PI_F32, "f16": PI_F16, "q4_0": PI_Q4_0}
-_ACT = {"relu": PI_RELU, "reglu": PI_REGLU}
+_ACT = {"relu": PI_RELU, "reglu": PI_REGLU, "relu2": PI_RELU2}
 
 
 class PiError(RuntimeError):

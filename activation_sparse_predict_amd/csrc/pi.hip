@@ -37,7 +37,7 @@ pi_status check_layer(const pi_layer* L) {
   if (!L) return PI_EINVAL;
   if (L->d <= 0 || L->ffn <= 0 || L->rank <= 0) return PI_EINVAL;
   if (L->d % 64 != 0 || L->rank % 64 != 0) return PI_EINVAL;
-  if (L->act != PI_RELU && L->act != PI_REGLU) return PI_EINVAL;
+  if (L->act != PI_RELU && L->act != PI_REGLU && L->act != PI_RELU2) return PI_EINVAL;
   if (L->w_dtype != PI_F32 && L->w_dtype != PI_F16 && L->w_dtype != PI_Q4_0) return PI_EINVAL;
   if (L->p_dtype == PI_Q4_0) return PI_EUNSUPPORTED;
   if (L->d > kMaxD || L->rank > kMaxRank) return PI_EUNSUPPORTED;   // vectors staged whole in LDS
@@ -315,20 +315,22 @@ void launch_k2_fused(const pi_layer* L, const K2Args& a, hipStream_t st) {
   }
 }
 
+template <int PT, int WT, int PCH>
+void launch_k2_act(const pi_layer* L, const K2Args& a, hipStream_t st) {
+  switch (L->act) {
+    case PI_REGLU: return launch_k2_fused<PT, WT, ACT_REGLU, PCH>(L, a, st);
+    case PI_RELU2: return launch_k2_fused<PT, WT, ACT_RELU2, PCH>(L, a, st);
+    default: return launch_k2_fused<PT, WT, ACT_RELU, PCH>(L, a, st);
+  }
+}
+
 template <int PT, int PCH>
 void launch_k2_p(const pi_layer* L, bool fuse, const K2Args& a, hipStream_t st) {
   if (!fuse) return launch_k2_t<PT, DT_F32, ACT_RELU, false, PCH, 1>(L, a, st);
-  const bool reglu = L->act == PI_REGLU;
   switch (L->w_dtype) {
-    case PI_F32:
-      return reglu ? launch_k2_fused<PT, DT_F32, ACT_REGLU, PCH>(L, a, st)
-                   : launch_k2_fused<PT, DT_F32, ACT_RELU, PCH>(L, a, st);
-    case PI_F16:
-      return reglu ? launch_k2_fused<PT, DT_F16, ACT_REGLU, PCH>(L, a, st)
-                   : launch_k2_fused<PT, DT_F16, ACT_RELU, PCH>(L, a, st);
-    default:
-      return reglu ? launch_k2_fused<PT, DT_Q4, ACT_REGLU, PCH>(L, a, st)
-                   : launch_k2_fused<PT, DT_Q4, ACT_RELU, PCH>(L, a, st);
+    case PI_F32: return launch_k2_act<PT, DT_F32, PCH>(L, a, st);
+    case PI_F16: return launch_k2_act<PT, DT_F16, PCH>(L, a, st);
+    default: return launch_k2_act<PT, DT_Q4, PCH>(L, a, st);
   }
 }
 
@@ -411,22 +413,22 @@ void launch_up_list_t(const pi_layer* L, const float* x, const int32_t* idx, con
   }
 }
 
+template <int WT>
+void up_list_w(const pi_layer* L, const float* x, const int32_t* idx, const int32_t* count, float* h_list,
+               hipStream_t st) {
+  switch (L->act) {
+    case PI_REGLU: return launch_up_list_t<WT, ACT_REGLU>(L, x, idx, count, h_list, st);
+    case PI_RELU2: return launch_up_list_t<WT, ACT_RELU2>(L, x, idx, count, h_list, st);
+    default: return launch_up_list_t<WT, ACT_RELU>(L, x, idx, count, h_list, st);
+  }
+}
+
 void up_list(const pi_layer* L, const float* x, const int32_t* idx, const int32_t* count, float* h_list,
              hipStream_t st) {
-  const bool reglu = L->act == PI_REGLU;
   switch (L->w_dtype) {
-    case PI_F32:
-      reglu ? launch_up_list_t<DT_F32, ACT_REGLU>(L, x, idx, count, h_list, st)
-            : launch_up_list_t<DT_F32, ACT_RELU>(L, x, idx, count, h_list, st);
-      break;
-    case PI_F16:
-      reglu ? launch_up_list_t<DT_F16, ACT_REGLU>(L, x, idx, count, h_list, st)
-            : launch_up_list_t<DT_F16, ACT_RELU>(L, x, idx, count, h_list, st);
-      break;
-    default:
-      reglu ? launch_up_list_t<DT_Q4, ACT_REGLU>(L, x, idx, count, h_list, st)
-            : launch_up_list_t<DT_Q4, ACT_RELU>(L, x, idx, count, h_list, st);
-      break;
+    case PI_F32: return up_list_w<DT_F32>(L, x, idx, count, h_list, st);
+    case PI_F16: return up_list_w<DT_F16>(L, x, idx, count, h_list, st);
+    default: return up_list_w<DT_Q4>(L, x, idx, count, h_list, st);
   }
 }
 
@@ -503,19 +505,22 @@ void b_ffn_t(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, co
 
 // the FFN over the union list for every sequence: BD_SPLIT partial vectors
 // y_part [BD_SPLIT][32][d] (rows b < batch written)
+template <int WT>
+void b_ffn_w(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, const int32_t* ucount, float* y,
+             hipStream_t st, const pi_trace* tr) {
+  switch (L->act) {
+    case PI_REGLU: return b_ffn_t<WT, ACT_REGLU>(L, batch, W, ulist, ucount, y, st, tr);
+    case PI_RELU2: return b_ffn_t<WT, ACT_RELU2>(L, batch, W, ulist, ucount, y, st, tr);
+    default: return b_ffn_t<WT, ACT_RELU>(L, batch, W, ulist, ucount, y, st, tr);
+  }
+}
+
 void b_ffn(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, const int32_t* ucount, float* y,
            hipStream_t st, const pi_trace* tr = nullptr) {
-  const bool reglu = L->act == PI_REGLU;
   switch (L->w_dtype) {
-    case PI_F32:
-      return reglu ? b_ffn_t<DT_F32, ACT_REGLU>(L, batch, W, ulist, ucount, y, st, tr)
-                   : b_ffn_t<DT_F32, ACT_RELU>(L, batch, W, ulist, ucount, y, st, tr);
-    case PI_F16:
-      return reglu ? b_ffn_t<DT_F16, ACT_REGLU>(L, batch, W, ulist, ucount, y, st, tr)
-                   : b_ffn_t<DT_F16, ACT_RELU>(L, batch, W, ulist, ucount, y, st, tr);
-    default:
-      return reglu ? b_ffn_t<DT_Q4, ACT_REGLU>(L, batch, W, ulist, ucount, y, st, tr)
-                   : b_ffn_t<DT_Q4, ACT_RELU>(L, batch, W, ulist, ucount, y, st, tr);
+    case PI_F32: return b_ffn_w<DT_F32>(L, batch, W, ulist, ucount, y, st, tr);
+    case PI_F16: return b_ffn_w<DT_F16>(L, batch, W, ulist, ucount, y, st, tr);
+    default: return b_ffn_w<DT_Q4>(L, batch, W, ulist, ucount, y, st, tr);
   }
 }
 

@@ -352,7 +352,7 @@ k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, con
       const _Float16* __restrict__ xh, const _Float16* __restrict__ xl, const int32_t* __restrict__ ulist,
       const int32_t* __restrict__ ucount, const uint8_t* __restrict__ m_nm, _Float16* __restrict__ hh_out,
       _Float16* __restrict__ hl_out) {
-  constexpr int NMAT = (ACT == ACT_RELU) ? 1 : 2;
+  constexpr int NMAT = act_nmat<ACT>();
   __shared__ float red[BUP_W][NMAT][BM * BM];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int col = lane % 32, half = lane / 32;
@@ -436,9 +436,7 @@ k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, con
       z[mt] = s;
     }
     const int rw = ulist[t0 + c];
-    float h;
-    if constexpr (ACT == ACT_RELU) h = fmaxf(z[0] + bias[rw], 0.f);
-    else h = fmaxf(z[0] + bias[rw], 0.f) * z[NMAT - 1];
+    float h = act_h<ACT>(z[0], bias[rw], z[NMAT - 1]);
     if (m_nm[(size_t)rw * BM + b] == 0) h = 0.f;
     _Float16 a, l;
     split_f16(h, &a, &l);

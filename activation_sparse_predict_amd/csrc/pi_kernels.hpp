@@ -30,7 +30,22 @@
 namespace pik {
 
 enum { DT_F32 = 0, DT_F16 = 1, DT_Q4 = 2 };
-enum { ACT_RELU = 0, ACT_REGLU = 1 };
+enum { ACT_RELU = 0, ACT_REGLU = 1, ACT_RELU2 = 2 };
+
+// Matrices an activation reads per neuron: the gate and up rows for ReGLU,
+// the up row alone for ReLU and Squared ReLU.
+template <int ACT> constexpr int act_nmat() { return ACT == ACT_REGLU ? 2 : 1; }
+
+// h from the gate (ReGLU) or up (ReLU, Squared ReLU) dot product zg, its bias
+// b and, for ReGLU, the up dot product zu:
+//   ReLU max(zg + b, 0); ReGLU max(zg + b, 0) * zu; Squared ReLU max(zg + b, 0)^2.
+template <int ACT>
+__device__ __forceinline__ float act_h(float zg, float b, float zu) {
+  const float r = fmaxf(zg + b, 0.f);
+  if constexpr (ACT == ACT_REGLU) return r * zu;
+  else if constexpr (ACT == ACT_RELU2) return r * r;
+  else return r;
+}
 
 constexpr int WAVE = 64;
 
@@ -653,9 +668,9 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
       if (mask2) mask2[i] = on ? 1 : 0;
     }
     if constexpr (FUSE) {
-      constexpr int NMAT = (ACT == ACT_RELU) ? 1 : 2;
-      const void* w0 = (ACT == ACT_RELU) ? up_w : gate_w;
-      const uint16_t* s0 = (ACT == ACT_RELU) ? up_sc : gate_sc;
+      constexpr int NMAT = act_nmat<ACT>();
+      const void* w0 = (ACT == ACT_REGLU) ? gate_w : up_w;
+      const uint16_t* s0 = (ACT == ACT_REGLU) ? gate_sc : up_sc;
       // wave w takes entries w, w + 4 (a pair when both exist and the pair's
       // rows fit the registers), then w + 8, w + 12, ...
       constexpr bool PAIR = NMAT * WCH <= 16;
@@ -665,8 +680,8 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
           const float b0 = bias[rows[0]], b1 = bias[rows[1]];
           float z[2][NMAT];
           gather_rows<WT, WCH, NMAT, 2>(w0, s0, up_w, up_sc, rows, d, xs, lane, z);
-          const float h0 = (ACT == ACT_RELU) ? fmaxf(z[0][0] + b0, 0.f) : fmaxf(z[0][0] + b0, 0.f) * z[0][NMAT - 1];
-          const float h1 = (ACT == ACT_RELU) ? fmaxf(z[1][0] + b1, 0.f) : fmaxf(z[1][0] + b1, 0.f) * z[1][NMAT - 1];
+          const float h0 = act_h<ACT>(z[0][0], b0, z[0][NMAT - 1]);
+          const float h1 = act_h<ACT>(z[1][0], b1, z[1][NMAT - 1]);
           nz += (h0 != 0.f) + (h1 != 0.f);
           if (lane == 0) {
             h_full[rows[0]] = h0;
@@ -679,7 +694,7 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
           const float b0 = bias[rows[0]];
           float z[1][NMAT];
           gather_rows<WT, WCH, NMAT, 1>(w0, s0, up_w, up_sc, rows, d, xs, lane, z);
-          const float h0 = (ACT == ACT_RELU) ? fmaxf(z[0][0] + b0, 0.f) : fmaxf(z[0][0] + b0, 0.f) * z[0][NMAT - 1];
+          const float h0 = act_h<ACT>(z[0][0], b0, z[0][NMAT - 1]);
           nz += (h0 != 0.f);
           if (lane == 0) {
             h_full[rows[0]] = h0;
@@ -723,9 +738,9 @@ k_up_list(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc,
     stage_f32<8>(xs, x, d, tid, blockDim.x);
   }
   __syncthreads();
-  constexpr int NMAT = (ACT == ACT_RELU) ? 1 : 2;
-  const void* w0 = (ACT == ACT_RELU) ? up_w : gate_w;
-  const uint16_t* s0 = (ACT == ACT_RELU) ? up_sc : gate_sc;
+  constexpr int NMAT = act_nmat<ACT>();
+  const void* w0 = (ACT == ACT_REGLU) ? gate_w : up_w;
+  const uint16_t* s0 = (ACT == ACT_REGLU) ? gate_sc : up_sc;
   for (int j = blockIdx.x * W + w; j < cnt; j += gridDim.x * W) {
     const int i = idx[j];
     float h = 0.f;
@@ -733,7 +748,7 @@ k_up_list(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc,
       const int rows[1] = {i};
       float z[1][NMAT];
       gather_rows<WT, WCH, NMAT, 1>(w0, s0, up_w, up_sc, rows, d, xs, lane, z);
-      h = (ACT == ACT_RELU) ? fmaxf(z[0][0] + bias[i], 0.f) : fmaxf(z[0][0] + bias[i], 0.f) * z[0][NMAT - 1];
+      h = act_h<ACT>(z[0][0], bias[i], z[0][NMAT - 1]);
     }
     if (lane == 0) h_list[j] = h;
   }

@@ -65,8 +65,9 @@ typedef enum {
 typedef enum { PI_F32 = 0, PI_F16 = 1, PI_Q4_0 = 2 } pi_dtype;
 
 /* ReLU: h = max(b + W_up x, 0).  ReGLU: h = max(b + W_gate x, 0) * (W_up x).
+ * Squared ReLU: h = max(b + W_up x, 0)^2.
  * (GeekNews summary: ReLU / ReGLU / Squared-ReLU models.) */
-typedef enum { PI_RELU = 0, PI_REGLU = 1 } pi_act;
+typedef enum { PI_RELU = 0, PI_REGLU = 1, PI_RELU2 = 2 } pi_act;
 
 /* One weight matrix [ffn][d].  F32/F16: `w` points at ffn*d elements and
  * `scale` is NULL.  Q4_0 (blocks of 32 4-bit values q in [0,15] with one
@@ -88,7 +89,7 @@ typedef struct {
   int32_t p_dtype;  /* pi_dtype of A and B (F32 or F16) */
   const void* A;    /* [rank][d] predictor first matrix */
   const void* B;    /* [ffn][rank] predictor second matrix, storage order */
-  const float* bias;/* [ffn] bias of the gate (ReGLU) or up (ReLU) projection */
+  const float* bias;/* [ffn] bias of the gate (ReGLU) or up (ReLU, Squared ReLU) projection */
   const float* pbias;/* [ffn] predictor output bias, s_i = pbias_i + B[i] . (A x);
                        NULL = use `bias` */
   pi_mat gate;      /* [ffn][d]; REGLU only (ignored for RELU) */
@@ -144,6 +145,7 @@ pi_status pi_predict(const pi_layer* layer, const float* x, int32_t batch, float
  *   for each listed i (and, when batch > 1, only where mask_{b,i} = 1):
  *     ReLU:  h = max(bias_i + up[i] . x_b, 0)
  *     ReGLU: h = max(bias_i + gate[i] . x_b, 0) * (up[i] . x_b)
+ *     Squared ReLU: h = max(bias_i + up[i] . x_b, 0)^2
  *   y_b = sum_i h * downT[i]  (+ b_down)
  * idx: ascending or not, distinct entries, first min(*count, ffn) used (count
  * is read on the device and clamped to [0, ffn]); entries outside [0, ffn)

@@ -38,6 +38,7 @@ SMALL = {
     "q4-relu": workload.CONFIGS[4].with_(d=1024, ffn=3001, rank=128, n_layers=2),
     "q4-reglu": workload.CONFIGS[4].with_(act="reglu", d=512, ffn=777, rank=64, n_layers=2),
     "f32-relu": workload.CONFIGS[0].with_(d=256, ffn=1000, rank=64, n_layers=2),
+    "f16-relu2": workload.CONFIGS[3].with_(act="relu2", d=512, ffn=1500, rank=128, n_layers=2),
 }
 
 

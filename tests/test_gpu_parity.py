@@ -36,6 +36,8 @@ SMALL = {
     "q4-relu": workload.CONFIGS[4].with_(d=1024, ffn=3001, rank=128, n_layers=3),
     "q4-reglu": workload.CONFIGS[4].with_(act="reglu", d=512, ffn=1500, rank=64, n_layers=2),
     "f32w-f16p-relu": workload.CONFIGS[0].with_(p_dtype="f16", d=256, ffn=777, rank=64, n_layers=2),
+    "f16-relu2": workload.CONFIGS[2].with_(act="relu2", d=512, ffn=2085, rank=128, n_layers=3),
+    "q4-relu2": workload.CONFIGS[4].with_(act="relu2", d=512, ffn=1500, rank=64, n_layers=2),
 }
 
 
@@ -115,7 +117,7 @@ def test_layer_small(name):
             f"score err {st['max_score_err']:.2e} y err {e:.2e}")
 
 
-@pytest.mark.parametrize("name", ["f16-reglu", "q4-relu", "f32-relu"])
+@pytest.mark.parametrize("name", ["f16-reglu", "q4-relu", "f32-relu", "f16-relu2"])
 def test_sparse_ffn_edge_cases(name):
     cfg = SMALL[name]
     say(f"[edge] {name}")
@@ -242,7 +244,8 @@ def run_stack_traced(layers, x, cfg):
     return out[:d].cpu().numpy(), res
 
 
-@pytest.mark.parametrize("name", ["f16-reglu", "f16-relu", "q4-relu", "q4-reglu", "f32w-f16p-relu"])
+@pytest.mark.parametrize("name", ["f16-reglu", "f16-relu", "q4-relu", "q4-reglu", "f32w-f16p-relu", "f16-relu2",
+                                  "q4-relu2"])
 def test_stack_small(name):
     cfg = SMALL[name]
     say(f"[stack_small] {name} L={cfg.n_layers}")

@@ -210,7 +210,7 @@ class FFNConfig:
     ffn: int
     rank: int
     n_layers: int
-    act: str          # "relu" | "reglu"
+    act: str          # "relu" | "reglu" | "relu2" (Squared ReLU)
     w_dtype: str      # "f32" | "f16" | "q4_0"
     p_dtype: str      # "f32" | "f16"
     mean_active: float
