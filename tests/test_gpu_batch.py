@@ -196,3 +196,53 @@ def test_batch_full_size(ci, nb, n_layers):
             f"worst out err {worst:.2e}")
     del layers
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------- maximum sizes
+def test_batch_maximum_width_and_rank():
+    """Batch 32 at the largest width and rank the library accepts (d = 16384, rank = 4096)."""
+    cfg = workload.CONFIGS[3].with_(d=16384, ffn=1100, rank=4096, n_layers=1)
+    nb = 32
+    say(f"[batch_max] d={cfg.d} f={cfg.ffn} r={cfg.rank} batch {nb}")
+    lw = workload.make_layer(cfg, 0)
+    L = pi.DeviceLayer.upload(lw, DEV)
+    X = workload.make_x(cfg, 4, seqs=nb)
+    ref = oracle.layer_forward(lw, X)
+    scores, mask, idx, count = run_predict(L, X)
+    for b in range(nb):
+        check_scores_masks(ref["scores"][b], scores[b], mask[b])
+    check_list(mask.astype(bool).any(axis=0), idx, count)
+    Y = run_sparse_ffn(L, X, ref["idx"], ref["masks"])
+    for b in range(nb):
+        check_y(Y[b], ref["y"][b], TOL[cfg.w_dtype])
+    say(f"  union {count}")
+
+
+def test_batch_maximum_ffn_every_neuron_active():
+    """The largest ffn of the batched path (65536) with every neuron active in every
+    sequence: the union list fills each split of the down GEMM to its LDS capacity."""
+    cfg = workload.CONFIGS[3].with_(d=64, ffn=65536, rank=64, n_layers=1)
+    nb = 8
+    lw = workload.make_layer(cfg, 0)
+    lw.pbias = np.full(cfg.ffn, 1000.0, np.float32)          # every score far above 0
+    say(f"[batch_max_ffn] d={cfg.d} f={cfg.ffn} r={cfg.rank} batch {nb}, all active")
+    L = pi.DeviceLayer.upload(lw, DEV)
+    X = workload.make_x(cfg, 6, seqs=nb)
+    ref = oracle.layer_forward(lw, X)
+    assert ref["count"] == cfg.ffn
+    scores, mask, idx, count = run_predict(L, X)
+    assert count == cfg.ffn and mask.all()
+    check_list(mask.astype(bool).any(axis=0), idx, count)
+    Y = run_sparse_ffn(L, X, ref["idx"], ref["masks"])
+    for b in range(nb):
+        check_y(Y[b], ref["y"][b], TOL[cfg.w_dtype])
+    # the stack path on the same layer: its union count is every neuron too
+    out = torch.empty(nb, cfg.d, device=DEV)
+    counts = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    pi.ffn_stack([L], dev(X), out, counts, batch=nb)
+    torch.cuda.synchronize()
+    assert int(counts[0]) == cfg.ffn
+    x_next = oracle.rms_glue(X, ref["y"])
+    for b in range(nb):
+        check_y(out[b].cpu().numpy(), x_next[b], max(TOL[cfg.w_dtype], 1e-5))
+

@@ -367,3 +367,36 @@ def test_full_size_stack(ci, n_layers, n_tok):
     say(f"  worst out err {worst:.2e}, band flips {flips}")
     del layers
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------- maximum sizes
+# The largest width and rank the library accepts (d <= 16384, rank <= 4096:
+# vectors are staged whole in LDS), with a ragged ffn.
+MAX = {
+    "f16-reglu": workload.CONFIGS[1].with_(d=16384, ffn=1100, rank=4096, n_layers=2),
+    "q4-relu": workload.CONFIGS[4].with_(d=16384, ffn=777, rank=4096, n_layers=2),
+}
+
+
+@pytest.mark.parametrize("name", list(MAX))
+def test_maximum_width_and_rank(name):
+    cfg = MAX[name]
+    say(f"[max] {name} d={cfg.d} f={cfg.ffn} r={cfg.rank} {cfg.w_dtype}/{cfg.p_dtype} {cfg.act}")
+    host = [workload.make_layer(cfg, l) for l in range(cfg.n_layers)]
+    layers = [pi.DeviceLayer.upload(h, DEV) for h in host]
+    x = workload.make_x(cfg, 5)
+    # single layer: predictor and the FFN over the oracle's list
+    ref = oracle.layer_forward(host[0], x)
+    scores, mask, idx, count = run_predict(layers[0], x[0])
+    check_scores_masks(ref["scores"][0], scores, mask)
+    check_list(mask, idx, count)
+    check_y(run_sparse_ffn(layers[0], x[0], ref["idx"]), ref["y"][0], TOL[cfg.w_dtype])
+    # the stack, layer-locally replayed
+    out, trace = run_stack_traced(layers, x[0], cfg)
+    st = compare_stack(oracle.stack_forward(host, x), trace, out, cfg.w_dtype)
+    for h, t in zip(host, trace):
+        check_nz_count(h, cfg.act, t["x_in"], t["mask"], t["nz"])
+    say(f"  count {count}, stack {st}")
+    del layers
+    torch.cuda.empty_cache()
+
