@@ -469,8 +469,13 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
         const _Float16* __restrict__ hl_in, const float* __restrict__ b_down, int batch,
         float* __restrict__ y_part) {
   constexpr int NW = (WT == DT_F16) ? 1 : 2;      // weight tiles: hi (and lo for fp32 and Q4_0)
-  __shared__ _Float16 wt[NW][BM][BD_PAD];         // [column][position]
-  __shared__ float red[4][BM * BM];
+  // The weight tiles [NW][column][position] and, after the last chunk, the
+  // waves' partial sums [4][BM * BM] share one buffer: 16 KB less LDS per
+  // block, so two blocks fit on a CU with fp32/Q4_0 weights, three with fp16.
+  constexpr size_t WT_BYTES = sizeof(_Float16) * NW * BM * BD_PAD, RED_BYTES = sizeof(float) * 4 * BM * BM;
+  __shared__ __attribute__((aligned(16))) unsigned char bd_smem[WT_BYTES > RED_BYTES ? WT_BYTES : RED_BYTES];
+  auto& wt = *reinterpret_cast<_Float16(*)[NW][BM][BD_PAD]>(bd_smem);
+  auto& red = *reinterpret_cast<float(*)[4][BM * BM]>(bd_smem);
   __shared__ int rows_l[BD_ROWS];                 // this split's share of the union list
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int ntile = (d + BM - 1) / BM;
