@@ -232,10 +232,11 @@ __device__ __forceinline__ float chunk_dot_q4t(uint4 c, float scale, const float
   return a * scale;
 }
 
-// acc[j] += h * w_j over one chunk (acc has EPL entries); off = q4_offset()
-// (Q4_0 only).
+// acc[j] += h * w_j over one chunk (acc has EPL entries).  For Q4_0 it adds
+// h d q_j and leaves the -8 offset to the caller: hsum collects h d, and
+// acc[j] - 8 hsum is the sum of h d (q_j - 8) = h w_j.
 template <int DT>
-__device__ __forceinline__ void chunk_axpy(uint4 c, float scale, float h, float* __restrict__ acc, float off) {
+__device__ __forceinline__ void chunk_axpy(uint4 c, float scale, float h, float* __restrict__ acc, float& hsum) {
   if constexpr (DT == DT_F32) {
     acc[0] = fmaf(h, __uint_as_float(c.x), acc[0]);
     acc[1] = fmaf(h, __uint_as_float(c.y), acc[1]);
@@ -247,6 +248,7 @@ __device__ __forceinline__ void chunk_axpy(uint4 c, float scale, float h, float*
     for (int j = 0; j < 8; ++j) acc[j] = fmaf(h, (float)v[j], acc[j]);
   } else {
     const float hs = h * scale;
+    hsum += hs;
     const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -256,8 +258,8 @@ __device__ __forceinline__ void chunk_axpy(uint4 c, float scale, float h, float*
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int j = 4 * k + b;
-        acc[j] = fmaf(hs, (float)((lo >> (8 * b)) & 0xFFu) - off, acc[j]);
-        acc[j + 16] = fmaf(hs, (float)((hi >> (8 * b)) & 0xFFu) - off, acc[j + 16]);
+        acc[j] = fmaf(hs, (float)((lo >> (8 * b)) & 0xFFu), acc[j]);
+        acc[j + 16] = fmaf(hs, (float)((hi >> (8 * b)) & 0xFFu), acc[j + 16]);
       }
     }
   }
@@ -814,7 +816,7 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
   float acc[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
-  const float off = WT == DT_Q4 ? q4_offset() : 0.f;
+  float hsum = 0.f;                               // Q4_0: sum of h d over this lane's segments
 
   int n = 0;                                      // entries in this wave's list
   // gather the listed rows' segments: entry e = e0 + k*RPW + rl for wave-load
@@ -835,7 +837,7 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
     }
     PI_ISSUE_FENCE();
 #pragma unroll
-    for (int k = 0; k < NL; ++k) chunk_axpy<WT>(c[k], sc[k], (e0 + k * RPW + rl < n) ? hv[k] : 0.f, acc, off);
+    for (int k = 0; k < NL; ++k) chunk_axpy<WT>(c[k], sc[k], (e0 + k * RPW + rl < n) ? hv[k] : 0.f, acc, hsum);
   };
   auto flush = [&]() __attribute__((always_inline)) {
     constexpr int NLMAX = WT == DT_Q4 ? 8 : K3_LOADS;
@@ -895,6 +897,10 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
     }
   }
   if (n > 0) flush();
+  if constexpr (WT == DT_Q4) {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) acc[j] = fmaf(-8.f, hsum, acc[j]);
+  }
 
   // Sum the RPW row lanes of each chunk column: lanes with equal lane % TWC
   // hold the same columns; lane q < TWC writes the wave's sums for chunk q.
