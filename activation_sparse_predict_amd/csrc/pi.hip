@@ -224,23 +224,23 @@ int k2_blocks_max(int ffn) { return std::max(k2_blocks_for(ffn, 64, PI_F32), k2_
 
 // K3: tiles of TWC = 4 chunks per row (64-byte row segments: one request per
 // row and tile, half an L2 line, the other half read by the neighbouring tile
-// on the same XCD), 8 chunks (a whole 128-byte line) for rows of 1024 chunks
-// or more (measured on MI355X: 15% faster at d = 8192 fp16, 12% slower at
-// d = 4096), fewer when the row is short, and NC neuron splits so that
-// the grid has at least ~256 blocks of 8 waves.  Wider tiles scan the mask
-// fewer times per row but give fewer blocks; narrower ones multiply the L2
-// requests per byte.
+// on the same XCD), 8 chunks (a whole 128-byte line) for rows of 768 chunks
+// or more (measured on MI355X: 15% faster at d = 8192 fp16, 23% at d = 7168,
+// 12% slower at d = 4096), fewer when the row is short, and NC neuron splits
+// so that the grid has at most 256 blocks of 8 waves (one round on the CUs).
+// Wider tiles scan the mask fewer times per row but give fewer blocks;
+// narrower ones multiply the L2 requests per byte.
 struct K3Shape {
   int twc, ct, nc;
 };
 K3Shape k3_shape(int d, int dt) {
   const int nchunks = d / epl_of(dt);
   K3Shape s;
-  s.twc = nchunks >= 1024 ? 8 : nchunks >= 64 ? 4 : nchunks >= 32 ? 2 : 1;
+  s.twc = nchunks >= 768 ? 8 : nchunks >= 64 ? 4 : nchunks >= 32 ? 2 : 1;
   s.ct = cdiv(nchunks, s.twc);
   // the next layer's predictor kernel stages x and the NC partials in LDS
   const int lds_parts = 147456 / (4 * dma_pad(d)) - 1;
-  s.nc = std::max(1, std::min(std::min(kMaxParts, lds_parts), cdiv(256, s.ct)));
+  s.nc = std::max(1, std::min(std::min(kMaxParts, lds_parts), std::max(1, 256 / s.ct)));
   return s;
 }
 
