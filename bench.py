@@ -106,6 +106,27 @@ def layer_bytes(cfg, k, batch=1, k_nz=None):
     return float(sum(kernel_bytes(cfg, batch, k, k_nz).values()))
 
 
+def copy_bandwidth(torch, dev, stream, mib=1024, reps=5):
+    """Device-copy bandwidth measured in this run: read + write bytes of a plain
+    elementwise copy of `mib` MiB, per second (the median of `reps` copies)."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device=dev)
+    dst = torch.empty_like(src)
+    times = []
+    with torch.cuda.stream(stream):
+        dst.copy_(src)
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dst.copy_(src)
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+    del src, dst
+    ms = sorted(times)[len(times) // 2]
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
 def source_digest():
     """sha256 over the HIP sources; counter summaries taken on other sources do not apply."""
     h = hashlib.sha256()
@@ -291,6 +312,9 @@ def main():
                        "nz_counts": nz_counts.cpu().numpy().tolist()}, fh)
     step_bytes = float(sum(layer_bytes(cfg, int(k), B, int(z)) for k, z in zip(cnt.ravel(), cnt_nz.ravel()))) / K
     stack_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    copy_gbs = copy_bandwidth(torch, dev, stream)
+    log(f"[bench] device copy in this run: {copy_gbs:.1f} GB/s (read + write); the step reaches "
+        f"{stack_gbs / copy_gbs:.3f} of it")
     mean_active = float(cnt.mean() / cfg.ffn)
     nz_share = float(cnt_nz.sum() / max(cnt.sum(), 1))
     log(f"[bench] mean active {mean_active:.4f} (h != 0: {nz_share:.3f} of them), {step_bytes / 1e6:.2f} MB/step, "
@@ -377,12 +401,14 @@ def main():
                    "graphs": not args.eager, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": dk["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": dk["gbs"] / HBM_PEAK_GBS, "traffic": traffic,
+                     "frac_of_measured_copy": dk["gbs"] / copy_gbs,
                      "kernel": dom, "avg_launch_us": dk["avg_us"],
                      "alg_bytes_per_launch": dk["alg_bytes_per_launch"],
                      "launches_timed": dk["launches"], "event_node_us_subtracted": node_us,
                      "traffic_unit": "HBM bytes per launch (counter summary "
                                      + (tr["file"] if tr else "absent or stale") + ")"},
         "stack_hbm": {"achieved": stack_gbs, "frac": stack_gbs / HBM_PEAK_GBS, "unit": "GB/s",
+                      "copy_gbs_measured": copy_gbs, "frac_of_copy": stack_gbs / copy_gbs,
                       "alg_bytes_per_step": step_bytes},
         "kernels": per_kernel,
         "cpu_baseline": cpu,
