@@ -498,7 +498,8 @@ void b_ffn_t(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, co
                      L->gate.scale, L->up.w, L->up.scale, L->bias, L->ffn, L->d, W.xh, W.xl, ulist, ucount, W.mnm,
                      W.hh, W.hl);
   mark(tr, 6, st);
-  hipLaunchKernelGGL(pib::k_bdown<WT>, dim3(cdiv(L->d, kBatchM) * pib::BD_SPLIT), dim3(256), 0, st, L->downT.w,
+  hipLaunchKernelGGL(pib::k_bdown<WT>, dim3(cdiv(L->d, kBatchM * pib::bd_tiles<WT>()) * pib::BD_SPLIT), dim3(256), 0,
+                     st, L->downT.w,
                      L->downT.scale, L->ffn, L->d, ulist, ucount, W.hh, W.hl, L->b_down, batch, y);
   mark(tr, 7, st);
 }

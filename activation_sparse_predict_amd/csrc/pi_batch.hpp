@@ -446,8 +446,8 @@ k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, con
 }
 
 // ------------------------------------------------------------------ down
-// y[b][c] = sum over union positions j of h[b][j] downT[u_j][c].  Block = one
-// column tile of 32 columns and one of BD_SPLIT splits of the union list,
+// y[b][c] = sum over union positions j of h[b][j] downT[u_j][c].  Block = NT
+// column tiles of 32 columns (bd_tiles) and one of BD_SPLIT splits of the union list,
 // whose partial sums go to y_part[split][b][c] (b < batch; the consumer adds
 // the splits in order, b_down rides on split 0).  A split's share of the
 // list is taken in chunks of BD_CH positions.  The weights of a chunk are
@@ -461,6 +461,9 @@ constexpr int BD_PAD = BD_CH + 8;        // padded position stride (halves) of a
 constexpr int BD_SPLIT = 8;              // splits of the union list (partial y vectors)
 constexpr int BD_MAXF = 65536;           // largest ffn of the batched path: a split's list fits in LDS
 constexpr int BD_ROWS = BD_MAXF / BD_SPLIT;
+// 32-column tiles per block: two for fp16 (a whole 128-byte line of every row
+// per block, and half the blocks re-reading the split's h), one otherwise
+template <int WT> constexpr int bd_tiles() { return WT == DT_F16 ? 2 : 1; }
 
 template <int WT>
 __global__ void __launch_bounds__(256)
@@ -469,33 +472,35 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
         const _Float16* __restrict__ hl_in, const float* __restrict__ b_down, int batch,
         float* __restrict__ y_part) {
   constexpr int NW = (WT == DT_F16) ? 1 : 2;      // weight tiles: hi (and lo for fp32 and Q4_0)
+  constexpr int NT = bd_tiles<WT>();               // 32-column tiles of this block
   // The weight tiles [NW][column][position] and, after the last chunk, the
-  // waves' partial sums [4][BM * BM] share one buffer: 16 KB less LDS per
-  // block, so two blocks fit on a CU with fp32/Q4_0 weights, three with fp16.
-  constexpr size_t WT_BYTES = sizeof(_Float16) * NW * BM * BD_PAD, RED_BYTES = sizeof(float) * 4 * BM * BM;
+  // waves' partial sums [4][NT][BM * BM] share one buffer, so two blocks fit
+  // on a CU.
+  constexpr size_t WT_BYTES = sizeof(_Float16) * NW * NT * BM * BD_PAD, RED_BYTES = sizeof(float) * 4 * NT * BM * BM;
   __shared__ __attribute__((aligned(16))) unsigned char bd_smem[WT_BYTES > RED_BYTES ? WT_BYTES : RED_BYTES];
-  auto& wt = *reinterpret_cast<_Float16(*)[NW][BM][BD_PAD]>(bd_smem);
-  auto& red = *reinterpret_cast<float(*)[4][BM * BM]>(bd_smem);
+  auto& wt = *reinterpret_cast<_Float16(*)[NW][NT * BM][BD_PAD]>(bd_smem);
+  auto& red = *reinterpret_cast<float(*)[4][NT][BM * BM]>(bd_smem);
   __shared__ int rows_l[BD_ROWS];                 // this split's share of the union list
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  const int ntile = (d + BM - 1) / BM;
+  const int ntile = (d + NT * BM - 1) / (NT * BM);
   // XCD-aware order for fp16/fp32: the hardware deals block ids to the 8 XCDs
   // round-robin, so logical block L = (id % 8) * (nblk / 8) + id / 8 puts
-  // adjacent column tiles -- which share the 128-byte lines of every row (2
-  // tiles per line for fp16) -- on one XCD and its L2 (MI355X, Falcon-40B
-  // shape at batch 8/32: 3-5% faster).  For Q4_0, whose 8 tiles per line
-  // would all land on one XCD, it measured 16% slower and is not used.
+  // adjacent column tiles on one XCD and its L2.  For Q4_0, whose 8 tiles per
+  // 128-byte line would all land on one XCD, it measured 16% slower and is
+  // not used.
   const int nblk = gridDim.x;
   const bool xcd = WT != DT_Q4 && nblk % 8 == 0;
   const int lb = xcd ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)blockIdx.x / 8 : (int)blockIdx.x;
-  const int c0 = (lb % ntile) * BM, split = lb / ntile;
+  const int c0 = (lb % ntile) * NT * BM, split = lb / ntile;
   const int n = min(max(*ucount, 0), f);
   const int nch_all = (n + BD_CH - 1) / BD_CH, cps = (nch_all + BD_SPLIT - 1) / BD_SPLIT;
   const int ch0 = split * cps;                     // this split's chunks [ch0, ch0 + nch)
   const int nch = max(0, min(nch_all, ch0 + cps) - ch0);
   const int rg = tid / 4, cq = tid % 4;            // staging: positions 4 rg .. 4 rg + 3, columns 8 cq ..
   const int row_a = lane % 32, kh = 8 * (lane / 32);
-  f16v acc = {};
+  f16v acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f16v{};
   // the split's list entries, so that no weight load waits for a list load
   {
     const int p0 = ch0 * BD_CH, np_ = min(n, (ch0 + nch) * BD_CH) - p0;
@@ -504,7 +509,7 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
   }
 
   struct Stage {
-    uint4 wv[4], wv2[4];     // four rows' 16-byte pieces (fp32: two each)
+    uint4 wv[NT][4], wv2[4]; // four rows' 16-byte pieces per tile (fp32: two each)
     float scale[4];
     h8v ah[4], al[4];        // this wave's four K steps of h (hi, lo)
   };
@@ -516,13 +521,16 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
       const int row = rows_l[e - ch0 * BD_CH];
       st.scale[q] = 1.f;
       if constexpr (WT == DT_F16) {
-        st.wv[q] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(downT) + (size_t)row * d + c0 + 8 * cq);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          st.wv[nt][q] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(downT) + (size_t)row * d + c0 +
+                                                         BM * nt + 8 * cq);
       } else if constexpr (WT == DT_F32) {
         const float* fp = static_cast<const float*>(downT) + (size_t)row * d + c0 + 8 * cq;
-        st.wv[q] = *reinterpret_cast<const uint4*>(fp);
+        st.wv[0][q] = *reinterpret_cast<const uint4*>(fp);
         st.wv2[q] = *reinterpret_cast<const uint4*>(fp + 4);
       } else {
-        st.wv[q] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(downT) + (size_t)row * (d / 2) + c0 / 2);
+        st.wv[0][q] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(downT) + (size_t)row * (d / 2) + c0 / 2);
         st.scale[q] = (float)__builtin_bit_cast(_Float16, down_sc[(size_t)row * (d / 32) + c0 / 32]);
       }
     }
@@ -551,36 +559,41 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
   };
   auto stage_lds = [&](const Stage& st, int c) __attribute__((always_inline)) {
     const int base = (ch0 + c) * BD_CH;
-    float v[4][8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool ok = base + 4 * rg + q < n;
-      if constexpr (WT == DT_F16) {
-        const h8v hv = as_h8(st.wv[q]);
+    for (int nt = 0; nt < NT; ++nt) {
+      float v[4][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[q][e] = ok ? (float)hv[e] : 0.f;
-      } else if constexpr (WT == DT_F32) {
-        const float a[8] = {__uint_as_float(st.wv[q].x), __uint_as_float(st.wv[q].y), __uint_as_float(st.wv[q].z),
-                            __uint_as_float(st.wv[q].w), __uint_as_float(st.wv2[q].x), __uint_as_float(st.wv2[q].y),
-                            __uint_as_float(st.wv2[q].z), __uint_as_float(st.wv2[q].w)};
+      for (int q = 0; q < 4; ++q) {
+        const bool ok = base + 4 * rg + q < n;
+        if constexpr (WT == DT_F16) {
+          const h8v hv = as_h8(st.wv[nt][q]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[q][e] = ok ? a[e] : 0.f;
-      } else {
-        // columns 8cq..8cq+7 of the 32-weight block: low nibbles of bytes 0..15 are
-        // weights 0..15, high nibbles weights 16..31
-        const h8v qv = q4_h8(st.wv[q], 8 * (cq & 1), cq >= 2);
+          for (int e = 0; e < 8; ++e) v[q][e] = ok ? (float)hv[e] : 0.f;
+        } else if constexpr (WT == DT_F32) {
+          const float a[8] = {__uint_as_float(st.wv[0][q].x), __uint_as_float(st.wv[0][q].y),
+                              __uint_as_float(st.wv[0][q].z), __uint_as_float(st.wv[0][q].w),
+                              __uint_as_float(st.wv2[q].x), __uint_as_float(st.wv2[q].y),
+                              __uint_as_float(st.wv2[q].z), __uint_as_float(st.wv2[q].w)};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[q][e] = ok ? st.scale[q] * (float)qv[e] : 0.f;
+          for (int e = 0; e < 8; ++e) v[q][e] = ok ? a[e] : 0.f;
+        } else {
+          // columns 8cq..8cq+7 of the 32-weight block: low nibbles of bytes 0..15 are
+          // weights 0..15, high nibbles weights 16..31
+          const h8v qv = q4_h8(st.wv[0][q], 8 * (cq & 1), cq >= 2);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[q][e] = ok ? st.scale[q] * (float)qv[e] : 0.f;
+        }
       }
-    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      _Float16 hi[4], lo[4];
+      for (int e = 0; e < 8; ++e) {
+        _Float16 hi[4], lo[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) split_f16(v[q][e], &hi[q], &lo[q]);
-      typedef _Float16 h4v __attribute__((ext_vector_type(4)));
-      *reinterpret_cast<h4v*>(&wt[0][8 * cq + e][4 * rg]) = h4v{hi[0], hi[1], hi[2], hi[3]};
-      if constexpr (NW == 2) *reinterpret_cast<h4v*>(&wt[1][8 * cq + e][4 * rg]) = h4v{lo[0], lo[1], lo[2], lo[3]};
+        for (int q = 0; q < 4; ++q) split_f16(v[q][e], &hi[q], &lo[q]);
+        typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<h4v*>(&wt[0][BM * nt + 8 * cq + e][4 * rg]) = h4v{hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (NW == 2)
+          *reinterpret_cast<h4v*>(&wt[1][BM * nt + 8 * cq + e][4 * rg]) = h4v{lo[0], lo[1], lo[2], lo[3]};
+      }
     }
   };
 
@@ -595,12 +608,15 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
     for (int s4 = 0; s4 < 4; ++s4) {
       const int kb = 16 * (4 * w + s4) + kh;
       if (base + 16 * (4 * w + s4) < n) {         // wave-uniform: a step wholly past the end is skipped
-        const h8v bw = *reinterpret_cast<const h8v*>(&wt[0][row_a][kb]);
-        acc = mfma(cur.ah[s4], bw, acc);
-        acc = mfma(cur.al[s4], bw, acc);
-        if constexpr (NW == 2) {
-          const h8v bl = *reinterpret_cast<const h8v*>(&wt[1][row_a][kb]);
-          acc = mfma(cur.ah[s4], bl, acc);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const h8v bw = *reinterpret_cast<const h8v*>(&wt[0][BM * nt + row_a][kb]);
+          acc[nt] = mfma(cur.ah[s4], bw, acc[nt]);
+          acc[nt] = mfma(cur.al[s4], bw, acc[nt]);
+          if constexpr (NW == 2) {
+            const h8v bl = *reinterpret_cast<const h8v*>(&wt[1][BM * nt + row_a][kb]);
+            acc[nt] = mfma(cur.ah[s4], bl, acc[nt]);
+          }
         }
       }
     }
@@ -614,14 +630,17 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
   }
   const int col = lane % 32, half = lane / 32;
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[w][(8 * g + 4 * half + v) * BM + col] = acc[4 * g + v];
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[w][nt][(8 * g + 4 * half + v) * BM + col] = acc[nt][4 * g + v];
   __syncthreads();
-  for (int e = tid; e < BM * BM; e += blockDim.x) {
-    const int b = e / BM, c = e % BM, cg = c0 + c;
+  for (int e2 = tid; e2 < NT * BM * BM; e2 += blockDim.x) {
+    const int nt = e2 / (BM * BM), e = e2 % (BM * BM);
+    const int b = e / BM, c = e % BM, cg = c0 + BM * nt + c;
     if (b >= batch || cg >= d) continue;
-    float v = red[0][e] + red[1][e] + red[2][e] + red[3][e];
+    float v = red[0][nt][e] + red[1][nt][e] + red[2][nt][e] + red[3][nt][e];
     if (b_down && split == 0) v += b_down[cg];
     y_part[((size_t)split * BM + b) * d + cg] = v;
   }
