@@ -163,7 +163,7 @@ def counter_traffic(kernel, workload, batch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); "
+        print(f"bench.py: the benchmark runs on exactly one GPU (asked for {args.gpus}); "
               "the sparse FFN is not sharded across GPUs here.", file=sys.stderr)
         sys.exit(2)
     B = args.batch

@@ -57,7 +57,7 @@ extern "C" {
 typedef enum {
   PI_OK = 0,
   PI_EINVAL = 1,        /* bad argument (NULL, size, alignment, dtype/act combination) */
-  PI_EUNSUPPORTED = 2,  /* valid request this build does not implement */
+  PI_EUNSUPPORTED = 2,  /* valid request the library does not implement */
   PI_EWORKSPACE = 3,    /* ws NULL or ws_bytes < pi_workspace_bytes(...) */
   PI_EHIP = 4           /* a kernel launch failed */
 } pi_status;
