@@ -18,7 +18,7 @@ What it computes (per layer, per sequence b, x_b in R^d):
       unite.ai article, "Online-Phase" and "Adaptive Sparsity-Prädiktoren";
       机器之心 article, Fig. 8 paragraph).  Reading taken: the hidden layer is
       the identity (a rank-r GEMV pair); the output bias c_i is the layer's
-      ``pbias`` when given, else the up/gate bias b_i.
+      ``pbias`` when given, else the up/gate bias b_i (``predictor_bias``).
   threshold   m_i = (float32(s_i) > 0), strict; NaN is inactive   (``threshold``)
       The pages give no threshold; 0 is the centre of the reported
       ambiguity band.  The decision is taken on the score rounded to float32,
@@ -212,6 +212,19 @@ def _get(layer, name):
     return layer.get(name) if isinstance(layer, dict) else getattr(layer, name, None)
 
 
+def predictor_bias(layer):
+    """The predictor's output bias c: the layer's ``pbias`` when it has one,
+    else the up/gate bias b (the predictor "plus bias b_i" of the workloads
+    whose rows have unit norm)."""
+    pbias = _get(layer, "pbias")
+    return _get(layer, "bias") if pbias is None else pbias
+
+
+def ffn_bias(layer):
+    """The bias of the gate (ReGLU) or up (ReLU, Squared ReLU) projection, b."""
+    return _get(layer, "bias")
+
+
 def layer_forward(layer, X, act: str | None = None) -> dict:
     """One layer for a batch of sequences X [nb][d].
 
@@ -220,13 +233,11 @@ def layer_forward(layer, X, act: str | None = None) -> dict:
     """
     act = act or _get(layer, "act") or _get(_get(layer, "cfg"), "act")
     X = np.atleast_2d(np.asarray(X, dtype=np.float64))
-    pbias = _get(layer, "pbias")
-    S = predictor_scores(_get(layer, "A"), _get(layer, "B"),
-                         _get(layer, "bias") if pbias is None else pbias, X)
+    S = predictor_scores(_get(layer, "A"), _get(layer, "B"), predictor_bias(layer), X)
     M = threshold(S)
     idx = active_list(union_mask(M))
     Y = sparse_ffn(act, _get(layer, "gate"), _get(layer, "up"), _get(layer, "downT"),
-                   _get(layer, "bias"), X, M, _get(layer, "b_down"))
+                   ffn_bias(layer), X, M, _get(layer, "b_down"))
     return {"x_in": X, "scores": S, "masks": M, "idx": idx, "count": int(idx.size), "y": Y}
 
 

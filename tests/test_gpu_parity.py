@@ -200,7 +200,7 @@ def test_predictor_degenerate_cases():
     z.B = np.zeros_like(lw.B)
     x = workload.make_x(cfg, 3)
     for sign, expect in ((-1.0, 0), (1.0, cfg.ffn)):
-        z.pbias = (sign * (np.abs(lw.pbias) + 0.5)).astype(np.float32)
+        z.pbias = (sign * (np.abs(lw.bias) + 0.5)).astype(np.float32)
         L = pi.DeviceLayer.upload(z, DEV)
         scores, mask, idx, count = run_predict(L, x[0])
         assert count == expect

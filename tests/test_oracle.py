@@ -23,12 +23,19 @@ class Q4:
         self.nibbles, self.scales = nibbles, scales
 
 
-def tiny_layer(rng, d, f, r, act="relu", scale=1.0):
-    """Small float64-exact layer (values are dyadic rationals, exact in float32)."""
+def tiny_layer(rng, d, f, r, act="relu", scale=1.0, pbias=False):
+    """Small float64-exact layer (values are dyadic rationals, exact in float32).
+
+    With pbias, the predictor gets an output bias of its own, drawn apart from
+    the up/gate bias (and of the opposite sign wherever they would coincide)."""
     def m(*shape):
         return (rng.integers(-64, 65, size=shape) / 32.0 * scale).astype(np.float32)
     L = dict(act=act, A=m(r, d), B=m(f, r), bias=m(f), up=m(f, d), downT=m(f, d),
              gate=m(f, d) if act == "reglu" else None, b_down=None)
+    if pbias:
+        c = m(f)
+        c[c == L["bias"]] = -L["bias"][c == L["bias"]] + np.float32(0.5)
+        L["pbias"] = c
     return L
 
 
@@ -36,11 +43,13 @@ def tiny_layer(rng, d, f, r, act="relu", scale=1.0):
 def frac_layer(L, x):
     """The layer in exact rational arithmetic, following the definitions step by step."""
     A, B, bias = L["A"], L["B"], L["bias"]
+    # the predictor's own output bias c where the layer has one, else b
+    c = L.get("pbias") if L.get("pbias") is not None else bias
     d = A.shape[1]
     r, f = A.shape[0], B.shape[0]
     X = [Fraction(float(v)) for v in x]
     t = [sum(Fraction(float(A[j, k])) * X[k] for k in range(d)) for j in range(r)]
-    s = [Fraction(float(bias[i])) + sum(Fraction(float(B[i, j])) * t[j] for j in range(r))
+    s = [Fraction(float(c[i])) + sum(Fraction(float(B[i, j])) * t[j] for j in range(r))
          for i in range(f)]
     m = [v > 0 for v in s]
     y = [Fraction(0)] * d
@@ -61,12 +70,13 @@ def frac_layer(L, x):
     return s, m, y
 
 
+@pytest.mark.parametrize("pbias", [False, True], ids=["shared_bias", "own_pbias"])
 @pytest.mark.parametrize("act", ["relu", "reglu", "relu2"])
 @pytest.mark.parametrize("seed", [0, 1, 2])
-def test_layer_matches_exact_rationals(act, seed):
+def test_layer_matches_exact_rationals(act, seed, pbias):
     rng = np.random.default_rng(seed)
     d, f, r = 12, 10, 5                   # all different, so a transposed operand cannot pass
-    L = tiny_layer(rng, d, f, r, act)
+    L = tiny_layer(rng, d, f, r, act, pbias=pbias)
     x = (rng.integers(-64, 65, size=d) / 16.0).astype(np.float32)
     s_ex, m_ex, y_ex = frac_layer(L, x)
     out = oracle.layer_forward(L, x[None, :])
@@ -319,6 +329,13 @@ def _mutants():
     def relu2_not_squared(act, zg, zu):
         return np.maximum(zg, 0.0) if act in ("relu", "relu2") else np.maximum(zg, 0.0) * zu
 
+    def pbias_ignored(layer):
+        return oracle._get(layer, "bias")
+
+    def pbias_in_the_ffn(layer):
+        pb = oracle._get(layer, "pbias")
+        return oracle._get(layer, "bias") if pb is None else pb
+
     def glue_no_residual(X, Y, eps=1e-6):
         V = np.atleast_2d(np.asarray(Y, dtype=np.float64))
         return V / np.sqrt((V * V).mean(axis=1, keepdims=True) + eps)
@@ -326,15 +343,18 @@ def _mutants():
     return [("predictor_scores", no_bias), ("predictor_scores", transposed_A),
             ("threshold", nonstrict_threshold), ("threshold", wrong_sign_threshold),
             ("active_list", off_by_one_list), ("_act", relu_on_up), ("_act", relu2_not_squared),
-            ("rms_glue", glue_no_residual)]
+            ("rms_glue", glue_no_residual), ("predictor_bias", pbias_ignored),
+            ("ffn_bias", pbias_in_the_ffn)]
 
 
 @pytest.mark.parametrize("name,fn", _mutants(), ids=lambda v: getattr(v, "__name__", str(v)))
 def test_planted_mistake_is_caught(monkeypatch, gen, name, fn):
     monkeypatch.setattr(oracle, name, fn)
-    pins = [lambda: test_layer_matches_exact_rationals("relu", 0),
-            lambda: test_layer_matches_exact_rationals("reglu", 1),
-            lambda: test_layer_matches_exact_rationals("relu2", 2),
+    pins = [lambda: test_layer_matches_exact_rationals("relu", 0, False),
+            lambda: test_layer_matches_exact_rationals("reglu", 1, False),
+            lambda: test_layer_matches_exact_rationals("relu2", 2, False),
+            lambda: test_layer_matches_exact_rationals("relu", 0, True),
+            lambda: test_layer_matches_exact_rationals("reglu", 1, True),
             test_predictor_zero_weights_gives_bias,
             test_threshold_is_strict_and_nan_inactive,
             test_active_list_matches_library,

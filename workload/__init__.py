@@ -23,10 +23,16 @@ Layouts (row-major, storage order = hot-first unless ``order="identity"``):
   bias   [ffn]         float32; gate bias (ReGLU) or up bias (ReLU):
                        PhiInv(p_i) * ||stored row_i||, so w_i.x + b_i > 0 with
                        probability p_i for x ~ N(0, I)
-  pbias  [ffn]         float32; the predictor's output bias PhiInv(p_i): its
-                       output B_i.(A x) has unit variance for x ~ N(0, I)
-                       (A ~ N(0, 1/d), B ~ N(0, 1/r)), so it also marks neuron
-                       i with probability ~p_i
+  pbias  [ffn]         float32 or None; the predictor's own output bias.
+                       None (the predictor adds the up/gate bias b_i) for
+                       fp32/fp16 weights, whose rows have norm ~1, so that
+                       b_i ~ PhiInv(p_i).  Q4_0 rows have norm ~37 (scale
+                       8|N(0, 1/d)| times q - 8 with q uniform), so b_i would
+                       mark only ~3% of the neurons instead of the configured
+                       8%; there pbias = PhiInv(p_i): the predictor output
+                       B_i.(A x) has unit variance for x ~ N(0, I)
+                       (A ~ N(0, 1/d), B ~ N(0, 1/r)), so c_i marks neuron i
+                       with probability ~p_i
   gate   [ffn][d]      ReGLU only                  (w_dtype)
   up     [ffn][d]                                  (w_dtype)
   downT  [ffn][d]      row i = column i of W_down  (w_dtype)
@@ -297,7 +303,9 @@ def make_layer(cfg: FFNConfig, layer: int, order: str = "hot_first", nthreads: i
     norms = row_norms(gate if cfg.act == "reglu" else up, nthreads)
     z = ndtri(p[perm])
     bias = (z * norms).astype(np.float32)
-    pbias = z.astype(np.float32)
+    # the predictor adds b_i where it is on the predictor's scale (rows of norm
+    # ~1), and its own PhiInv(p_i) where it is not (Q4_0 rows, norm ~37)
+    pbias = z.astype(np.float32) if cfg.w_dtype == "q4_0" else None
     return LayerWeights(cfg, layer, p, perm, A, B, bias, up, downT, gate, None, pbias)
 
 
