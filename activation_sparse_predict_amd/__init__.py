@@ -48,7 +48,7 @@ class PiLayer(ctypes.Structure):
 
 class PiTrace(ctypes.Structure):
     _fields_ = [("x_in", ctypes.c_void_p), ("scores", ctypes.c_void_p), ("mask", ctypes.c_void_p),
-                ("idx", ctypes.c_void_p), ("count", ctypes.c_void_p),
+                ("idx", ctypes.c_void_p), ("count", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32)]
 
 
@@ -223,7 +223,7 @@ def make_trace(n_layers: int, recs: Sequence[dict]):
         else:
             ev_arg, n_ev = None, 0
         arr[i] = PiTrace(_p(r.get("x_in")), _p(r.get("scores")), _p(r.get("mask")),
-                         _p(r.get("idx")), _p(r.get("count")), ev_arg, n_ev)
+                         _p(r.get("idx")), _p(r.get("count")), _p(r.get("y")), ev_arg, n_ev)
     arr._keep = keep
     return arr
 

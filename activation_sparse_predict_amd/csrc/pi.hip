@@ -653,6 +653,9 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
         hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, tr->idx ? tr->idx : W.ulist,
                            tr->count ? tr->count : W.misc + 1, nullptr, nullptr);
       b_ffn(L, batch, W, W.ulist, W.misc, W.y[cur], st, tr);
+      if (tr && tr->y)   // the layer's y for the record: its partial vectors added in order
+        hipLaunchKernelGGL(pib::k_bsum_y, dim3(cdiv(batch * L->d, 256)), dim3(256), 0, st, W.y[cur], batch, L->d,
+                           tr->y);
     }
     const int last = (n_layers - 1) & 1;
     hipLaunchKernelGGL(pib::k_bglue_out, dim3(batch), dim3(256), sizeof(float) * D.d, st, W.x[last], W.y[last],
@@ -683,6 +686,8 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
     np_prev = k3<false>(L, K3Args{W.mask, W.h, nullptr, nullptr, nullptr, W.y[cur], W.cnt, k2_blocks(L), c1, c2,
                                   nz_counts ? nz_counts + l : nullptr}, st);
     mark(tr, 3, st);
+    if (tr && tr->y)     // the layer's y for the record: its partial vectors added in the glue's order
+      hipLaunchKernelGGL(k_finalize, dim3(cdiv(L->d, 256)), dim3(256), 0, st, W.y[cur], np_prev, tr->y, L->d);
   }
   {
     const int last = (n_layers - 1) & 1;

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define PI_ABI_VERSION 3
+#define PI_ABI_VERSION 4
 
 typedef enum {
   PI_OK = 0,
@@ -106,13 +106,14 @@ typedef struct {
   uint8_t* mask;    /* [batch][ffn] 1 if score > 0; 16-byte aligned (PI_EINVAL) */
   int32_t* idx;     /* [ffn]        ascending storage ids of the union mask */
   int32_t* count;   /* [1]          number of entries in idx */
+  float* y;         /* [batch][d]   the layer's FFN output y_l (before the glue) */
   /* Timing: hipEvent_t handles (as void*) recorded on the stream, events[0]
    * before the layer's first kernel and events[i] after its i-th kernel, for
    * i < n_events.  Kernels of a layer, in order -- batch 1: predictor GEMV 1
    * with the glue, scores with the fused up/gate gather, down projection;
    * batch > 1: glue, predictor GEMM 1, its split sum, scores and union, union
    * compaction, up/gate GEMM, down GEMM.  Record-only kernels of the trace
-   * (list compaction) are not counted. */
+   * (list compaction, the sum of y's partial vectors) are not counted. */
   void** events;
   int32_t n_events;
 } pi_trace;

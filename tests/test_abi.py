@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(pi):
 
 
 def test_abi_version_and_status_strings(pi):
-    assert pi.abi_version() == 3
+    assert pi.abi_version() == 4
     assert pi.status_str(0) == "ok"
     assert "workspace" in pi.status_str(3)
 

@@ -3,8 +3,9 @@
 Per sequence: scores within the threshold band, masks bit-exact outside it,
 the union list equal to the ascending list of the GPU's own union, and each
 sequence's FFN output equal to its own single-sequence result (the oracle's
-batch semantics).  The FFN is checked layer by layer on the oracle's masks,
-so that a band neuron decided differently cannot leak into the comparison.
+batch semantics).  Single layers are checked on the oracle's masks; stacks by
+layer-local replay on the GPU's own inputs and masks, so that a band neuron
+decided differently cannot leak into the comparison.
 """
 import sys
 
@@ -13,7 +14,7 @@ import pytest
 
 import oracle
 import workload
-from parity import BAND, TOL, check_list, check_scores_masks, check_y, rel_err
+from parity import BAND, TOL, check_list, check_scores_masks, check_y, rel_err, replay_stack
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -119,8 +120,25 @@ def test_batch_edge_cases():
         check_y(Y[b], ref[b], TOL[cfg.w_dtype])
 
 
+def traced_records(n, nb, d, f):
+    return [dict(x_in=torch.empty(nb, d, device=DEV), scores=torch.empty(nb, f, device=DEV),
+                 mask=torch.empty(nb, f, dtype=torch.uint8, device=DEV),
+                 idx=torch.empty(f, dtype=torch.int32, device=DEV),
+                 count=torch.empty(1, dtype=torch.int32, device=DEV),
+                 y=torch.full((nb, d), float("nan"), device=DEV)) for _ in range(n)]
+
+
+def to_host(recs):
+    out = []
+    for r in recs:
+        h = {k: v.cpu().numpy() for k, v in r.items()}
+        h["count"] = int(h["count"][0])
+        out.append(h)
+    return out
+
+
 def test_batch_stack_deterministic_and_traced():
-    cfg = SMALL["f16-reglu"]
+    cfg = SMALL["f16-reglu"].with_(n_layers=3)
     nb = 8
     say(f"[batch_stack] {cfg.n_layers} layers, batch {nb}, traced")
     host = [workload.make_layer(cfg, l) for l in range(cfg.n_layers)]
@@ -130,72 +148,44 @@ def test_batch_stack_deterministic_and_traced():
     stack = pi.Stack(layers, batch=nb)
     outs = []
     for rep in range(2):
-        recs = [dict(x_in=torch.empty(nb, d, device=DEV), scores=torch.empty(nb, f, device=DEV),
-                     mask=torch.empty(nb, f, dtype=torch.uint8, device=DEV),
-                     idx=torch.empty(f, dtype=torch.int32, device=DEV),
-                     count=torch.empty(1, dtype=torch.int32, device=DEV)) for _ in range(n)]
+        recs = traced_records(n, nb, d, f)
         out = torch.empty(nb, d, device=DEV)
         counts = torch.zeros(n, dtype=torch.int32, device=DEV)
         stack(dev(X), out, counts, pi.make_trace(n, recs))
         torch.cuda.synchronize()
-        outs.append((out.cpu(), counts.cpu(), [{k: v.cpu().numpy() for k, v in r.items()} for r in recs]))
+        outs.append((out.cpu(), counts.cpu(), to_host(recs)))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
     out, counts, recs = outs[0][0].numpy(), outs[0][1].numpy(), outs[0][2]
-    # layer-local replay: the oracle takes the GPU's layer input and masks
-    for l, (h, r) in enumerate(zip(host, recs)):
-        ref = oracle.layer_forward(h, r["x_in"])
-        for b in range(nb):
-            check_scores_masks(ref["scores"][b], r["scores"][b], r["mask"][b])
-        union = r["mask"].astype(bool).any(axis=0)
-        check_list(union, r["idx"], int(r["count"][0]))
-        assert int(counts[l]) == int(r["count"][0])
-        y_ref = oracle.sparse_ffn(cfg.act, h.gate, h.up, h.downT, h.bias, r["x_in"], r["mask"].astype(bool))
-        x_next = oracle.rms_glue(r["x_in"], y_ref)
-        target = recs[l + 1]["x_in"] if l + 1 < n else out
-        for b in range(nb):
-            check_y(target[b], x_next[b], max(TOL[cfg.w_dtype], 1e-5))
+    assert [r["count"] for r in recs] == counts.tolist()
+    st = replay_stack(host, recs, out, X, cfg.w_dtype, cfg.act)
+    say(f"  {st}")
 
 
-FULL = [(3, 8, 1), (3, 32, 1), (4, 32, 1)]
+# (workload, batch, layers, sequences replayed: None = all)
+FULL = [(3, 8, 2, None), (3, 32, 2, None), (4, 32, 2, [0, 1, 16, 31])]
 
 
-@pytest.mark.parametrize("ci,nb,n_layers", FULL, ids=lambda v: str(v))
-def test_batch_full_size(ci, nb, n_layers):
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("ci,nb,n_layers,seqs", FULL, ids=lambda v: str(v))
+def test_batch_full_size(ci, nb, n_layers, seqs):
     """Real layer shapes of the batched workloads, through the stack, layer-locally replayed."""
     cfg = workload.CONFIGS[ci]
-    say(f"[batch_full] config {ci} {cfg.name}: batch {nb}, {n_layers} layer(s)")
-    host = [workload.make_layer(cfg, l) for l in range(n_layers)]
+    say(f"[batch_full] config {ci} {cfg.name}: batch {nb}, {n_layers} layers, "
+        f"sequences replayed: {'all' if seqs is None else seqs}")
+    host = [workload.make_layer(cfg, l, nthreads=16) for l in range(n_layers)]
     layers = [pi.DeviceLayer.upload(h, DEV) for h in host]
     X = workload.make_x(cfg, 0, seqs=nb)
     d, f = cfg.d, cfg.ffn
-    recs = [dict(x_in=torch.empty(nb, d, device=DEV), scores=torch.empty(nb, f, device=DEV),
-                 mask=torch.empty(nb, f, dtype=torch.uint8, device=DEV),
-                 idx=torch.empty(f, dtype=torch.int32, device=DEV),
-                 count=torch.empty(1, dtype=torch.int32, device=DEV)) for _ in range(n_layers)]
+    recs = traced_records(n_layers, nb, d, f)
     out = torch.empty(nb, d, device=DEV)
     pi.ffn_stack(layers, dev(X), out, trace=pi.make_trace(n_layers, recs), batch=nb)
     torch.cuda.synchronize()
     out = out.cpu().numpy()
-    recs = [{k: v.cpu().numpy() for k, v in r.items()} for r in recs]
-    # sample 4 sequences for the float64 replay (the oracle is slow at these sizes)
-    sample = sorted({0, 1, nb // 2, nb - 1})
-    for l, (h, r) in enumerate(zip(host, recs)):
-        ref = oracle.layer_forward(h, r["x_in"][sample])
-        flips = 0
-        for j, b in enumerate(sample):
-            flips += check_scores_masks(ref["scores"][j], r["scores"][b], r["mask"][b])["band_flips"]
-        union = r["mask"].astype(bool).any(axis=0)
-        check_list(union, r["idx"], int(r["count"][0]))
-        M = r["mask"][sample].astype(bool)
-        y_ref = oracle.sparse_ffn(cfg.act, h.gate, h.up, h.downT, h.bias, r["x_in"][sample], M)
-        x_next = oracle.rms_glue(r["x_in"][sample], y_ref)
-        worst = 0.0
-        for j, b in enumerate(sample):
-            worst = max(worst, check_y(out[b], x_next[j], max(TOL[cfg.w_dtype], 1e-5)))
-        say(f"  layer {l}: union {int(r['count'][0])} ({r['count'][0] / f:.3f}), band flips {flips}, "
-            f"worst out err {worst:.2e}")
+    recs = to_host(recs)
     del layers
     torch.cuda.empty_cache()
+    st = replay_stack(host, recs, out, X, cfg.w_dtype, cfg.act, seqs=seqs, end_to_end=False)
+    say(f"  unions {[r['count'] for r in recs]} of {f}; {st}")
 
 
 # ------------------------------------------------------------- maximum sizes
