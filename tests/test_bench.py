@@ -55,3 +55,51 @@ def test_more_than_one_gpu_is_refused():
                        text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def _write_csv(path, header, rows):
+    import csv
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_summarize_trace(tmp_path):
+    hdr = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Workgroup_Size_X",
+           "Arch_VGPR_Count", "Accum_VGPR_Count", "Group_Segment_Size", "Private_Segment_Size"]
+    rows = [["void pik::k_score<1, 2>(int)", 1000, 3000, 131072, 256, 124, 0, 33072, 0],
+            ["void pik::k_score<1, 2>(int)", 5000, 9000, 131072, 256, 124, 0, 33072, 0],
+            ["pik::k_down(int)", 9000, 10000, 65536, 512, 72, 0, 66624, 0]]
+    p = tmp_path / "kt.csv"
+    _write_csv(p, hdr, rows)
+    out = tmp_path / "s.md"
+    bench.summarize_trace(str(p), "test", ["cmd"], str(out))
+    text = out.read_text()
+    line = [l for l in text.splitlines() if "k_score" in l][0].split("|")
+    assert line[2].strip() == "2" and line[3].strip() == "3.00"            # calls, mean of 2 and 4 us
+    assert line[5].strip() == "2.00" and line[6].strip() == "4.00"        # min, max
+    assert "k_down" in text and "| 1 | 1.00 |" in text
+
+
+def test_summarize_traffic(tmp_path):
+    import json
+    cfg = workload.CONFIGS[1].with_(n_layers=2)
+    counts = [[100, 200], [300, 400]]
+    nz = [[50, 60], [70, 80]]
+    cj = tmp_path / "c.json"
+    cj.write_text(json.dumps({"config": 1, "layers": 2, "batch": 1, "calib_mb": 1024, "counts": counts,
+                              "nz_counts": nz}))
+    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    # the fetch counter reads half of the calibration map's bytes: scale 2
+    _write_csv(tmp_path / "f.csv", hdr, [["elementwise_kernel<neg>", "FETCH_SIZE", 524288]] * 3 +
+               [["void pik::k_down<1, 4, false>(int)", "FETCH_SIZE", 1000.0]] * 6)
+    _write_csv(tmp_path / "w.csv", hdr, [["elementwise_kernel<neg>", "WRITE_SIZE", 1048576]] * 3 +
+               [["void pik::k_down<1, 4, false>(int)", "WRITE_SIZE", 10.0]] * 6)
+    out = tmp_path / "t.md"
+    bench.summarize_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(cj), "k_down", ["c"], str(out))
+    kv = dict(l[2:].split(": ", 1) for l in out.read_text().splitlines() if l.startswith("- "))
+    assert float(kv["traffic_bytes_per_launch"].strip("`")) == pytest.approx((2000 + 10) * 1024)
+    # passes: token 0 (warm-up), then tokens 0 and 1; layers 0 and 1
+    alg = [bench.kernel_bytes(cfg, 1, counts[t][l], nz[t][l])["k_down"] for t in (0, 0, 1) for l in (0, 1)]
+    assert float(kv["alg_bytes_per_launch"].strip("`")) == pytest.approx(sum(alg) / len(alg))
