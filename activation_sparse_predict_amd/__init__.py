@@ -79,6 +79,8 @@ def lib():
         L.pi_sparse_ffn.restype = ctypes.c_int
         L.pi_ffn_stack.argtypes = [P, I32, P, I32, P, P, P, P, P, SZ, P]
         L.pi_ffn_stack.restype = ctypes.c_int
+        L.pi_ffn_stack_static.argtypes = [P, I32, P, I32, P, P, P, P, P]
+        L.pi_ffn_stack_static.restype = ctypes.c_int
         L.pi_last_hip_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -249,6 +251,18 @@ def ffn_stack(layers, x, out, counts=None, trace=None, ws=None, batch: int = 1, 
     Stack(layers, batch, ws)(x, out, counts, trace, stream, nz_counts)
 
 
+STATIC_WORKSPACE_BYTES = 64 << 20   # PI_STATIC_WORKSPACE_BYTES
+
+
+def ffn_stack_static(layers, x, out, counts=None, trace=None, batch: int = 1, stream=None, nz_counts=None):
+    """pi_ffn_stack_static: the stack on the library's own per-GPU scratch array (no workspace)."""
+    arr = _layer_array(list(layers))
+    tr = None if trace is None else ctypes.cast(trace, ctypes.c_void_p)
+    st = lib().pi_ffn_stack_static(ctypes.cast(arr, ctypes.c_void_p), len(arr), _p(x), batch, _p(out),
+                                   _p(counts), _p(nz_counts), tr, _stream(stream))
+    _check(st, "pi_ffn_stack_static")
+
+
 # ------------------------------------------------------- HIP runtime plumbing
 _hip = None
 
@@ -351,5 +365,5 @@ class HipGraph:
                 _hip.hipGraphDestroy(self.g)
 
 
-EXPORTED = ("pi_workspace_bytes", "pi_predict", "pi_sparse_ffn", "pi_ffn_stack", "pi_status_str",
-            "pi_abi_version", "pi_last_hip_error")
+EXPORTED = ("pi_workspace_bytes", "pi_predict", "pi_sparse_ffn", "pi_ffn_stack", "pi_ffn_stack_static",
+            "pi_status_str", "pi_abi_version", "pi_last_hip_error")

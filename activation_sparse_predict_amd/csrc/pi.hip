@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "pi_batch.hpp"
 #include "pi_kernels.hpp"
@@ -536,6 +537,137 @@ pi_status launch_status() {
 
 }  // namespace
 
+namespace {
+
+// Host-only validation of a stack call; on success *WL is its workspace layout.
+pi_status validate_stack(const pi_layer* layers, int32_t n_layers, const float* x, int32_t batch, const float* out,
+                         const pi_trace* trace, WsLayout* WL) {
+  if (!layers || n_layers <= 0) return PI_EINVAL;
+  pi_status s;
+  for (int l = 0; l < n_layers; ++l)
+    if ((s = check_layer(&layers[l])) != PI_OK) return s;
+  if ((s = check_batch(batch)) != PI_OK) return s;
+  for (int l = 0; l < n_layers; ++l)
+    if ((s = check_batched_ffn(&layers[l], batch)) != PI_OK) return s;
+  if (!x || !aligned(x, 16) || !out) return PI_EINVAL;
+  if (trace)
+    for (int l = 0; l < n_layers; ++l)
+      if (trace[l].mask && !aligned(trace[l].mask, 16)) return PI_EINVAL;
+  Dims D;
+  if (!dims_of(layers, n_layers, &D)) return PI_EINVAL;
+  *WL = layout(D, batch);
+  return PI_OK;
+}
+
+// Enqueue a validated stack call on stream st with workspace ws (WL.total bytes).
+pi_status run_stack(const pi_layer* layers, int32_t n_layers, const float* x, int32_t batch, float* out,
+                    int32_t* counts, int32_t* nz_counts, const pi_trace* trace, const WsLayout& WL, void* ws,
+                    hipStream_t st) {
+  Dims D;
+  dims_of(layers, n_layers, &D);
+  Ws W = carve(ws, WL);
+  (void)hipGetLastError();
+  if (batch > 1) {
+    for (int l = 0; l < n_layers; ++l) {
+      const pi_layer* L = &layers[l];
+      const pi_trace* tr = trace ? &trace[l] : nullptr;
+      const int cur = l & 1, prv = cur ^ 1;
+      mark(tr, 0, st);
+      b_glue(l == 0 ? x : W.x[prv], l == 0 ? nullptr : W.y[prv], batch, L->d, W.x[cur], tr ? tr->x_in : nullptr,
+             W, st);
+      mark(tr, 1, st);
+      b_predict(L, batch, W, tr ? tr->scores : nullptr, tr ? tr->mask : nullptr, W.ulist, W.misc,
+                counts ? counts + l : nullptr, nz_counts ? nz_counts + l : nullptr, st, tr);
+      if (tr && (tr->idx || tr->count))   // the union list and count for the record
+        hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, tr->idx ? tr->idx : W.ulist,
+                           tr->count ? tr->count : W.misc + 1, nullptr, nullptr);
+      b_ffn(L, batch, W, W.ulist, W.misc, W.y[cur], st, tr);
+      if (tr && tr->y)   // the layer's y for the record: its partial vectors added in order
+        hipLaunchKernelGGL(pib::k_bsum_y, dim3(cdiv(batch * L->d, 256)), dim3(256), 0, st, W.y[cur], batch, L->d,
+                           tr->y);
+    }
+    const int last = (n_layers - 1) & 1;
+    hipLaunchKernelGGL(pib::k_bglue_out, dim3(batch), dim3(256), sizeof(float) * D.d, st, W.x[last], W.y[last],
+                       pib::BD_SPLIT, D.d, out);
+    return launch_status();
+  }
+  int np_prev = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const pi_layer* L = &layers[l];
+    const pi_trace* tr = trace ? &trace[l] : nullptr;
+    const int cur = l & 1, prv = cur ^ 1;
+    mark(tr, 0, st);
+    const bool q4 = L->w_dtype == PI_Q4_0;
+    k1(L, K1Args{l == 0 ? x : W.x[prv], l == 0 ? nullptr : W.y[prv], np_prev, W.x[cur], q4 ? W.xq : nullptr,
+                 tr ? tr->x_in : nullptr, W.t}, st);
+    mark(tr, 1, st);
+    // W.mask marks the active neurons with h != 0 (the rows the down projection
+    // reads); the predictor's own mask goes to the record, or to W.pmask when
+    // only the record's list asks for it
+    uint8_t* pmask = tr ? (tr->mask ? tr->mask : (tr->idx ? W.pmask : nullptr)) : nullptr;
+    k2(L, true, K2Args{W.t, q4 ? W.xq : W.x[cur], tr ? tr->scores : nullptr, W.mask, pmask, W.cnt, W.h}, st);
+    mark(tr, 2, st);
+    int32_t* c1 = counts ? counts + l : nullptr;
+    int32_t* c2 = (tr && tr->count && !tr->idx) ? tr->count : nullptr;
+    if (tr && tr->idx)   // ascending list of the predictor's mask, for the record
+      hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, pmask, L->ffn, tr->idx,
+                         tr->count ? tr->count : W.misc, nullptr, nullptr);
+    np_prev = k3<false>(L, K3Args{W.mask, W.h, nullptr, nullptr, nullptr, W.y[cur], W.cnt, k2_blocks(L), c1, c2,
+                                  nz_counts ? nz_counts + l : nullptr}, st);
+    mark(tr, 3, st);
+    if (tr && tr->y)     // the layer's y for the record: its partial vectors added in the glue's order
+      hipLaunchKernelGGL(k_finalize, dim3(cdiv(L->d, 256)), dim3(256), 0, st, W.y[cur], np_prev, tr->y, L->d);
+  }
+  {
+    const int last = (n_layers - 1) & 1;
+    hipLaunchKernelGGL(k_glue_out, dim3(1), dim3(256), sizeof(float) * D.d, st, W.x[last], W.y[last], np_prev,
+                       out, D.d);
+  }
+  return launch_status();
+}
+
+}  // namespace
+
+// ------------------------------------------------- workspace without allocation
+// The workspace of pi_ffn_stack_static: one file-scope array, of which every
+// GPU holds its own copy until the process ends.  In host code `scratch` names
+// a host-side stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is ever passed
+// to a kernel.
+static __device__ __align__(256) unsigned char scratch[PI_STATIC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr size_t kStaticWsBytes = size_t(PI_STATIC_WORKSPACE_BYTES);
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on its first use).
+pi_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip = e;
+    return PI_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return PI_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      g_last_hip = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return PI_EHIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PI_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t pi_abi_version(void) { return PI_ABI_VERSION; }
@@ -620,81 +752,25 @@ pi_status pi_sparse_ffn(const pi_layer* layer, const float* x, int32_t batch, co
 pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x, int32_t batch, float* out,
                        int32_t* counts, int32_t* nz_counts, const pi_trace* trace, void* ws, size_t ws_bytes,
                        void* stream) {
-  if (!layers || n_layers <= 0) return PI_EINVAL;
-  pi_status s;
-  for (int l = 0; l < n_layers; ++l)
-    if ((s = check_layer(&layers[l])) != PI_OK) return s;
-  if ((s = check_batch(batch)) != PI_OK) return s;
-  for (int l = 0; l < n_layers; ++l)
-    if ((s = check_batched_ffn(&layers[l], batch)) != PI_OK) return s;
-  if (!x || !aligned(x, 16) || !out) return PI_EINVAL;
-  if (trace)
-    for (int l = 0; l < n_layers; ++l)
-      if (trace[l].mask && !aligned(trace[l].mask, 16)) return PI_EINVAL;
-  Dims D;
-  if (!dims_of(layers, n_layers, &D)) return PI_EINVAL;
-  const WsLayout WL = layout(D, batch);
+  WsLayout WL;
+  const pi_status s = validate_stack(layers, n_layers, x, batch, out, trace, &WL);
+  if (s != PI_OK) return s;
   if (!ws || ws_bytes < WL.total || !aligned(ws, kAlign)) return PI_EWORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  Ws W = carve(ws, WL);
-  (void)hipGetLastError();
-  if (batch > 1) {
-    for (int l = 0; l < n_layers; ++l) {
-      const pi_layer* L = &layers[l];
-      const pi_trace* tr = trace ? &trace[l] : nullptr;
-      const int cur = l & 1, prv = cur ^ 1;
-      mark(tr, 0, st);
-      b_glue(l == 0 ? x : W.x[prv], l == 0 ? nullptr : W.y[prv], batch, L->d, W.x[cur], tr ? tr->x_in : nullptr,
-             W, st);
-      mark(tr, 1, st);
-      b_predict(L, batch, W, tr ? tr->scores : nullptr, tr ? tr->mask : nullptr, W.ulist, W.misc,
-                counts ? counts + l : nullptr, nz_counts ? nz_counts + l : nullptr, st, tr);
-      if (tr && (tr->idx || tr->count))   // the union list and count for the record
-        hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, tr->idx ? tr->idx : W.ulist,
-                           tr->count ? tr->count : W.misc + 1, nullptr, nullptr);
-      b_ffn(L, batch, W, W.ulist, W.misc, W.y[cur], st, tr);
-      if (tr && tr->y)   // the layer's y for the record: its partial vectors added in order
-        hipLaunchKernelGGL(pib::k_bsum_y, dim3(cdiv(batch * L->d, 256)), dim3(256), 0, st, W.y[cur], batch, L->d,
-                           tr->y);
-    }
-    const int last = (n_layers - 1) & 1;
-    hipLaunchKernelGGL(pib::k_bglue_out, dim3(batch), dim3(256), sizeof(float) * D.d, st, W.x[last], W.y[last],
-                       pib::BD_SPLIT, D.d, out);
-    return launch_status();
-  }
-  int np_prev = 0;
-  for (int l = 0; l < n_layers; ++l) {
-    const pi_layer* L = &layers[l];
-    const pi_trace* tr = trace ? &trace[l] : nullptr;
-    const int cur = l & 1, prv = cur ^ 1;
-    mark(tr, 0, st);
-    const bool q4 = L->w_dtype == PI_Q4_0;
-    k1(L, K1Args{l == 0 ? x : W.x[prv], l == 0 ? nullptr : W.y[prv], np_prev, W.x[cur], q4 ? W.xq : nullptr,
-                 tr ? tr->x_in : nullptr, W.t}, st);
-    mark(tr, 1, st);
-    // W.mask marks the active neurons with h != 0 (the rows the down projection
-    // reads); the predictor's own mask goes to the record, or to W.pmask when
-    // only the record's list asks for it
-    uint8_t* pmask = tr ? (tr->mask ? tr->mask : (tr->idx ? W.pmask : nullptr)) : nullptr;
-    k2(L, true, K2Args{W.t, q4 ? W.xq : W.x[cur], tr ? tr->scores : nullptr, W.mask, pmask, W.cnt, W.h}, st);
-    mark(tr, 2, st);
-    int32_t* c1 = counts ? counts + l : nullptr;
-    int32_t* c2 = (tr && tr->count && !tr->idx) ? tr->count : nullptr;
-    if (tr && tr->idx)   // ascending list of the predictor's mask, for the record
-      hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, pmask, L->ffn, tr->idx,
-                         tr->count ? tr->count : W.misc, nullptr, nullptr);
-    np_prev = k3<false>(L, K3Args{W.mask, W.h, nullptr, nullptr, nullptr, W.y[cur], W.cnt, k2_blocks(L), c1, c2,
-                                  nz_counts ? nz_counts + l : nullptr}, st);
-    mark(tr, 3, st);
-    if (tr && tr->y)     // the layer's y for the record: its partial vectors added in the glue's order
-      hipLaunchKernelGGL(k_finalize, dim3(cdiv(L->d, 256)), dim3(256), 0, st, W.y[cur], np_prev, tr->y, L->d);
-  }
-  {
-    const int last = (n_layers - 1) & 1;
-    hipLaunchKernelGGL(k_glue_out, dim3(1), dim3(256), sizeof(float) * D.d, st, W.x[last], W.y[last], np_prev,
-                       out, D.d);
-  }
-  return launch_status();
+  return run_stack(layers, n_layers, x, batch, out, counts, nz_counts, trace, WL, ws,
+                   static_cast<hipStream_t>(stream));
+}
+
+pi_status pi_ffn_stack_static(const pi_layer* layers, int32_t n_layers, const float* x, int32_t batch, float* out,
+                              int32_t* counts, int32_t* nz_counts, const pi_trace* trace, void* stream) {
+  WsLayout WL;
+  const pi_status s = validate_stack(layers, n_layers, x, batch, out, trace, &WL);
+  if (s != PI_OK) return s;
+  if (WL.total > kStaticWsBytes) return PI_EWORKSPACE;   // checked before any HIP call
+  void* ws = nullptr;
+  const pi_status sp = scratch_of_current_device(&ws);
+  if (sp != PI_OK) return sp;
+  return run_stack(layers, n_layers, x, batch, out, counts, nz_counts, trace, WL, ws,
+                   static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

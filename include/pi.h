@@ -174,6 +174,27 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
                        float* out, int32_t* counts, int32_t* nz_counts, const pi_trace* trace,
                        void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * pi_ffn_stack_static -- pi_ffn_stack without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  It computes exactly what
+ * pi_ffn_stack computes, with the same kernels, and calls no allocating
+ * routine: its workspace is a file-scope device array of
+ * PI_STATIC_WORKSPACE_BYTES that every GPU the library runs on holds until the
+ * process ends (its device address is looked up once per device, on the
+ * first call with that device current).
+ * Returns PI_EWORKSPACE, before any HIP call, when
+ * pi_workspace_bytes(layers, n_layers, batch) exceeds PI_STATIC_WORKSPACE_BYTES
+ * (64 MiB covers every batch 1..32 at the largest accepted width, rank and
+ * batched ffn).  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and give undefined
+ * results; calls ordered on one stream are independent.
+ */
+#define PI_STATIC_WORKSPACE_BYTES (64u << 20)
+pi_status pi_ffn_stack_static(const pi_layer* layers, int32_t n_layers, const float* x, int32_t batch,
+                              float* out, int32_t* counts, int32_t* nz_counts, const pi_trace* trace,
+                              void* stream);
+
 const char* pi_status_str(pi_status s);
 int32_t pi_abi_version(void);
 /* Name of the HIP error behind the calling thread's most recent PI_EHIP

@@ -176,3 +176,26 @@ def test_struct_layouts_match_the_header(pi, tmp_path):
         assert int(out[st]) == ctypes.sizeof(cls), st
         for f in fields[st]:
             assert int(out[f"{st}.{f}"]) == getattr(cls, f).offset, f"{st}.{f}"
+
+
+def test_static_stack_checks_come_before_any_hip_call(pi):
+    """pi_ffn_stack_static refuses bad arguments and a workspace beyond its fixed array
+    on the host, so these calls return without touching a GPU."""
+    lib = pi.lib()
+    L = make_layer(pi)
+    one = (pi.PiLayer * 1)(L)
+    assert lib.pi_ffn_stack_static(ctypes.cast(one, ctypes.c_void_p), 1, None, 1, FAKE, None, None, None,
+                                   None) == 1
+    assert lib.pi_ffn_stack_static(ctypes.cast(one, ctypes.c_void_p), 1, FAKE, 33, FAKE, None, None, None,
+                                   None) == 1
+    big = make_layer(pi, ffn=16 << 20)           # ~7 bytes of workspace per neuron: > 64 MiB
+    assert ws_bytes(pi, big) > pi.STATIC_WORKSPACE_BYTES
+    arr = (pi.PiLayer * 1)(big)
+    assert lib.pi_ffn_stack_static(ctypes.cast(arr, ctypes.c_void_p), 1, FAKE, 1, FAKE, None, None, None,
+                                   None) == 3
+
+
+def test_static_workspace_size_matches_the_header(pi):
+    with open(os.path.join(ROOT, "include", "pi.h")) as fh:
+        m = re.search(r"#define PI_STATIC_WORKSPACE_BYTES \((\d+)u << (\d+)\)", fh.read())
+    assert pi.STATIC_WORKSPACE_BYTES == int(m.group(1)) << int(m.group(2))
