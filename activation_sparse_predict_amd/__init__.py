@@ -251,7 +251,7 @@ def ffn_stack(layers, x, out, counts=None, trace=None, ws=None, batch: int = 1, 
     Stack(layers, batch, ws)(x, out, counts, trace, stream, nz_counts)
 
 
-STATIC_WORKSPACE_BYTES = 64 << 20   # PI_STATIC_WORKSPACE_BYTES
+STATIC_WORKSPACE_BYTES = 48 << 20   # PI_STATIC_WORKSPACE_BYTES
 
 
 def ffn_stack_static(layers, x, out, counts=None, trace=None, batch: int = 1, stream=None, nz_counts=None):

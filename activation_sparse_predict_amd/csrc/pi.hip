@@ -33,6 +33,7 @@ pi_status check_mat(const pi_mat& m, int32_t dtype) {
 
 constexpr int kMaxD = 16384;
 constexpr int kMaxRank = 4096;
+constexpr int kMaxFfn = 1 << 21;   // the score kernel keeps each wave's active list in LDS
 
 pi_status check_layer(const pi_layer* L) {
   if (!L) return PI_EINVAL;
@@ -42,6 +43,7 @@ pi_status check_layer(const pi_layer* L) {
   if (L->w_dtype != PI_F32 && L->w_dtype != PI_F16 && L->w_dtype != PI_Q4_0) return PI_EINVAL;
   if (L->p_dtype == PI_Q4_0) return PI_EUNSUPPORTED;
   if (L->d > kMaxD || L->rank > kMaxRank) return PI_EUNSUPPORTED;   // vectors staged whole in LDS
+  if (L->ffn > kMaxFfn) return PI_EUNSUPPORTED;
   if (L->p_dtype != PI_F32 && L->p_dtype != PI_F16) return PI_EINVAL;
   if (!L->A || !L->B || !L->bias) return PI_EINVAL;
   if (!aligned(L->A, 16) || !aligned(L->B, 16) || !aligned(L->bias, 16)) return PI_EINVAL;
@@ -75,14 +77,17 @@ constexpr int kK2Grid = 512;   // two per compute unit of an MI355X
 int epl_of(int dt) { return dt == PI_F32 ? 4 : (dt == PI_F16 ? 8 : 32); }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// Grid size of the predictor kernel (one active count per block): at most this.
-int k2_blocks_for(int ffn, int rank, int p_dtype);
-int k2_blocks_max(int ffn);
+// Grid size of the score kernel (one active count per block), at most kK2Grid,
+// the capacity of each block's (neuron, h) list, and the entries of all lists.
+int k2_blocks_for(int ffn) { return std::max(1, std::min(kK2Grid, cdiv(ffn, 2 * K2_WAVES))); }   // >= 2 rows per wave
+int k2_blocks_max(int ffn) { return k2_blocks_for(ffn); }
+int k2_cap(int ffn) { return K2_WAVES * cdiv(ffn, k2_blocks_for(ffn) * K2_WAVES); }
+size_t k2_pairs_max(int ffn) { return (size_t)k2_blocks_for(ffn) * k2_cap(ffn); }
 // blocks of the batched score kernel: one tile of 32 neurons each
 int bscore_blocks(int ffn) { return cdiv(ffn, pib::BM); }
 
 struct WsLayout {
-  size_t t, xbuf, ybuf, xq, mask, pmask, h, cnt, misc;
+  size_t t, xbuf, ybuf, mask, pmask, h, pid, ph, cnt, misc;
   // batched path (batch > 1)
   size_t xh, xl, tpart, th, tl, mnm, ulist, hh, hl;
   size_t total;
@@ -101,10 +106,12 @@ WsLayout layout(const Dims& D, int batch) {
   w.t = o;    o += align_up(sizeof(float) * (size_t)D.rmax * batch);
   w.xbuf = o; o += w.xs * 2;
   w.ybuf = o; o += w.ys * 2;
-  w.xq = o;   o += align_up(sizeof(float) * (size_t)D.d);   // x' pair-transposed for Q4_0 gathers (batch 1)
   w.mask = o; o += align_up(fpad);                       // one byte per neuron (the union when batch > 1)
   w.pmask = o; o += align_up(fpad);                      // the predictor's mask for a trace list (batch 1)
   w.h = o;    o += align_up(sizeof(float) * (size_t)D.fmax);
+  // the score kernel's per-block (neuron, h) lists [blocks][cap] (batch 1)
+  w.pid = o;  o += align_up(sizeof(int32_t) * k2_pairs_max(D.fmax));
+  w.ph = o;   o += align_up(sizeof(float) * k2_pairs_max(D.fmax));
   // per-block counts: active neurons, then those with h != 0 (batch 1)
   w.cnt = o;  o += align_up(sizeof(int32_t) * (size_t)std::max(2 * k2_blocks_max(D.fmax), bscore_blocks(D.fmax)));
   w.misc = o; o += kAlign;
@@ -127,10 +134,11 @@ struct Ws {
   float* t;
   float* x[2];
   float* y[2];
-  float* xq;
   uint8_t* mask;
   uint8_t* pmask;
   float* h;
+  int32_t* pid;
+  float* ph;
   int32_t* cnt;
   int32_t* misc;
   _Float16 *xh, *xl, *th, *tl, *hh, *hl;
@@ -147,10 +155,11 @@ Ws carve(void* base, const WsLayout& L) {
   w.x[1] = reinterpret_cast<float*>(b + L.xbuf + L.xs);
   w.y[0] = reinterpret_cast<float*>(b + L.ybuf);
   w.y[1] = reinterpret_cast<float*>(b + L.ybuf + L.ys);
-  w.xq = reinterpret_cast<float*>(b + L.xq);
   w.mask = reinterpret_cast<uint8_t*>(b + L.mask);
   w.pmask = reinterpret_cast<uint8_t*>(b + L.pmask);
   w.h = reinterpret_cast<float*>(b + L.h);
+  w.pid = reinterpret_cast<int32_t*>(b + L.pid);
+  w.ph = reinterpret_cast<float*>(b + L.ph);
   w.cnt = reinterpret_cast<int32_t*>(b + L.cnt);
   w.misc = reinterpret_cast<int32_t*>(b + L.misc);
   if (L.xh) {
@@ -202,26 +211,16 @@ int k1_blocks(int r) { return std::max(1, cdiv(r, K1_WAVES)); }
 // K2: chunks per lane per row of B held at once (1 or 2)
 int k2_pch_of(int rank, int p_dtype) { return chunks_of(rank, p_dtype) <= 1 ? 1 : 2; }
 int k2_pch(const pi_layer* L) { return k2_pch_of(L->rank, L->p_dtype); }
-// chunks per lane per gathered up/gate row held at once
-constexpr int kWchF32[] = {2, 8};
-constexpr int kWchF16[] = {2, 8, 14, 16};
-constexpr int kWchQ4[] = {1, 6};
-int k2_wch(const pi_layer* L) {
-  const int n = chunks_of(L->d, L->w_dtype);
-  return L->w_dtype == PI_F32 ? pick(kWchF32, n) : L->w_dtype == PI_F16 ? pick(kWchF16, n) : pick(kWchQ4, n);
+// Chunks per lane of a gathered row (each of the block's 256 lanes owns
+// chunks tid + 256 j): the smallest supported power of two that covers the row.
+constexpr int kCplF32[] = {1, 2, 4, 8, 16};
+constexpr int kCplF16[] = {1, 2, 4, 8};
+constexpr int kCplQ4[] = {1, 2};
+int k2_cpl(const pi_layer* L) {
+  const int n = cdiv(L->d / epl_of(L->w_dtype), K2_THREADS);
+  return L->w_dtype == PI_F32 ? pick(kCplF32, n) : L->w_dtype == PI_F16 ? pick(kCplF16, n) : pick(kCplQ4, n);
 }
-// about one batch of B rows per wave, and at least ~4 waves per CU when ffn allows
-// K2: two blocks of K2_WAVES waves per CU at most, each wave with one batch
-// of rows of B when the layer is small enough, several batches (in turn) when
-// it is not.  Two blocks on some CUs and one on others would make the CUs with
-// two the kernel's tail.
-int k2_blocks_for(int ffn, int rank, int p_dtype) {
-  (void)rank;
-  (void)p_dtype;
-  return std::max(1, std::min(kK2Grid, cdiv(ffn, 2 * K2_WAVES)));   // at least two rows per wave
-}
-int k2_blocks(const pi_layer* L) { return k2_blocks_for(L->ffn, L->rank, L->p_dtype); }
-int k2_blocks_max(int ffn) { return std::max(k2_blocks_for(ffn, 64, PI_F32), k2_blocks_for(ffn, 1 << 20, PI_F32)); }
+int k2_blocks(const pi_layer* L) { return k2_blocks_for(L->ffn); }
 
 // K3: tiles of TWC = 4 chunks per row (64-byte row segments: one request per
 // row and tile, half an L2 line, the other half read by the neighbouring tile
@@ -251,7 +250,6 @@ struct K1Args {
   const float* y_prev;
   int y_np;
   float* x_out;
-  float* xq_out;   // pair-transposed copy of x' (Q4_0 gathers) or NULL
   float* x_trace;
   float* t;
 };
@@ -260,7 +258,7 @@ template <int PT, int NCH>
 void launch_k1_t(const pi_layer* L, const K1Args& a, hipStream_t st) {
   hipLaunchKernelGGL((k_predict_t<PT, NCH>), dim3(k1_blocks(L->rank)), dim3(K1_WAVES * WAVE),
                      sizeof(float) * (size_t)dma_pad(L->d) * (1 + a.y_np), st, L->A, L->rank, L->d, a.x_prev, a.y_prev, a.y_np, a.x_out,
-                     a.xq_out, a.x_trace, a.t);
+                     a.x_trace, a.t);
 }
 
 template <int PT>
@@ -283,36 +281,39 @@ void k1(const pi_layer* L, const K1Args& a, hipStream_t st) {
 
 struct K2Args {
   const float* t;
-  const float* xcur;   // x' (pair-transposed for Q4_0 weights)
+  const float* xcur;   // x' (the fused gathers)
   float* scores;
-  uint8_t* mask;
-  uint8_t* mask2;
-  int32_t* cnt;
-  float* h;
+  uint8_t* pmask;      // the predictor's mask byte per neuron, or NULL
+  int32_t* cnt;        // [2 * blocks]: active neurons, then those with h != 0
+  int32_t* pid;        // [blocks][cap] (neuron, h) lists of the fused gathers
+  float* ph;
 };
 
-template <int PT, int WT, int ACT, bool FUSE, int PCH, int WCH>
+template <int PT, int WT, int ACT, bool FUSE, int PCH, int CPL>
 void launch_k2_t(const pi_layer* L, const K2Args& a, hipStream_t st) {
-  const size_t lds = sizeof(float) * ((size_t)K2_WAVES * dma_pad(L->rank) + (FUSE ? (size_t)dma_pad(L->d) : 0));
-  hipLaunchKernelGGL((k_score<PT, WT, ACT, FUSE, PCH, WCH>), dim3(k2_blocks(L)), dim3(K2_WAVES * WAVE), lds, st,
+  const int nb = k2_blocks(L);
+  const size_t lds = sizeof(float) * (size_t)K2_WAVES * (dma_pad(L->rank) + cdiv(L->ffn, nb * K2_WAVES));
+  hipLaunchKernelGGL((k_score<PT, WT, ACT, FUSE, PCH, CPL>), dim3(nb), dim3(K2_THREADS), lds, st,
                      L->B, L->pbias ? L->pbias : L->bias, L->bias, a.t, L->ffn, L->rank, L->gate.w, L->gate.scale,
-                     L->up.w, L->up.scale, a.xcur, L->d, a.scores, a.mask, a.mask2, a.cnt, a.h);
+                     L->up.w, L->up.scale, a.xcur, L->d, a.scores, a.pmask, a.cnt, a.pid, a.ph, k2_cap(L->ffn));
 }
 
 template <int PT, int WT, int ACT, int PCH>
 void launch_k2_fused(const pi_layer* L, const K2Args& a, hipStream_t st) {
-  const int wch = k2_wch(L);
-  if constexpr (WT == DT_F32) {
-    if (wch == 2) return launch_k2_t<PT, WT, ACT, true, PCH, 2>(L, a, st);
-    return launch_k2_t<PT, WT, ACT, true, PCH, 8>(L, a, st);
-  } else if constexpr (WT == DT_F16) {
-    if (wch == 2) return launch_k2_t<PT, WT, ACT, true, PCH, 2>(L, a, st);
-    if (wch == 8) return launch_k2_t<PT, WT, ACT, true, PCH, 8>(L, a, st);
-    if (wch == 14) return launch_k2_t<PT, WT, ACT, true, PCH, 14>(L, a, st);
-    return launch_k2_t<PT, WT, ACT, true, PCH, 16>(L, a, st);
+  const int cpl = k2_cpl(L);
+  if constexpr (WT == DT_Q4) {
+    if (cpl == 1) return launch_k2_t<PT, WT, ACT, true, PCH, 1>(L, a, st);
+    return launch_k2_t<PT, WT, ACT, true, PCH, 2>(L, a, st);
   } else {
-    if (wch == 1) return launch_k2_t<PT, WT, ACT, true, PCH, 1>(L, a, st);
-    return launch_k2_t<PT, WT, ACT, true, PCH, 6>(L, a, st);
+    if (cpl == 1) return launch_k2_t<PT, WT, ACT, true, PCH, 1>(L, a, st);
+    if (cpl == 2) return launch_k2_t<PT, WT, ACT, true, PCH, 2>(L, a, st);
+    if (cpl == 4) return launch_k2_t<PT, WT, ACT, true, PCH, 4>(L, a, st);
+    if constexpr (WT == DT_F16) {
+      return launch_k2_t<PT, WT, ACT, true, PCH, 8>(L, a, st);
+    } else {
+      if (cpl == 8) return launch_k2_t<PT, WT, ACT, true, PCH, 8>(L, a, st);
+      return launch_k2_t<PT, WT, ACT, true, PCH, 16>(L, a, st);
+    }
   }
 }
 
@@ -344,8 +345,9 @@ void k2(const pi_layer* L, bool fuse_up, const K2Args& a, hipStream_t st) {
 }
 
 struct K3Args {
-  const uint8_t* mask;       // implicit mode
-  const float* h_full;
+  const int32_t* pid;        // list mode: the score kernel's per-block (neuron, h) lists
+  const float* ph;
+  int cap;
   const int32_t* idx;        // explicit mode
   const int32_t* count;
   const float* h_list;
@@ -362,7 +364,7 @@ void launch_k3_t(const pi_layer* L, const K3Shape& sh, const K3Args& a, hipStrea
   const int nblk = sh.ct * sh.nc;
   const int xcd = (nblk % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((k_down<WT, TWC, EXPL>), dim3(nblk), dim3(K3_WAVES * WAVE), 0, st, L->downT.w,
-                     L->downT.scale, L->ffn, L->d, sh.ct, sh.nc, xcd, a.mask, a.h_full, a.idx, a.count, a.h_list,
+                     L->downT.scale, L->ffn, L->d, sh.ct, sh.nc, xcd, a.pid, a.ph, a.cap, a.idx, a.count, a.h_list,
                      L->b_down, a.y_part, a.cnt_blk, a.n_cnt_blk, a.count_out, a.count_out2, a.nz_out);
 }
 
@@ -392,14 +394,23 @@ template <int WT, int ACT, int WCH>
 void launch_up_list_w(const pi_layer* L, const float* x, const int32_t* idx, const int32_t* count, float* h_list,
                       hipStream_t st) {
   const int nb = std::max(1, std::min(1024, cdiv(L->ffn, 4)));
-  hipLaunchKernelGGL((k_up_list<WT, ACT, WCH>), dim3(nb), dim3(kThreads), sizeof(float) * L->d, st, L->gate.w,
+  hipLaunchKernelGGL((k_up_list<WT, ACT, WCH>), dim3(nb), dim3(kThreads), sizeof(float) * q4t_len(L->d), st, L->gate.w,
                      L->gate.scale, L->up.w, L->up.scale, L->bias, x, L->d, L->ffn, idx, count, h_list);
+}
+
+// chunks per lane per gathered up/gate row held at once (explicit lists)
+constexpr int kWchF32[] = {2, 8};
+constexpr int kWchF16[] = {2, 8, 14, 16};
+constexpr int kWchQ4[] = {1, 6};
+int up_list_wch(const pi_layer* L) {
+  const int n = chunks_of(L->d, L->w_dtype);
+  return L->w_dtype == PI_F32 ? pick(kWchF32, n) : L->w_dtype == PI_F16 ? pick(kWchF16, n) : pick(kWchQ4, n);
 }
 
 template <int WT, int ACT>
 void launch_up_list_t(const pi_layer* L, const float* x, const int32_t* idx, const int32_t* count, float* h_list,
                       hipStream_t st) {
-  const int wch = k2_wch(L);
+  const int wch = up_list_wch(L);
   if constexpr (WT == DT_F32) {
     if (wch == 2) return launch_up_list_w<WT, ACT, 2>(L, x, idx, count, h_list, st);
     return launch_up_list_w<WT, ACT, 8>(L, x, idx, count, h_list, st);
@@ -597,22 +608,21 @@ pi_status run_stack(const pi_layer* layers, int32_t n_layers, const float* x, in
     const pi_trace* tr = trace ? &trace[l] : nullptr;
     const int cur = l & 1, prv = cur ^ 1;
     mark(tr, 0, st);
-    const bool q4 = L->w_dtype == PI_Q4_0;
-    k1(L, K1Args{l == 0 ? x : W.x[prv], l == 0 ? nullptr : W.y[prv], np_prev, W.x[cur], q4 ? W.xq : nullptr,
-                 tr ? tr->x_in : nullptr, W.t}, st);
+    k1(L, K1Args{l == 0 ? x : W.x[prv], l == 0 ? nullptr : W.y[prv], np_prev, W.x[cur], tr ? tr->x_in : nullptr,
+                 W.t}, st);
     mark(tr, 1, st);
-    // W.mask marks the active neurons with h != 0 (the rows the down projection
-    // reads); the predictor's own mask goes to the record, or to W.pmask when
-    // only the record's list asks for it
+    // the predictor's own mask goes to the record, or to W.pmask when only the
+    // record's list asks for it
     uint8_t* pmask = tr ? (tr->mask ? tr->mask : (tr->idx ? W.pmask : nullptr)) : nullptr;
-    k2(L, true, K2Args{W.t, q4 ? W.xq : W.x[cur], tr ? tr->scores : nullptr, W.mask, pmask, W.cnt, W.h}, st);
+    k2(L, true, K2Args{W.t, W.x[cur], tr ? tr->scores : nullptr, pmask, W.cnt, W.pid, W.ph}, st);
     mark(tr, 2, st);
     int32_t* c1 = counts ? counts + l : nullptr;
     int32_t* c2 = (tr && tr->count && !tr->idx) ? tr->count : nullptr;
     if (tr && tr->idx)   // ascending list of the predictor's mask, for the record
       hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, pmask, L->ffn, tr->idx,
                          tr->count ? tr->count : W.misc, nullptr, nullptr);
-    np_prev = k3<false>(L, K3Args{W.mask, W.h, nullptr, nullptr, nullptr, W.y[cur], W.cnt, k2_blocks(L), c1, c2,
+    np_prev = k3<false>(L, K3Args{W.pid, W.ph, k2_cap(L->ffn), nullptr, nullptr, nullptr, W.y[cur], W.cnt,
+                                  k2_blocks(L), c1, c2,
                                   nz_counts ? nz_counts + l : nullptr}, st);
     mark(tr, 3, st);
     if (tr && tr->y)     // the layer's y for the record: its partial vectors added in the glue's order
@@ -709,9 +719,10 @@ pi_status pi_predict(const pi_layer* layer, const float* x, int32_t batch, float
     b_predict(layer, batch, W, scores, mask, idx, count, nullptr, nullptr, st);
     return launch_status();
   }
-  k1(layer, K1Args{x, nullptr, 0, nullptr, nullptr, nullptr, W.t}, st);
-  k2(layer, false, K2Args{W.t, nullptr, scores, W.mask, mask, nullptr, nullptr}, st);
-  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, layer->ffn, idx, count, nullptr, nullptr);
+  k1(layer, K1Args{x, nullptr, 0, nullptr, nullptr, W.t}, st);
+  uint8_t* pm = mask ? mask : W.mask;
+  k2(layer, false, K2Args{W.t, nullptr, scores, pm, nullptr, nullptr, nullptr}, st);
+  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, pm, layer->ffn, idx, count, nullptr, nullptr);
   return launch_status();
 }
 
@@ -743,7 +754,8 @@ pi_status pi_sparse_ffn(const pi_layer* layer, const float* x, int32_t batch, co
     return launch_status();
   }
   up_list(layer, x, idx, count, W.h, st);
-  const int np = k3<true>(layer, K3Args{nullptr, nullptr, idx, count, W.h, W.y[0], nullptr, 0, nullptr, nullptr, nullptr},
+  const int np = k3<true>(layer, K3Args{nullptr, nullptr, 0, idx, count, W.h, W.y[0], nullptr, 0, nullptr, nullptr,
+                                        nullptr},
                           st);
   hipLaunchKernelGGL(k_finalize, dim3(cdiv(layer->d, 256)), dim3(256), 0, st, W.y[0], np, y, layer->d);
   return launch_status();

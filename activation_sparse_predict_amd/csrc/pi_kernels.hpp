@@ -7,14 +7,16 @@
 // retire):
 //   K1 k_predict_t  residual RMS glue (recomputed identically by every block)
 //                   and the predictor's first GEMV t = A x
-//   K2 k_score      predictor second GEMV s = B t + c, threshold s > 0, one mask
-//                   byte per neuron, and -- fused -- the gathered up/gate GEMV
-//                   with ReLU or ReGLU for the active neurons (h per neuron)
-//   K3 k_down       down projection over the active neurons; each block owns a
-//                   column tile (and one of NC neuron splits), builds its list
-//                   of active neurons from the mask bytes in LDS, gathers their
-//                   row segments and writes its partial y with plain stores;
-//                   the consumer adds the NC partials in a fixed order
+//   K2 k_score      predictor second GEMV s = B t + c and threshold s > 0 for
+//                   every neuron, then -- fused -- the gathered up/gate GEMV
+//                   with its activation for the block's active neurons, all of
+//                   the block's lanes on each row; per-block lists of the
+//                   (neuron, h) pairs with h != 0
+//   K3 k_down       down projection over the listed neurons; each block owns a
+//                   column tile (and one of NC neuron splits), copies its share
+//                   of the lists into LDS, gathers their row segments and
+//                   writes its partial y with plain stores; the consumer adds
+//                   the NC partials in a fixed order
 //
 // Weight loads are 16 bytes per lane (4 fp32, 8 fp16 or one Q4_0 block of 32
 // nibbles).  Every batch of loads is issued unconditionally (indices clamped
@@ -129,6 +131,20 @@ __device__ __forceinline__ float group_sum(float x, int lane) {
   return res;
 }
 
+// Sum over the lanes of each 16-lane row that share lane % G (G = 1, 2, 4, 8
+// or 16), left in the row's last G lanes: lane 16 r + 16 - G + q holds the sum
+// for residue q of row r.  Row shifts that are multiples of G, added in a
+// fixed order; the other lanes hold partial sums.
+template <int G>
+__device__ __forceinline__ float row_group_sum(float x) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "bad group");
+  if constexpr (G <= 1) x += dpp_f<0x111>(x);
+  if constexpr (G <= 2) x += dpp_f<0x112>(x);
+  if constexpr (G <= 4) x += dpp_f<0x114>(x);
+  if constexpr (G <= 8) x += dpp_f<0x118>(x);
+  return x;
+}
+
 // 16-byte chunk of row `row` starting at element `e` (a multiple of EPL).
 template <int DT>
 __device__ __forceinline__ uint4 ld_chunk(const void* __restrict__ w, size_t row, int n, int e) {
@@ -171,20 +187,8 @@ __device__ __forceinline__ float chunk_dot(uint4 c, float scale, const float* __
     a = fmaf((float)h[7], x1.w, a);
     return a;
   } else {
-    // weight j < 16: low nibble of byte j; weight j + 16: high nibble of byte j
-    const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
-    float a = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint32_t byte = (wd[k] >> (8 * b)) & 0xFFu;
-        const int j = 4 * k + b;
-        a = fmaf((float)((int)(byte & 15u) - 8), x[j], a);
-        a = fmaf((float)((int)(byte >> 4) - 8), x[j + 16], a);
-      }
-    }
-    return a * scale;
+    static_assert(DT != DT_Q4, "Q4_0 rows are dotted with chunk_dot_q4t");
+    return 0.f;
   }
 }
 
@@ -197,39 +201,44 @@ __device__ __forceinline__ int opaque_zero() {
   return z;
 }
 
-// 8.0f that the compiler cannot see as a constant.  With a literal 8, it
-// rewrites (float)q - 8 as (float)(int)(q - 8) and extracts every nibble with
-// a separate bit-field instruction; with this, each nibble costs one
-// byte-to-float conversion (v_cvt_f32_ubyte*) and one subtract.
-__device__ __forceinline__ float q4_offset() { return __int_as_float(0x41000000 + opaque_zero()); }
+// The low and the high nibble of each byte of w, each in a byte of its own
+// (w & 0x0F0F0F0F, (w >> 4) & 0x0F0F0F0F), with a mask the compiler cannot
+// see as a constant.  Seeing it, the compiler extracts every nibble with a
+// bit-field instruction of its own before converting it; this way each byte
+// is converted in place (v_cvt_f32_ubyte0..3): one instruction per weight.
+__device__ __forceinline__ uint32_t nib_mask() { return 0x0F0F0F0Fu + (uint32_t)opaque_zero(); }
+__device__ __forceinline__ float ubyte_f(uint32_t w, int b) { return (float)((w >> (8 * b)) & 0xFFu); }
 
 // Q4_0 activations in LDS for the gathered dot products, pair-transposed:
 // element 32 b + j (block b, 0 <= j < 32) is half j / 16 of the float2 at
 // xq[(j % 16) * nb + b], nb = d / 32.  A lane that owns block b reads its 16
 // pairs at stride nb, so the 64 lanes of a wave read 64 consecutive 8-byte
 // words per access: no LDS bank conflicts (the linear layout puts the lanes
-// 128 bytes apart, all on the same banks).
+// 128 bytes apart, all on the same banks).  The block sums of x follow the d
+// values: xq[d + b] = sum of the 32 elements of block b.
 __host__ __device__ constexpr int q4t_pos(int k, int d) { return ((k & 15) * (d >> 5) + (k >> 5)) * 2 + ((k >> 4) & 1); }
+// floats of a pair-transposed x with its block sums (padded to whole 16-byte vectors)
+__host__ __device__ constexpr int q4t_len(int d) { return d + ((d >> 5) + 3) / 4 * 4; }
 
-// sum_j w_j * x_j over Q4_0 block `blk`, x in the pair-transposed layout; the
-// same operation order as chunk_dot<DT_Q4>.
+// sum_j w_j * x_j over Q4_0 block `blk`, x in the pair-transposed layout and
+// xsum the block's sum of x: sum_j d (q_j - 8) x_j = d (sum_j q_j x_j - 8 xsum),
+// so each weight costs one conversion and one FMA.
 __device__ __forceinline__ float chunk_dot_q4t(uint4 c, float scale, const float2* __restrict__ xq, int blk, int nb,
-                                               float off) {
+                                               float xsum) {
   const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
+  const uint32_t m = nib_mask();
   float a = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    // the nibbles of four bytes as bytes: each (x >> 8 b) & 0xFF becomes one
-    // byte-to-float conversion
-    const uint32_t lo = wd[k] & 0x0F0F0F0Fu, hi = (wd[k] >> 4) & 0x0F0F0F0Fu;
+    const uint32_t lo = wd[k] & m, hi = (wd[k] >> 4) & m;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const float2 xv = xq[(4 * k + b) * nb + blk];
-      a = fmaf((float)((lo >> (8 * b)) & 0xFFu) - off, xv.x, a);
-      a = fmaf((float)((hi >> (8 * b)) & 0xFFu) - off, xv.y, a);
+      a = fmaf(ubyte_f(lo, b), xv.x, a);
+      a = fmaf(ubyte_f(hi, b), xv.y, a);
     }
   }
-  return a * scale;
+  return fmaf(-8.f, xsum, a) * scale;
 }
 
 // acc[j] += h * w_j over one chunk (acc has EPL entries).  For Q4_0 it adds
@@ -250,16 +259,15 @@ __device__ __forceinline__ void chunk_axpy(uint4 c, float scale, float h, float*
     const float hs = h * scale;
     hsum += hs;
     const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
+    const uint32_t m = nib_mask();
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      // the nibbles of four bytes as bytes: each (x >> 8 b) & 0xFF becomes one
-      // byte-to-float conversion
-      const uint32_t lo = wd[k] & 0x0F0F0F0Fu, hi = (wd[k] >> 4) & 0x0F0F0F0Fu;
+      const uint32_t lo = wd[k] & m, hi = (wd[k] >> 4) & m;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int j = 4 * k + b;
-        acc[j] = fmaf(hs, (float)((lo >> (8 * b)) & 0xFFu), acc[j]);
-        acc[j + 16] = fmaf(hs, (float)((hi >> (8 * b)) & 0xFFu), acc[j + 16]);
+        acc[j] = fmaf(hs, ubyte_f(lo, b), acc[j]);
+        acc[j + 16] = fmaf(hs, ubyte_f(hi, b), acc[j + 16]);
       }
     }
   }
@@ -366,7 +374,8 @@ __device__ __forceinline__ float stage_residual(float* __restrict__ lds, const f
 }
 
 // Dot products of rows rows[0..NN) of NMAT matrices (NMAT = 2: gate, up) with
-// the LDS vector xs[d] (pair-transposed for Q4_0, see q4t_pos): all NN * NMAT * NCH chunk loads of a round are issued
+// the LDS vector xs[d] (for Q4_0 pair-transposed, with its block sums: see q4t_pos): all NN * NMAT * NCH chunk
+// loads of a round are issued
 // before the first multiply, one HBM round trip per round.  z[n][m] is row
 // rows[n] of matrix m dotted with xs, in every lane.  Chunks past the row
 // (ragged tail, or beyond the row's chunk count) load a clamped, valid address
@@ -378,7 +387,6 @@ __device__ __forceinline__ void gather_rows(const void* __restrict__ w0, const u
                                             float (&z)[NN][NMAT]) {
   constexpr int EPL = Tr<WT>::EPL, TW = WAVE * EPL, NV = NN * NMAT;
   const int nch = (d + TW - 1) / TW;
-  const float off = WT == DT_Q4 ? q4_offset() : 0.f;
   float a[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) a[v] = 0.f;
@@ -404,7 +412,8 @@ __device__ __forceinline__ void gather_rows(const void* __restrict__ w0, const u
       for (int v = 0; v < NV; ++v) {
         float p;
         if constexpr (WT == DT_Q4)
-          p = chunk_dot_q4t(c[v][q], fs[v][q], reinterpret_cast<const float2*>(xs), ok ? e / 32 : 0, d / 32, off);
+          p = chunk_dot_q4t(c[v][q], fs[v][q], reinterpret_cast<const float2*>(xs), ok ? e / 32 : 0, d / 32,
+                            xs[d + (ok ? e / 32 : 0)]);
         else
           p = chunk_dot<WT>(c[v][q], fs[v][q], xs + (ok ? e : 0));
         a[v] += ok ? p : 0.f;
@@ -425,7 +434,7 @@ __device__ __forceinline__ void gather_rows(const void* __restrict__ w0, const u
 // flight.  The dot product takes v and the row's result is scaled by
 // 1 / sqrt(mean(v^2) + 1e-6).  Every block computes the same v and scale with
 // the same operation order, so all agree bit for bit; each block writes its
-// slice of x' (and, if xq_out is given, of its pair-transposed Q4_0 copy).
+// slice of x'.
 // Eight waves per block halve the blocks that repeat the glue (MI355X: 5%
 // faster at d = 8192 and 12288, neutral at 4096).
 constexpr int K1_WAVES = 8;
@@ -433,8 +442,8 @@ constexpr int K1_WAVES = 8;
 template <int PT, int NCH>
 __global__ void __launch_bounds__(K1_WAVES * WAVE)
 k_predict_t(const void* __restrict__ A, int r, int d, const float* __restrict__ x_prev,
-            const float* __restrict__ y_prev, int y_np, float* __restrict__ x_out, float* __restrict__ xq_out,
-            float* __restrict__ x_trace, float* __restrict__ t) {
+            const float* __restrict__ y_prev, int y_np, float* __restrict__ x_out, float* __restrict__ x_trace,
+            float* __restrict__ t) {
   extern __shared__ float smem[];
   __shared__ float red[K1_WAVES];
   constexpr int EPL = Tr<PT>::EPL, TW = WAVE * EPL;
@@ -500,7 +509,6 @@ k_predict_t(const void* __restrict__ A, int r, int d, const float* __restrict__ 
     for (int k = b * cx + tid; k < min(d, (b + 1) * cx); k += blockDim.x) {
       const float xk = y_np > 0 ? xs[k] * inv : xs[k];
       if (x_out) x_out[k] = xk;
-      if (xq_out) xq_out[q4t_pos(k, d)] = xk;
       if (x_trace) x_trace[k] = xk;
     }
   }
@@ -531,59 +539,140 @@ k_predict_t(const void* __restrict__ A, int r, int d, const float* __restrict__ 
 }
 
 // ----------------------------------------------------------------------- K2
-// Scores s_i = c_i + B[i] . t, threshold s_i > 0, one mask byte per neuron,
-// and -- if FUSE -- the gathered up/gate GEMV with ReLU or ReGLU for the active
-// neurons.  The neurons are dealt to the blocks round-robin (so the hot-first
-// order spreads the frequently active rows evenly over the blocks).  Each
-// wave copies t into its own LDS slice and the block copies x' into LDS, both
-// by LDS-DMA issued ahead of the rows of B, so no barrier and no register
-// staging stands between the rows' arrival and the first multiply.  A wave
-// loads RB = 16 / PCH rows of B (PCH 16-byte chunks per lane each) before its
-// first multiply and reduces the RB dot products with one butterfly each.
-// The waves' active neurons then go to per-wave lists in LDS (ballot order,
-// no atomics) and the block's waves take the concatenated list two at a time
-// (gate and up rows of both, WCH chunks per lane per row, in one HBM round
-// trip): the number of actives per wave varies a lot, per block much less,
-// and the slowest wave sets the kernel's time.
-// The block's active count goes to cnt_blk[block] (summed over batches) and
-// the count of its active neurons with h != 0 to cnt_blk[nb + block].
-// With FUSE, `mask` marks only the neurons whose h is nonzero: a neuron the
-// predictor marks but whose ReLU output is 0 adds nothing to y, so the down
-// projection does not read its row; `mask2` (if given) is the predictor's mask.
-// Global stores come after the block barrier so that the barrier does not wait
-// for them.
+// Scores s_i = c_i + B[i] . t, threshold s_i > 0, and -- if FUSE -- the
+// gathered up/gate GEMV with ReLU, ReGLU or Squared ReLU for the active
+// neurons, in two phases:
+//  1. The rows of B.  The neurons are dealt to the blocks round-robin (so the
+//     hot-first order spreads the frequently active rows evenly over the
+//     blocks); wave w of block b owns neurons b + nb (w + K2_WAVES m).  Each
+//     wave copies t into its own LDS slice by LDS-DMA ahead of its rows of B,
+//     loads RB = 16 / PCH rows (PCH 16-byte chunks per lane each) before its
+//     first multiply, and appends the active ones to its own list in LDS
+//     (ballot order: ascending within the wave).  No barrier: the waves stream
+//     B independently.
+//  2. The block's active list (the waves' lists one after another), R rows
+//     at a time, by all 256 lanes together: lane tid owns chunks tid + 256 j
+//     (j < CPL) of every row, and holds its x' values for those chunks in
+//     registers, loaded at the start.  Every load of a round is issued before
+//     the first multiply; the lanes' partial dot products are summed per wave
+//     and the waves' sums in a fixed order.  Wave 0 then applies the bias and
+//     the activation and appends the neurons with h != 0 to the block's list
+//     of (neuron, h) pairs: pair_id / pair_h [block][cap].  A neuron whose
+//     ReLU output is 0 adds nothing to y, so the down projection reads only
+//     the listed rows.
+// cnt_blk[block] = active neurons of the block, cnt_blk[nb + block] = those
+// with h != 0.  pmask (if given) gets the predictor's mask byte per neuron.
 constexpr int K2_WAVES = 4;
+constexpr int K2_THREADS = K2_WAVES * WAVE;
 
-template <int PT, int WT, int ACT, bool FUSE, int PCH, int WCH>
-__global__ void __launch_bounds__(K2_WAVES * WAVE) __attribute__((amdgpu_waves_per_eu(2)))
+// Chunk slots of a lane loaded at once in a gather round (rows longer than
+// 256 * 8 chunks take several groups), and rows per round: as many as keep
+// NMAT * CG chunk loads per row at 16 per lane (at least 1).
+template <int CPL> constexpr int k2_cg() { return CPL < 8 ? CPL : 8; }
+template <int NMAT, int CPL> constexpr int k2_rows() {
+  return (16 / (NMAT * k2_cg<CPL>())) < 1 ? 1 : 16 / (NMAT * k2_cg<CPL>());
+}
+
+// x' for the chunks a lane owns, in registers (EPL floats per chunk, and
+// for Q4_0 the chunk's block sum).
+template <int WT, int CPL>
+struct XReg {
+  float v[CPL][Tr<WT>::EPL];
+  float bsum[CPL];
+};
+
+template <int WT, int CPL>
+__device__ __forceinline__ void load_xreg(XReg<WT, CPL>& xr, const float* __restrict__ x, int nch, int tid) {
+  constexpr int EPL = Tr<WT>::EPL;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = min(tid + K2_THREADS * j, nch - 1);
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(x + (size_t)c * EPL + e);
+      xr.v[j][e] = v.x;
+      xr.v[j][e + 1] = v.y;
+      xr.v[j][e + 2] = v.z;
+      xr.v[j][e + 3] = v.w;
+    }
+  }
+}
+
+// The Q4_0 block sums of the chunks, once their values have arrived.
+template <int WT, int CPL>
+__device__ __forceinline__ void xreg_sums(XReg<WT, CPL>& xr) {
+  if constexpr (WT == DT_Q4) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) sum += xr.v[j][e];
+      xr.bsum[j] = sum;
+    }
+  }
+}
+
+// sum_j w_j * x_j over one chunk with x in registers (the chunk's EPL values).
+// Q4_0: d (sum_j q_j x_j - 8 xsum), one conversion and one FMA per weight.
+template <int DT>
+__device__ __forceinline__ float chunk_dot_reg(uint4 c, float scale, const float* xv, float xsum) {
+  if constexpr (DT == DT_F32) {
+    float a = __uint_as_float(c.x) * xv[0];
+    a = fmaf(__uint_as_float(c.y), xv[1], a);
+    a = fmaf(__uint_as_float(c.z), xv[2], a);
+    a = fmaf(__uint_as_float(c.w), xv[3], a);
+    return a;
+  } else if constexpr (DT == DT_F16) {
+    const half8_t h = __builtin_bit_cast(half8_t, c);
+    float a = (float)h[0] * xv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) a = fmaf((float)h[e], xv[e], a);
+    return a;
+  } else {
+    const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
+    const uint32_t m = nib_mask();
+    float a = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = wd[k] & m, hi = (wd[k] >> 4) & m;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        a = fmaf(ubyte_f(lo, b), xv[4 * k + b], a);
+        a = fmaf(ubyte_f(hi, b), xv[4 * k + b + 16], a);
+      }
+    }
+    return fmaf(-8.f, xsum, a) * scale;
+  }
+}
+
+template <int PT, int WT, int ACT, bool FUSE, int PCH, int CPL>
+__global__ void __launch_bounds__(K2_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const float* __restrict__ bias,
         const float* __restrict__ t, int f, int r,
         const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc,
         const void* __restrict__ up_w, const uint16_t* __restrict__ up_sc,
         const float* __restrict__ xcur, int d,
-        float* __restrict__ scores, uint8_t* __restrict__ mask, uint8_t* __restrict__ mask2,
-        int32_t* __restrict__ cnt_blk, float* __restrict__ h_full) {
+        float* __restrict__ scores, uint8_t* __restrict__ pmask, int32_t* __restrict__ cnt_blk,
+        int32_t* __restrict__ pair_id, float* __restrict__ pair_h, int cap) {
   constexpr int RB = 16 / PCH;                               // rows of B per batch
   constexpr int PEPL = Tr<PT>::EPL, PTW = WAVE * PEPL;
+  constexpr int NMAT = act_nmat<ACT>();
+  constexpr int R = k2_rows<NMAT, CPL>();                    // rows per gather round
+  constexpr int EPL = Tr<WT>::EPL;
   extern __shared__ float smem[];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  float* ts = smem + w * dma_pad(r);               // this wave's own copy of t [dma_pad(r)]
-  float* xs = smem + K2_WAVES * dma_pad(r);        // x' [dma_pad(d)] (FUSE only)
-  // per-batch active lists, one per wave (in row order) with its length, two
-  // slots in rotation: batch b writes slot b % 2 before its barrier and reads
-  // it after; batch b + 2 writes it again only after barrier b + 1, which no
-  // wave passes before every wave is done reading batch b's lists
-  __shared__ int act[2][K2_WAVES][RB];
-  __shared__ int nact[2][K2_WAVES];
-  // wave w of block b owns neurons i = b + nb (w + K2_WAVES m), m = 0, 1, ...:
-  // the block index runs fastest, so every block gets an equal share of each
-  // stretch of the hot-first order and the blocks' active counts are alike
   const int nb = gridDim.x, b = blockIdx.x, NW = nb * K2_WAVES;
   const int g = b + nb * w;                                  // the wave's first neuron
   const int M = g < f ? (f - 1 - g) / NW + 1 : 0;            // neurons of this wave
   const int Mb = b < f ? (f - 1 - b) / NW + 1 : 0;           // wave 0 has the most: block-uniform trip count
+  const int Mw = (f + NW - 1) / NW;                          // list capacity per wave (= Mb of block 0)
+  float* ts = smem + w * dma_pad(r);                         // this wave's own copy of t [dma_pad(r)]
+  int* act = reinterpret_cast<int*>(smem + K2_WAVES * dma_pad(r));   // [K2_WAVES][Mw] active lists
+  __shared__ int nact[K2_WAVES];
+  __shared__ float red[2][K2_WAVES][R * NMAT];
   const int pch = (r + PTW - 1) / PTW;
   const int my_u = min(lane, RB - 1);                        // lane u < RB reports row u of the batch
+  const int nch = (d + EPL - 1) / EPL;                       // chunks per gathered row
 
   // Rows past the wave's last neuron (all rows, for a wave without neurons)
   // and chunks past the row end load a clamped, valid address and are
@@ -603,18 +692,16 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
     PI_ISSUE_FENCE();
   };
 
-  // t (a copy per wave, so that no barrier stands between it and the first
-  // dot products) and x' (shared; first read after the score barrier) go to
-  // LDS by LDS-DMA ahead of the first rows of B.  The rows' addresses depend on
-  // an opaque zero taken after the copies are issued, so the rows stay behind
-  // them and t arrives while the rows are still in flight.
+  // t goes to LDS by LDS-DMA ahead of everything else; x' for the gathers to
+  // registers next (it is needed last); the rows of B after both, their
+  // addresses depending on an opaque zero so they cannot be hoisted.
   dma_f32(ts, t, r, 0, 1, lane);
-  if constexpr (FUSE) dma_f32(xs, xcur, d, w, K2_WAVES, lane);
+  XReg<WT, CPL> xr;
+  if constexpr (FUSE) load_xreg<WT, CPL>(xr, xcur, nch, tid);
   issue(0, 0, opaque_zero());
 
-  int block_count = 0;
-  int nz = 0;                                                // this wave's gathered neurons with h != 0
-  for (int m0 = 0, batch = 0; m0 < Mb; m0 += RB, ++batch) {
+  int n_w = 0;                                               // this wave's active neurons so far
+  for (int m0 = 0; m0 < Mb; m0 += RB) {
     float acc[RB];
 #pragma unroll
     for (int u = 0; u < RB; ++u) acc[u] = 0.f;
@@ -640,86 +727,114 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
     const int m = m0 + my_u;
     const bool rep = lane < RB && m < M;
     const int i = g + NW * m;
-    const float s = dot + pb;
-    const bool on = rep && s > 0.f;
-
-    const int par = batch & 1;
+    const float sc = dot + pb;
+    const bool on = rep && sc > 0.f;
     const uint64_t bal = __ballot(on);                       // lanes u < RB: rows in order
-    if (on) act[par][w][__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = i;
-    if (lane == 0) nact[par][w] = __popcll(bal);
-    __syncthreads();
-    // the block's list is the waves' lists one after another; entry a is in
-    // the list of the wave whose prefix bounds it
-    int pre[K2_WAVES + 1];
-    pre[0] = 0;
-#pragma unroll
-    for (int v = 0; v < K2_WAVES; ++v) pre[v + 1] = pre[v] + nact[par][v];
-    const int n = pre[K2_WAVES];
-    auto entry = [&](int a) __attribute__((always_inline)) {
-      int ww = 0, base = 0;
-#pragma unroll
-      for (int v = 1; v < K2_WAVES; ++v)
-        if (a >= pre[v]) { ww = v; base = pre[v]; }
-      return act[par][ww][a - base];
-    };
-    if (tid == 0) block_count += n;
-    if (m0 + RB < Mb) issue(m0 + RB, 0, 0);    // the next batch's rows of B, in flight during the gather
+    if (on) act[w * Mw + n_w + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = i;
+    n_w += __popcll(bal);
+    if (m0 + RB < Mb) issue(m0 + RB, 0, 0);                  // the next batch's rows of B
     if (rep) {
-      if (scores) scores[i] = s;
-      // fused: mask marks the neurons whose h is nonzero (the rows the down
-      // projection reads); inactive ones here, active ones when h is known
-      if (!FUSE || !on) mask[i] = on ? 1 : 0;
-      if (mask2) mask2[i] = on ? 1 : 0;
+      if (scores) scores[i] = sc;
+      if (pmask) pmask[i] = on ? 1 : 0;
     }
-    if constexpr (FUSE) {
-      constexpr int NMAT = act_nmat<ACT>();
-      const void* w0 = (ACT == ACT_REGLU) ? gate_w : up_w;
-      const uint16_t* s0 = (ACT == ACT_REGLU) ? gate_sc : up_sc;
-      // wave w takes entries w, w + 4 (a pair when both exist and the pair's
-      // rows fit the registers), then w + 8, w + 12, ...
-      constexpr bool PAIR = NMAT * WCH <= 16;
-      for (int a = w; a < n; a += (PAIR ? 2 : 1) * K2_WAVES) {
-        if (PAIR && a + K2_WAVES < n) {
-          const int rows[2] = {entry(a), entry(a + K2_WAVES)};
-          const float b0 = bias[rows[0]], b1 = bias[rows[1]];
-          float z[2][NMAT];
-          gather_rows<WT, WCH, NMAT, 2>(w0, s0, up_w, up_sc, rows, d, xs, lane, z);
-          const float h0 = act_h<ACT>(z[0][0], b0, z[0][NMAT - 1]);
-          const float h1 = act_h<ACT>(z[1][0], b1, z[1][NMAT - 1]);
-          nz += (h0 != 0.f) + (h1 != 0.f);
-          if (lane == 0) {
-            h_full[rows[0]] = h0;
-            h_full[rows[1]] = h1;
-            mask[rows[0]] = h0 != 0.f;
-            mask[rows[1]] = h1 != 0.f;
-          }
-        } else {
-          const int rows[1] = {entry(a)};
-          const float b0 = bias[rows[0]];
-          float z[1][NMAT];
-          gather_rows<WT, WCH, NMAT, 1>(w0, s0, up_w, up_sc, rows, d, xs, lane, z);
-          const float h0 = act_h<ACT>(z[0][0], b0, z[0][NMAT - 1]);
-          nz += (h0 != 0.f);
-          if (lane == 0) {
-            h_full[rows[0]] = h0;
-            mask[rows[0]] = h0 != 0.f;
-          }
+  }
+  if (lane == 0) nact[w] = n_w;
+  __syncthreads();
+  int pre[K2_WAVES + 1];
+  pre[0] = 0;
+#pragma unroll
+  for (int v = 0; v < K2_WAVES; ++v) pre[v + 1] = pre[v] + nact[v];
+  const int n = pre[K2_WAVES];
+  // entry a of the block's list: in the list of the wave whose prefix bounds it
+  auto entry = [&](int a) __attribute__((always_inline)) {
+    int ww = 0, base = 0;
+#pragma unroll
+    for (int v = 1; v < K2_WAVES; ++v)
+      if (a >= pre[v]) { ww = v; base = pre[v]; }
+    return act[ww * Mw + a - base];
+  };
+
+  int nz = 0;                                                // wave 0: neurons listed with h != 0
+  if constexpr (FUSE) {
+    xreg_sums<WT, CPL>(xr);
+    const void* w0 = (ACT == ACT_REGLU) ? gate_w : up_w;
+    const uint16_t* s0 = (ACT == ACT_REGLU) ? gate_sc : up_sc;
+    for (int a0 = 0, round = 0; a0 < n; a0 += R, ++round) {
+      int rows[R];
+#pragma unroll
+      for (int u = 0; u < R; ++u) rows[u] = entry(min(a0 + u, n - 1));
+      // wave 0, lane u < R: row u of the round and its bias (read with the rows)
+      const int my_row = entry(min(a0 + min(lane, R - 1), n - 1));
+      float bb = 0.f;
+      constexpr int CG = k2_cg<CPL>();
+      float part[R][NMAT];
+#pragma unroll
+      for (int u = 0; u < R; ++u)
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt) part[u][mt] = 0.f;
+#pragma unroll
+      for (int j0 = 0; j0 < CPL; j0 += CG) {
+        uint4 c[R][NMAT][CG];
+        float fs[R][NMAT][CG];
+#pragma unroll
+        for (int u = 0; u < R; ++u)
+#pragma unroll
+          for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+            for (int j = 0; j < CG; ++j) {
+              const int cc = min(tid + K2_THREADS * (j0 + j), nch - 1);
+              c[u][mt][j] = ld_chunk<WT>(mt ? up_w : w0, (size_t)rows[u], d, cc * EPL);
+              fs[u][mt][j] = (WT == DT_Q4) ? ld_scale(mt ? up_sc : s0, (size_t)rows[u], d, cc * EPL) : 1.f;
+            }
+        if (j0 == 0 && w == 0) bb = bias[my_row];
+        PI_ISSUE_FENCE();
+#pragma unroll
+        for (int u = 0; u < R; ++u)
+#pragma unroll
+          for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+            for (int j = 0; j < CG; ++j) {
+              const float p = chunk_dot_reg<WT>(c[u][mt][j], fs[u][mt][j], xr.v[j0 + j], xr.bsum[j0 + j]);
+              part[u][mt] += (tid + K2_THREADS * (j0 + j) < nch) ? p : 0.f;
+            }
+      }
+      const int buf = round & 1;
+#pragma unroll
+      for (int u = 0; u < R; ++u)
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt) {
+          const float v = wave_sum(part[u][mt]);
+          if (lane == 0) red[buf][w][u * NMAT + mt] = v;
         }
+      __syncthreads();
+      if (w == 0) {
+        // lane u < R: row u of the round (my_row)
+        const int u = min(lane, R - 1);
+        float z[NMAT];
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt) {
+          float zz = 0.f;
+#pragma unroll
+          for (int v = 0; v < K2_WAVES; ++v) zz += red[buf][v][u * NMAT + mt];
+          z[mt] = zz;
+        }
+        const float h = act_h<ACT>(z[0], bb, z[NMAT - 1]);
+        const bool put = lane < R && a0 + lane < n && h != 0.f;
+        const uint64_t hb = __ballot(put);
+        if (put) {
+          const int pos = nz + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(hb >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)hb, 0u));
+          pair_id[(size_t)b * cap + pos] = my_row;
+          pair_h[(size_t)b * cap + pos] = h;
+        }
+        nz += __popcll(hb);
       }
     }
   }
-  if (cnt_blk) {
-    // cnt_blk[block]: active neurons; cnt_blk[nb + block]: those with h != 0
-    __shared__ int nz_w[K2_WAVES];
-    if (lane == 0) nz_w[w] = nz;
-    __syncthreads();
-    if (tid == 0) {
-      cnt_blk[blockIdx.x] = block_count;
-      int tot = 0;
-#pragma unroll
-      for (int v = 0; v < K2_WAVES; ++v) tot += nz_w[v];
-      cnt_blk[nb + blockIdx.x] = tot;
-    }
+  if (tid == 0 && cnt_blk) {
+    cnt_blk[b] = n;
+    cnt_blk[nb + b] = nz;
   }
 }
 
@@ -738,6 +853,11 @@ k_up_list(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc,
   if ((int)blockIdx.x * W >= cnt) return;
   if constexpr (WT == DT_Q4) {
     for (int k = tid; k < d; k += blockDim.x) xs[q4t_pos(k, d)] = x[k];
+    for (int qb = tid; qb < d / 32; qb += blockDim.x) {
+      float sum = 0.f;
+      for (int j = 0; j < 32; ++j) sum += x[32 * qb + j];
+      xs[d + qb] = sum;
+    }
   } else {
     stage_f32<8>(xs, x, d, tid, blockDim.x);
   }
@@ -759,28 +879,31 @@ k_up_list(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc,
 }
 
 // ----------------------------------------------------------------------- K3
-// Down projection y = sum over active neurons i of h_i * downT[i].
+// Down projection y = sum over listed neurons i of h_i * downT[i].
 // Block (t, nc): column tile t (TWC 16-byte chunks = TWC*EPL columns) and
 // neuron split nc of NC.  With the XCD-aware order, the blocks that the
 // hardware places on one XCD (block ids congruent mod 8) own adjacent tiles,
 // so the tiles that share a 128-byte line of a row share that XCD's L2.
-// Each wave builds, in LDS, the list of neurons that its share of the mask
-// marks (16-neuron groups g = nc*8 + w + S*k, S = 8*NC; the mask marks active
-// neurons with h != 0) or of an explicit list (entries with h != 0),
-// then gathers the tile's segments of those rows, RPW = 64 / TWC rows per
-// wave-wide load and K3_LOADS loads per HBM round trip, accumulating in fp32
-// in list order.  Lanes of one chunk column are summed with a transposed
-// butterfly, the block's waves in a fixed order, and the tile's partial sums
-// are written to y_part[nc][cols] with plain stores.
+// Each wave copies its share of the (neuron, h) entries into LDS -- in the
+// stack, the per-block lists of the score kernel (wave s of S = 8*NC takes
+// the lists of score blocks s, s + S, ...; a wave prefix sum of their counts
+// places them); for pi_sparse_ffn, the caller's list with its h values
+// (entries s, s + S, ... with h != 0) -- then gathers the tile's segments of
+// those rows, RPW = 64 / TWC rows per wave-wide load and K3_LOADS loads per
+// HBM round trip, accumulating in fp32 in list order.  The lanes of one chunk
+// column are summed inside each 16-lane row, then the rows of all waves in a
+// fixed order, and the tile's partial sums are written to y_part[nc][cols]
+// with plain stores.
 constexpr int K3_WAVES = 8;
-constexpr int K3_CAP = 2048;     // list entries per wave
+constexpr int K3_CAP = 1024;     // list entries per wave held at once
 constexpr int K3_LOADS = 16;     // row segments per lane per HBM round trip (8 for Q4_0, whose
                                  // 32 values per segment need more registers to decode)
+constexpr int K3_MAXLISTS = 64;  // score-block lists per wave (one per lane)
 
 template <int WT, int TWC, bool EXPLICIT>
 __global__ void __launch_bounds__(512)
 k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int f, int d, int CT, int NC,
-       int xcd_order, const uint8_t* __restrict__ mask, const float* __restrict__ h_full,
+       int xcd_order, const int32_t* __restrict__ pair_id, const float* __restrict__ pair_h, int cap,
        const int32_t* __restrict__ idx, const int32_t* __restrict__ count, const float* __restrict__ h_list,
        const float* __restrict__ b_down, float* __restrict__ y_part, const int32_t* __restrict__ cnt_blk,
        int n_cnt_blk, int32_t* __restrict__ count_out, int32_t* __restrict__ count_out2,
@@ -788,10 +911,12 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
   constexpr int EPL = Tr<WT>::EPL;
   constexpr int RPW = WAVE / TWC;                 // rows per wave-wide load
   constexpr int TCOL = TWC * EPL;                 // columns per tile
-  constexpr int HC = EXPLICIT ? K3_CAP : 1;
-  __shared__ int l_id[K3_WAVES][K3_CAP];
-  __shared__ float l_h[K3_WAVES][HC];
-  __shared__ float red[K3_WAVES][TCOL];
+  // the waves' lists; after the gathers, the same memory holds the row sums
+  // of every wave [K3_WAVES][4 rows][TCOL]
+  static_assert(sizeof(float) * K3_WAVES * 4 * TCOL <= sizeof(int) * K3_WAVES * K3_CAP, "row sums fit the lists");
+  __shared__ __attribute__((aligned(16))) int l_id[K3_WAVES][K3_CAP];
+  __shared__ float l_h[K3_WAVES][K3_CAP];
+  __shared__ int l_pre[K3_WAVES][K3_MAXLISTS];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int nblk = CT * NC;
   int L = blockIdx.x;
@@ -802,7 +927,7 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
   const int col = tile * TCOL + q * EPL;
   const int colc = min(col, d - EPL);             // lanes past d read a valid chunk, unused
 
-  // block 0 also adds up the predictor kernel's per-block counts: active
+  // block 0 also adds up the score kernel's per-block counts: active
   // neurons in cnt_blk[0, n), those with h != 0 in cnt_blk[n, 2n)
   __shared__ int cnt_red[2][K3_WAVES];
   const bool do_cnt = blockIdx.x == 0 && (count_out || count_out2 || nz_out);
@@ -832,8 +957,7 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
       const int row = l_id[w][ec];
       c[k] = ld_chunk<WT>(downT, (size_t)row, d, colc);
       sc[k] = (WT == DT_Q4) ? ld_scale(down_sc, (size_t)row, d, colc) : 1.f;
-      if constexpr (EXPLICIT) hv[k] = l_h[w][ec];
-      else hv[k] = h_full[row];
+      hv[k] = l_h[w][ec];
     }
     PI_ISSUE_FENCE();
 #pragma unroll
@@ -851,31 +975,47 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
   };
 
   if constexpr (!EXPLICIT) {
-    // Each lane turns its 16 mask bytes (0 or 1) into 16 bits; a wave prefix
-    // sum of the bit counts places every lane's active neurons in the list.
-    const int ngrp = (f + 15) / 16;                // 16-neuron mask groups (the buffer is padded)
-    auto bits4 = [](uint32_t x) __attribute__((always_inline)) { return ((x & 0x01010101u) * 0x01020408u) >> 24; };
-    auto grp_of = [&](int r) __attribute__((always_inline)) { return s + S * (lane + WAVE * r); };
-    // one 16-byte group per lane per round; the next round's group is loaded
-    // while this one is scanned
-    uint4 nxt = reinterpret_cast<const uint4*>(mask)[min(grp_of(0), ngrp - 1)];
-    for (int r = 0; s + S * WAVE * r < ngrp; ++r) {
-      const uint4 cur = nxt;
-      if (s + S * WAVE * (r + 1) < ngrp) nxt = reinterpret_cast<const uint4*>(mask)[min(grp_of(r + 1), ngrp - 1)];
-      if (n > K3_CAP - 16 * WAVE) flush();
-      const int grp = grp_of(r);
-      uint32_t bits = bits4(cur.x) | (bits4(cur.y) << 4) | (bits4(cur.z) << 8) | (bits4(cur.w) << 12);
-      if (grp >= ngrp) bits = 0;
-      else if (grp * 16 + 16 > f) bits &= (1u << (f - grp * 16)) - 1u;
-      const int c = __popc(bits);
-      const int incl = wave_scan(c);
-      int pos = n + incl - c;
-      while (bits) {
-        const int b = __ffs(bits) - 1;
-        bits &= bits - 1;
-        l_id[w][pos++] = grp * 16 + b;
+    // the counts of this wave's score-block lists (block s + S i in lane i),
+    // their exclusive prefix sums in LDS, and the wave's total
+    const int nlw = n_cnt_blk > s ? (n_cnt_blk - 1 - s) / S + 1 : 0;     // <= K3_MAXLISTS
+    const int cl = lane < nlw ? cnt_blk[n_cnt_blk + s + S * lane] : 0;
+    const int incl = wave_scan(cl);
+    l_pre[w][lane] = incl - cl;
+    const int ntot = lane_i(incl, WAVE - 1);
+    // entries e0 .. e0 + K3_CAP at a time; entry e is in the list i whose
+    // prefix bounds it (a search over the nlw prefixes), at offset e - pre[i]
+    for (int e0 = 0; e0 < ntot; e0 += K3_CAP) {
+      const int ne = min(K3_CAP, ntot - e0);
+      for (int k0 = 0; k0 < ne; k0 += 4 * WAVE) {
+        size_t slot[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int e = e0 + min(k0 + k * WAVE + lane, ne - 1);
+          int lo = 0;
+#pragma unroll
+          for (int step = K3_MAXLISTS / 2; step >= 1; step >>= 1)
+            if (lo + step < nlw && l_pre[w][min(lo + step, K3_MAXLISTS - 1)] <= e) lo += step;
+          slot[k] = (size_t)(s + S * lo) * cap + (e - l_pre[w][lo]);
+        }
+        int id4[4];
+        float h4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          id4[k] = pair_id[slot[k]];
+          h4[k] = pair_h[slot[k]];
+        }
+        PI_ISSUE_FENCE();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int e = k0 + k * WAVE + lane;
+          if (e < ne) {
+            l_id[w][e] = id4[k];
+            l_h[w][e] = h4[k];
+          }
+        }
       }
-      n += lane_i(incl, WAVE - 1);
+      n = ne;
+      flush();
     }
   } else {
     const int cnt = min(max(*count, 0), f);
@@ -895,19 +1035,24 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
       }
       n += __popcll(bal);
     }
+    if (n > 0) flush();
   }
-  if (n > 0) flush();
   if constexpr (WT == DT_Q4) {
 #pragma unroll
     for (int j = 0; j < EPL; ++j) acc[j] = fmaf(-8.f, hsum, acc[j]);
   }
 
-  // Sum the RPW row lanes of each chunk column: lanes with equal lane % TWC
-  // hold the same columns; lane q < TWC writes the wave's sums for chunk q.
+  // Sum the row lanes of each chunk column (lanes with equal lane % TWC hold
+  // the same columns) inside each 16-lane row; the last TWC lanes of each row
+  // then write their sums, and the block adds the 4 rows of its 8 waves.
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const float v = group_sum<TWC>(acc[j], lane);
-    if (lane < TWC) red[w][lane * EPL + j] = v;
+  for (int j = 0; j < EPL; ++j) acc[j] = row_group_sum<TWC>(acc[j]);
+  __syncthreads();                                // every wave is done with its list
+  float* rsum = reinterpret_cast<float*>(&l_id[0][0]);   // [K3_WAVES][4][TCOL]
+  if ((lane & 15) >= 16 - TWC) {
+    float* dst = rsum + ((size_t)w * 4 + lane / 16) * TCOL + (lane % TWC) * EPL;
+#pragma unroll
+    for (int j = 0; j < EPL; j += 4) *reinterpret_cast<float4*>(dst + j) = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
   }
   if (do_cnt) {
     cpart = wave_sum(cpart);
@@ -933,7 +1078,7 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
     if (cg >= d) continue;
     float v = 0.f;
 #pragma unroll
-    for (int i = 0; i < K3_WAVES; ++i) v += red[i][cc];
+    for (int i = 0; i < K3_WAVES * 4; ++i) v += rsum[(size_t)i * TCOL + cc];
     if (b_down && nc == 0) v += b_down[cg];
     y_part[(size_t)nc * d + cg] = v;
   }

@@ -29,7 +29,8 @@
  *    16-byte aligned, Q4_0 scales 4-byte aligned; 1 <= batch <= 32;
  *    act REGLU needs `gate`; predictor dtype F32 or F16 (Q4_0 predictor:
  *    PI_EUNSUPPORTED); d <= 16384 and rank <= 4096 (vectors are staged whole
- *    in LDS; larger: PI_EUNSUPPORTED); the FFN at batch > 1 needs
+ *    in LDS; larger: PI_EUNSUPPORTED); ffn <= 2^21 (the score kernel keeps
+ *    each wave's active neurons in LDS) and, for the FFN at batch > 1,
  *    ffn <= 65536 (PI_EUNSUPPORTED otherwise); every layer of a stack has the
  *    same d.
  *  - Calls on distinct workspaces are independent; calls sharing a workspace
@@ -185,12 +186,12 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
  * first call with that device current).
  * Returns PI_EWORKSPACE, before any HIP call, when
  * pi_workspace_bytes(layers, n_layers, batch) exceeds PI_STATIC_WORKSPACE_BYTES
- * (64 MiB covers every batch 1..32 at the largest accepted width, rank and
- * batched ffn).  Every call on one GPU shares that GPU's array: calls that
+ * (48 MiB covers batch 1 at every accepted shape and batch 2..32 up to
+ * d = 12288 with ffn = 49152 and rank = 1024).  Every call on one GPU shares that GPU's array: calls that
  * overlap on one GPU (other streams, other threads) race and give undefined
  * results; calls ordered on one stream are independent.
  */
-#define PI_STATIC_WORKSPACE_BYTES (64u << 20)
+#define PI_STATIC_WORKSPACE_BYTES (48u << 20)
 pi_status pi_ffn_stack_static(const pi_layer* layers, int32_t n_layers, const float* x, int32_t batch,
                               float* out, int32_t* counts, int32_t* nz_counts, const pi_trace* trace,
                               void* stream);

@@ -93,6 +93,7 @@ def test_workspace_bytes(pi):
     (dict(pbias=FAKE + 4), 1),
     (dict(w_dtype=2), 1),                              # Q4_0 without scales
     (dict(d=16384 + 64), 2), (dict(rank=4096 + 64), 2),  # beyond the LDS staging limits
+    (dict(ffn=(1 << 21) + 1), 2),                      # beyond the score kernel's LDS lists
 ])
 def test_predict_rejects_bad_layers(pi, kw, status):
     assert predict(pi, make_layer(pi, **kw)) == status
@@ -188,11 +189,13 @@ def test_static_stack_checks_come_before_any_hip_call(pi):
                                    None) == 1
     assert lib.pi_ffn_stack_static(ctypes.cast(one, ctypes.c_void_p), 1, FAKE, 33, FAKE, None, None, None,
                                    None) == 1
-    big = make_layer(pi, ffn=16 << 20)           # ~7 bytes of workspace per neuron: > 64 MiB
-    assert ws_bytes(pi, big) > pi.STATIC_WORKSPACE_BYTES
+    big = make_layer(pi, d=16384, rank=4096, ffn=65536)   # the largest batched shape
+    assert ws_bytes(pi, big, batch=32) > pi.STATIC_WORKSPACE_BYTES
     arr = (pi.PiLayer * 1)(big)
-    assert lib.pi_ffn_stack_static(ctypes.cast(arr, ctypes.c_void_p), 1, FAKE, 1, FAKE, None, None, None,
+    assert lib.pi_ffn_stack_static(ctypes.cast(arr, ctypes.c_void_p), 1, FAKE, 32, FAKE, None, None, None,
                                    None) == 3
+    # batch 1 at the largest accepted ffn fits
+    assert 0 < ws_bytes(pi, make_layer(pi, d=16384, rank=4096, ffn=1 << 21)) <= pi.STATIC_WORKSPACE_BYTES
 
 
 def test_static_workspace_size_matches_the_header(pi):
