@@ -71,7 +71,8 @@ struct Dims {
   int d = 0, fmax = 0, rmax = 0;
 };
 
-constexpr int kMaxParts = 4;       // neuron splits of the down projection (partial y vectors)
+constexpr int kMaxParts = 8;       // neuron splits of the down projection (partial y vectors)
+constexpr int kK1MaxSplit = 4;     // column slices of the predictor's first product
 constexpr int kK2Grid = 512;   // two per compute unit of an MI355X
 
 int epl_of(int dt) { return dt == PI_F32 ? 4 : (dt == PI_F16 ? 8 : 32); }
@@ -87,7 +88,7 @@ size_t k2_pairs_max(int ffn) { return (size_t)k2_blocks_for(ffn) * k2_cap(ffn); 
 int bscore_blocks(int ffn) { return cdiv(ffn, pib::BM); }
 
 struct WsLayout {
-  size_t t, xbuf, ybuf, mask, pmask, h, pid, ph, cnt, misc;
+  size_t t, v, xbuf, ybuf, mask, pmask, h, pid, ph, cnt, misc;
   // batched path (batch > 1)
   size_t xh, xl, tpart, th, tl, mnm, ulist, hh, hl;
   size_t total;
@@ -103,7 +104,8 @@ WsLayout layout(const Dims& D, int batch) {
   const size_t fpad = (size_t)cdiv(D.fmax, 16) * 16;
   w.xs = align_up(sizeof(float) * (size_t)D.d * batch);
   w.ys = align_up(sizeof(float) * (size_t)D.d * (batch > 1 ? pib::BD_SPLIT * kBatchM : kMaxParts));
-  w.t = o;    o += align_up(sizeof(float) * (size_t)D.rmax * batch);
+  w.t = o;    o += align_up(sizeof(float) * (size_t)D.rmax * std::max(batch, kK1MaxSplit));
+  w.v = o;    o += align_up(sizeof(float) * ((size_t)D.d + kK1MaxSplit));   // v, then its slices' sums of squares
   w.xbuf = o; o += w.xs * 2;
   w.ybuf = o; o += w.ys * 2;
   w.mask = o; o += align_up(fpad);                       // one byte per neuron (the union when batch > 1)
@@ -132,6 +134,7 @@ WsLayout layout(const Dims& D, int batch) {
 
 struct Ws {
   float* t;
+  float* v;
   float* x[2];
   float* y[2];
   uint8_t* mask;
@@ -151,6 +154,7 @@ Ws carve(void* base, const WsLayout& L) {
   char* b = static_cast<char*>(base);
   Ws w{};
   w.t = reinterpret_cast<float*>(b + L.t);
+  w.v = reinterpret_cast<float*>(b + L.v);
   w.x[0] = reinterpret_cast<float*>(b + L.xbuf);
   w.x[1] = reinterpret_cast<float*>(b + L.xbuf + L.xs);
   w.y[0] = reinterpret_cast<float*>(b + L.ybuf);
@@ -204,9 +208,16 @@ int pick(const int (&opts)[K], int n) {
   return opts[K - 1];
 }
 
-// K1: one wave per row of A.
-constexpr int kK1Nch[] = {2, 4, 8, 16, 24};
-int k1_blocks(int r) { return std::max(1, cdiv(r, K1_WAVES)); }
+// K1: one wave per row of A and column slice; the slices multiply the blocks
+// of a small rank up to about 256 (at most 4 slices, and no more than the
+// score kernel's LDS copies of t allow).
+constexpr int kK1Nch[] = {2, 4, 8, 12, 16, 24};
+int k1_split(int r) {
+  int ks = 1;
+  while (ks < kK1MaxSplit && cdiv(r, K1_WAVES) * ks * 2 <= 256 && ks * 2 * dma_pad(r) <= 16384) ks *= 2;
+  return ks;
+}
+int k1_blocks(int r) { return std::max(1, cdiv(r, K1_WAVES)) * k1_split(r); }
 
 // K2: chunks per lane per row of B held at once (1 or 2)
 int k2_pch_of(int rank, int p_dtype) { return chunks_of(rank, p_dtype) <= 1 ? 1 : 2; }
@@ -225,48 +236,55 @@ int k2_blocks(const pi_layer* L) { return k2_blocks_for(L->ffn); }
 // K3: tiles of TWC = 4 chunks per row (64-byte row segments: one request per
 // row and tile, half an L2 line, the other half read by the neighbouring tile
 // on the same XCD), 8 chunks (a whole 128-byte line) for rows of 768 chunks
-// or more (measured on MI355X: 15% faster at d = 8192 fp16, 23% at d = 7168,
-// 12% slower at d = 4096), fewer when the row is short, and NC neuron splits
-// so that the grid has at most 256 blocks of 8 waves (one round on the CUs).
-// Wider tiles scan the mask fewer times per row but give fewer blocks;
-// narrower ones multiply the L2 requests per byte.
+// or more, and for Q4_0 rows of 384 chunks or more (measured on MI355X: 15%
+// faster at d = 8192 fp16, 23% at d = 7168, 24% at d = 12288 Q4_0, 12% slower
+// at d = 4096 fp16), fewer when the row is short, and NC neuron splits so that
+// the grid has at most 256 blocks of 8 waves (one round on the CUs).  Wider
+// tiles scan the mask fewer times per row but give fewer blocks; narrower ones
+// multiply the DRAM requests per byte.
 struct K3Shape {
   int twc, ct, nc;
 };
 K3Shape k3_shape(int d, int dt) {
   const int nchunks = d / epl_of(dt);
   K3Shape s;
-  s.twc = nchunks >= 768 ? 8 : nchunks >= 64 ? 4 : nchunks >= 32 ? 2 : 1;
+  const bool wide = nchunks >= 768 || (dt == PI_Q4_0 && nchunks >= 384);
+  s.twc = wide ? 8 : nchunks >= 64 ? 4 : nchunks >= 32 ? 2 : 1;
   s.ct = cdiv(nchunks, s.twc);
-  // the next layer's predictor kernel stages x and the NC partials in LDS
-  const int lds_parts = 147456 / (4 * dma_pad(d)) - 1;
-  s.nc = std::max(1, std::min(std::min(kMaxParts, lds_parts), std::max(1, 256 / s.ct)));
+  s.nc = std::max(1, std::min(kMaxParts, 256 / s.ct));
   return s;
 }
+
+// The next layer's predictor kernel stages its column slice of x and of up to
+// k1_slots(n) partial y vectors (n floats each) in LDS at once (144 KiB of
+// it), the rest in later rounds.
+int k1_slots(int n) { return std::max(1, 147456 / (4 * dma_pad(n)) - 1); }
 
 // ---------------------------------------------------------------- dispatch
 struct K1Args {
   const float* x_prev;
-  const float* y_prev;
+  const float* y_prev;   // y_np partial vectors, or NULL (no glue)
   int y_np;
-  float* x_out;
-  float* x_trace;
-  float* t;
+  float* v;              // v = x_prev + y_prev [d], then the slices' sums of squares [k1_split]
+  float* t_part;         // [k1_split][rank]
 };
 
 template <int PT, int NCH>
 void launch_k1_t(const pi_layer* L, const K1Args& a, hipStream_t st) {
+  const int ks = k1_split(L->rank), ds = L->d / ks;
+  const int slots = std::max(1, std::min(a.y_np, k1_slots(ds)));
   hipLaunchKernelGGL((k_predict_t<PT, NCH>), dim3(k1_blocks(L->rank)), dim3(K1_WAVES * WAVE),
-                     sizeof(float) * (size_t)dma_pad(L->d) * (1 + a.y_np), st, L->A, L->rank, L->d, a.x_prev, a.y_prev, a.y_np, a.x_out,
-                     a.x_trace, a.t);
+                     sizeof(float) * (size_t)dma_pad(ds) * (1 + (a.y_np > 0 ? slots : 0)), st, L->A, L->rank, L->d,
+                     ks, a.x_prev, a.y_prev, a.y_np, slots, a.v, a.v + L->d, a.t_part);
 }
 
 template <int PT>
 void launch_k1_p(const pi_layer* L, const K1Args& a, hipStream_t st) {
-  switch (pick(kK1Nch, chunks_of(L->d, L->p_dtype))) {
+  switch (pick(kK1Nch, chunks_of(L->d / k1_split(L->rank), L->p_dtype))) {
     case 2: return launch_k1_t<PT, 2>(L, a, st);
     case 4: return launch_k1_t<PT, 4>(L, a, st);
     case 8: return launch_k1_t<PT, 8>(L, a, st);
+    case 12: return launch_k1_t<PT, 12>(L, a, st);
     case 16: return launch_k1_t<PT, 16>(L, a, st);
     default: return launch_k1_t<PT, 24>(L, a, st);
   }
@@ -280,8 +298,11 @@ void k1(const pi_layer* L, const K1Args& a, hipStream_t st) {
 }
 
 struct K2Args {
-  const float* t;
-  const float* xcur;   // x' (the fused gathers)
+  const float* t_part; // the predictor kernel's slices of t [k1_split][rank]
+  const float* ss;     // their sums of squares of v, or NULL (no glue: x' = v)
+  const float* v;      // v (the fused gathers take x' = v inv)
+  float* x_out;        // x', or NULL
+  float* x_trace;
   float* scores;
   uint8_t* pmask;      // the predictor's mask byte per neuron, or NULL
   int32_t* cnt;        // [2 * blocks]: active neurons, then those with h != 0
@@ -292,10 +313,12 @@ struct K2Args {
 template <int PT, int WT, int ACT, bool FUSE, int PCH, int CPL>
 void launch_k2_t(const pi_layer* L, const K2Args& a, hipStream_t st) {
   const int nb = k2_blocks(L);
-  const size_t lds = sizeof(float) * (size_t)K2_WAVES * (dma_pad(L->rank) + cdiv(L->ffn, nb * K2_WAVES));
+  const int ks = k1_split(L->rank);
+  const size_t lds = sizeof(float) * ((size_t)ks * dma_pad(L->rank) + (size_t)K2_WAVES * cdiv(L->ffn, nb * K2_WAVES));
   hipLaunchKernelGGL((k_score<PT, WT, ACT, FUSE, PCH, CPL>), dim3(nb), dim3(K2_THREADS), lds, st,
-                     L->B, L->pbias ? L->pbias : L->bias, L->bias, a.t, L->ffn, L->rank, L->gate.w, L->gate.scale,
-                     L->up.w, L->up.scale, a.xcur, L->d, a.scores, a.pmask, a.cnt, a.pid, a.ph, k2_cap(L->ffn));
+                     L->B, L->pbias ? L->pbias : L->bias, L->bias, a.t_part, ks, a.ss, L->ffn, L->rank, L->gate.w,
+                     L->gate.scale, L->up.w, L->up.scale, a.v, L->d, a.x_out, a.x_trace, a.scores, a.pmask, a.cnt,
+                     a.pid, a.ph, k2_cap(L->ffn));
 }
 
 template <int PT, int WT, int ACT, int PCH>
@@ -608,13 +631,14 @@ pi_status run_stack(const pi_layer* layers, int32_t n_layers, const float* x, in
     const pi_trace* tr = trace ? &trace[l] : nullptr;
     const int cur = l & 1, prv = cur ^ 1;
     mark(tr, 0, st);
-    k1(L, K1Args{l == 0 ? x : W.x[prv], l == 0 ? nullptr : W.y[prv], np_prev, W.x[cur], tr ? tr->x_in : nullptr,
-                 W.t}, st);
+    const bool glue = l > 0;
+    k1(L, K1Args{glue ? W.x[prv] : x, glue ? W.y[prv] : nullptr, glue ? np_prev : 0, W.v, W.t}, st);
     mark(tr, 1, st);
     // the predictor's own mask goes to the record, or to W.pmask when only the
     // record's list asks for it
     uint8_t* pmask = tr ? (tr->mask ? tr->mask : (tr->idx ? W.pmask : nullptr)) : nullptr;
-    k2(L, true, K2Args{W.t, W.x[cur], tr ? tr->scores : nullptr, pmask, W.cnt, W.pid, W.ph}, st);
+    k2(L, true, K2Args{W.t, glue ? W.v + L->d : nullptr, glue ? W.v : x, W.x[cur], tr ? tr->x_in : nullptr,
+                       tr ? tr->scores : nullptr, pmask, W.cnt, W.pid, W.ph}, st);
     mark(tr, 2, st);
     int32_t* c1 = counts ? counts + l : nullptr;
     int32_t* c2 = (tr && tr->count && !tr->idx) ? tr->count : nullptr;
@@ -719,9 +743,9 @@ pi_status pi_predict(const pi_layer* layer, const float* x, int32_t batch, float
     b_predict(layer, batch, W, scores, mask, idx, count, nullptr, nullptr, st);
     return launch_status();
   }
-  k1(layer, K1Args{x, nullptr, 0, nullptr, nullptr, W.t}, st);
+  k1(layer, K1Args{x, nullptr, 0, W.v, W.t}, st);
   uint8_t* pm = mask ? mask : W.mask;
-  k2(layer, false, K2Args{W.t, nullptr, scores, pm, nullptr, nullptr, nullptr}, st);
+  k2(layer, false, K2Args{W.t, nullptr, nullptr, nullptr, nullptr, scores, pm, nullptr, nullptr, nullptr}, st);
   hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, pm, layer->ffn, idx, count, nullptr, nullptr);
   return launch_status();
 }

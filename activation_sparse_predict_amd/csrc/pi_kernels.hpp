@@ -322,53 +322,34 @@ __device__ __forceinline__ void dma_f32(float* lds, const float* g, int n, int w
         (__attribute__((address_space(3))) void*)(lds + c * 256), 16, 0, 0);
 }
 
-// v = x + sum_{p < np} y[p] (np <= 4 partial vectors of n floats, added in the
+// v = x + sum_{p < np} y[p] (np partial vectors of n floats, added in the
 // order p = 0, 1, ...) into LDS, returning this thread's sum of v^2 over its
-// elements in a fixed order (the same in every block).  np == 0: v = x.
-template <int MAXV>
+// elements in a fixed order.  np == 0: v = x.
 __device__ __forceinline__ float stage_residual(float* __restrict__ lds, const float* __restrict__ x,
                                                 const float* __restrict__ y, int np, int n, int tid, int nthr) {
   const int nv = n / 4;
   float ss = 0.f;
-  for (int base = 0; base < nv; base += MAXV * nthr) {
-    float4 xv[MAXV], yv[4][MAXV];
-#pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-      const int k = min(base + j * nthr + tid, nv - 1);
-      xv[j] = reinterpret_cast<const float4*>(x)[k];
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        if (p < np) yv[p][j] = reinterpret_cast<const float4*>(y + (size_t)p * n)[k];
-    }
-    PI_ISSUE_FENCE();
-#pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-      const int kr = base + j * nthr + tid;
-      float4 v = xv[j];
-      if (np > 0) {
-        float4 y4 = yv[0][j];
-#pragma unroll
-        for (int p = 1; p < 4; ++p) {
-          if (p < np) {
-            y4.x += yv[p][j].x;
-            y4.y += yv[p][j].y;
-            y4.z += yv[p][j].z;
-            y4.w += yv[p][j].w;
-          }
-        }
-        v.x += y4.x;
-        v.y += y4.y;
-        v.z += y4.z;
-        v.w += y4.w;
+  for (int k = tid; k < nv; k += nthr) {
+    float4 v = reinterpret_cast<const float4*>(x)[k];
+    if (np > 0) {
+      float4 y4 = reinterpret_cast<const float4*>(y)[k];
+      for (int p = 1; p < np; ++p) {
+        const float4 u = reinterpret_cast<const float4*>(y + (size_t)p * n)[k];
+        y4.x += u.x;
+        y4.y += u.y;
+        y4.z += u.z;
+        y4.w += u.w;
       }
-      reinterpret_cast<float4*>(lds)[min(kr, nv - 1)] = v;
-      if (kr < nv) {
-        ss = fmaf(v.x, v.x, ss);
-        ss = fmaf(v.y, v.y, ss);
-        ss = fmaf(v.z, v.z, ss);
-        ss = fmaf(v.w, v.w, ss);
-      }
+      v.x += y4.x;
+      v.y += y4.y;
+      v.z += y4.z;
+      v.w += y4.w;
     }
+    reinterpret_cast<float4*>(lds)[k] = v;
+    ss = fmaf(v.x, v.x, ss);
+    ss = fmaf(v.y, v.y, ss);
+    ss = fmaf(v.z, v.z, ss);
+    ss = fmaf(v.w, v.w, ss);
   }
   return ss;
 }
@@ -425,131 +406,165 @@ __device__ __forceinline__ void gather_rows(const void* __restrict__ w0, const u
 }
 
 // ----------------------------------------------------------------------- K1
-// t = A x', x' = glue(x_prev, y_prev) if y_np > 0 else x_prev, with glue
-// v = x_prev + y_prev, x' = v / sqrt(mean(v^2) + 1e-6) and y_prev given as y_np
-// partial vectors that are added in order.  One wave per row of A.  x_prev
-// and the partials go to LDS by LDS-DMA first; the row of A (NCH chunks per
-// lane per round) is issued after them, its addresses depending on an opaque
-// zero, so the glue waits only for the copies and runs while the row is in
-// flight.  The dot product takes v and the row's result is scaled by
-// 1 / sqrt(mean(v^2) + 1e-6).  Every block computes the same v and scale with
-// the same operation order, so all agree bit for bit; each block writes its
-// slice of x'.
-// Eight waves per block halve the blocks that repeat the glue (MI355X: 5%
-// faster at d = 8192 and 12288, neutral at 4096).
+// The predictor's first product in KS column slices: t_part[k][row] =
+// A[row, slice k] . v[slice k], where v = x_prev + y_prev (the residual sum,
+// y_prev given as y_np partial vectors added in order) or v = x_prev when
+// y_np == 0.  The glue's normalisation x' = v / sqrt(mean(v^2) + 1e-6) is a
+// scalar factor, so it is applied by the score kernel to the sum of the
+// slices' products; here the blocks of group 0 write v and their slice's
+// sum of squares ss[k] for it.
+// Block b takes slice k = b % KS and rows 8 (b / KS) + w, one wave per row.
+// The slice of x_prev and the first `slots` partials go to LDS by LDS-DMA
+// first; the row segment of A (NCH chunks per lane per round) is issued after
+// them, its addresses depending on an opaque zero, so the residual sum waits
+// only for the copies and runs while the row is in flight.  Further partials
+// (when LDS holds fewer than y_np) are copied into the same slots a round at a
+// time.  Each thread adds the partials of its elements in registers
+// (y = ((y_0 + y_1) + y_2) + ...), then v = x_prev + y.  Every block of a slice
+// computes the same v with the same operation order.
+// The column split doubles (or quadruples) the blocks of a small rank, so the
+// read of A covers the whole chip, and divides the LDS a block stages.
 constexpr int K1_WAVES = 8;
+constexpr int K1_THREADS = K1_WAVES * WAVE;
+constexpr int K1_MAXV = 8;           // float4 elements of a slice per thread (d / KS <= 16384)
 
 template <int PT, int NCH>
-__global__ void __launch_bounds__(K1_WAVES * WAVE)
-k_predict_t(const void* __restrict__ A, int r, int d, const float* __restrict__ x_prev,
-            const float* __restrict__ y_prev, int y_np, float* __restrict__ x_out, float* __restrict__ x_trace,
-            float* __restrict__ t) {
+__global__ void __launch_bounds__(K1_THREADS)
+k_predict_t(const void* __restrict__ A, int r, int d, int KS, const float* __restrict__ x_prev,
+            const float* __restrict__ y_prev, int y_np, int slots, float* __restrict__ v_out,
+            float* __restrict__ ss_out, float* __restrict__ t_part) {
   extern __shared__ float smem[];
   __shared__ float red[K1_WAVES];
   constexpr int EPL = Tr<PT>::EPL, TW = WAVE * EPL;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  const int row = blockIdx.x * K1_WAVES + w;
+  const int ks = blockIdx.x % KS, grp = blockIdx.x / KS;
+  const int row = grp * K1_WAVES + w;
   const size_t rowc = (size_t)min(row, r - 1);       // a wave without a row reads row r-1 and discards it
-  const int nch = (d + TW - 1) / TW;
-  const int dp = dma_pad(d);
+  const int ds = d / KS, off = ks * ds;               // this block's columns [off, off + ds)
+  const int nch = (ds + TW - 1) / TW;
+  const int dp = dma_pad(ds);
   float* xs = smem;                                   // x_prev, then v [dp]
-  float* ys = smem + dp;                              // the y partials [y_np][dp]
+  float* ys = smem + dp;                              // the y partials of a round [slots][dp]
 
-  dma_f32(xs, x_prev, d, w, K1_WAVES, lane);
-  for (int p = 0; p < y_np; ++p) dma_f32(ys + (size_t)p * dp, y_prev + (size_t)p * d, d, w, K1_WAVES, lane);
+  dma_f32(xs, x_prev + off, ds, w, K1_WAVES, lane);
+  const int n0 = min(y_np, slots);
+  for (int p = 0; p < n0; ++p)
+    dma_f32(ys + (size_t)p * dp, y_prev + (size_t)p * d + off, ds, w, K1_WAVES, lane);
   const int z = opaque_zero();
   uint4 c[NCH];
 #pragma unroll
   for (int q = 0; q < NCH; ++q)
-    c[q] = ld_chunk<PT>(A, rowc + z, d, min(min(q, nch - 1) * TW + lane * EPL, d - EPL));
+    c[q] = ld_chunk<PT>(A, rowc + z, d, off + min(min(q, nch - 1) * TW + lane * EPL, ds - EPL));
   PI_ISSUE_FENCE();
   wait_vm_lds<NCH>();                                 // the copies, not the row
   __builtin_amdgcn_s_barrier();
 
-  const int nv = d / 4;
+  const int nv = ds / 4;
   if (y_np > 0) {
+    float4 y4[K1_MAXV];                               // this thread's elements k = tid + K1_THREADS j
+    for (int p0 = 0; p0 < y_np; p0 += slots) {
+      const int cnt = min(slots, y_np - p0);
+      if (p0 > 0) {                                   // this round's copies (issued behind the row)
+        wait_vm_lds<0>();
+        __builtin_amdgcn_s_barrier();
+      }
+#pragma unroll
+      for (int j = 0; j < K1_MAXV; ++j) {
+        const int k = tid + K1_THREADS * j;
+        if (k < nv) {
+          for (int q = 0; q < cnt; ++q) {
+            const float4 u = reinterpret_cast<const float4*>(ys + (size_t)q * dp)[k];
+            if (p0 + q == 0) {
+              y4[j] = u;
+            } else {
+              y4[j].x += u.x;
+              y4[j].y += u.y;
+              y4[j].z += u.z;
+              y4[j].w += u.w;
+            }
+          }
+        }
+      }
+      if (p0 + slots < y_np) {                        // the next round's partials, into the same slots
+        __syncthreads();
+        for (int q = 0; q < min(slots, y_np - p0 - slots); ++q)
+          dma_f32(ys + (size_t)q * dp, y_prev + (size_t)(p0 + slots + q) * d + off, ds, w, K1_WAVES, lane);
+      }
+    }
     float ss = 0.f;
     float4* x4 = reinterpret_cast<float4*>(xs);
-    const float4* y4p = reinterpret_cast<const float4*>(ys);
-    for (int k = tid; k < nv; k += blockDim.x) {
-      float4 y4 = y4p[k];
-      for (int p = 1; p < y_np; ++p) {
-        const float4 u = y4p[(size_t)p * (dp / 4) + k];
-        y4.x += u.x;
-        y4.y += u.y;
-        y4.z += u.z;
-        y4.w += u.w;
+#pragma unroll
+    for (int j = 0; j < K1_MAXV; ++j) {
+      const int k = tid + K1_THREADS * j;
+      if (k < nv) {
+        float4 v = x4[k];
+        v.x += y4[j].x;
+        v.y += y4[j].y;
+        v.z += y4[j].z;
+        v.w += y4[j].w;
+        x4[k] = v;
+        if (grp == 0) {
+          reinterpret_cast<float4*>(v_out + off)[k] = v;
+          ss = fmaf(v.x, v.x, ss);
+          ss = fmaf(v.y, v.y, ss);
+          ss = fmaf(v.z, v.z, ss);
+          ss = fmaf(v.w, v.w, ss);
+        }
       }
-      float4 v = x4[k];
-      v.x += y4.x;
-      v.y += y4.y;
-      v.z += y4.z;
-      v.w += y4.w;
-      x4[k] = v;
-      ss = fmaf(v.x, v.x, ss);
-      ss = fmaf(v.y, v.y, ss);
-      ss = fmaf(v.z, v.z, ss);
-      ss = fmaf(v.w, v.w, ss);
     }
-    ss = wave_sum(ss);
-    if (lane == 0) red[w] = ss;
+    if (grp == 0) {
+      ss = wave_sum(ss);
+      if (lane == 0) red[w] = ss;
+    }
   }
   __syncthreads();
-  float inv = 1.f;
-  if (y_np > 0) {
+  if (y_np > 0 && grp == 0 && tid == 0) {
     float tot = 0.f;
 #pragma unroll
     for (int i = 0; i < K1_WAVES; ++i) tot += red[i];
-    inv = 1.0f / sqrtf(tot / (float)d + 1e-6f);
-  }
-
-  {
-    const int nb = gridDim.x, b = blockIdx.x;
-    const int cx = (d + nb - 1) / nb;
-    for (int k = b * cx + tid; k < min(d, (b + 1) * cx); k += blockDim.x) {
-      const float xk = y_np > 0 ? xs[k] * inv : xs[k];
-      if (x_out) x_out[k] = xk;
-      if (x_trace) x_trace[k] = xk;
-    }
+    ss_out[ks] = tot;
   }
 
   float a = 0.f;
 #pragma unroll
   for (int q = 0; q < NCH; ++q) {
     const int e = q * TW + lane * EPL;
-    const bool ok = q < nch && e < d;
+    const bool ok = q < nch && e < ds;
     const float p = chunk_dot<PT>(c[q], 1.f, xs + (ok ? e : 0));
     a += ok ? p : 0.f;
   }
-  for (int q0 = NCH; q0 < nch; q0 += NCH) {            // rows longer than NCH chunks per lane
+  for (int q0 = NCH; q0 < nch; q0 += NCH) {            // slices longer than NCH chunks per lane
 #pragma unroll
     for (int q = 0; q < NCH; ++q)
-      c[q] = ld_chunk<PT>(A, rowc, d, min(min(q0 + q, nch - 1) * TW + lane * EPL, d - EPL));
+      c[q] = ld_chunk<PT>(A, rowc, d, off + min(min(q0 + q, nch - 1) * TW + lane * EPL, ds - EPL));
     PI_ISSUE_FENCE();
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
       const int e = (q0 + q) * TW + lane * EPL;
-      const bool ok = q0 + q < nch && e < d;
+      const bool ok = q0 + q < nch && e < ds;
       const float p = chunk_dot<PT>(c[q], 1.f, xs + (ok ? e : 0));
       a += ok ? p : 0.f;
     }
   }
   a = wave_sum(a);
-  if (row < r && lane == 0) t[row] = y_np > 0 ? a * inv : a;
+  if (row < r && lane == 0) t_part[(size_t)ks * r + row] = a;
 }
 
 // ----------------------------------------------------------------------- K2
 // Scores s_i = c_i + B[i] . t, threshold s_i > 0, and -- if FUSE -- the
 // gathered up/gate GEMV with ReLU, ReGLU or Squared ReLU for the active
-// neurons, in two phases:
+// neurons, in two phases.  t arrives as the predictor kernel's KS column-slice
+// products; with a glue, t = inv (t_0 + ... + t_{KS-1}) and x' = v inv, inv =
+// 1 / sqrt(ss / d + 1e-6) from the slices' sums of squares ss of v.
 //  1. The rows of B.  The neurons are dealt to the blocks round-robin (so the
 //     hot-first order spreads the frequently active rows evenly over the
-//     blocks); wave w of block b owns neurons b + nb (w + K2_WAVES m).  Each
-//     wave copies t into its own LDS slice by LDS-DMA ahead of its rows of B,
-//     loads RB = 16 / PCH rows (PCH 16-byte chunks per lane each) before its
-//     first multiply, and appends the active ones to its own list in LDS
-//     (ballot order: ascending within the wave).  No barrier: the waves stream
-//     B independently.
+//     blocks); wave w of block b owns neurons b + nb (w + K2_WAVES m).  The
+//     block copies the slices of t into LDS by LDS-DMA ahead of the rows of B
+//     and adds them up there (one barrier each side) while the first rows are
+//     in flight.  Each wave loads RB = 16 / PCH rows (PCH 16-byte chunks per
+//     lane each) before its first multiply, and appends the active ones to its
+//     own list in LDS (ballot order: ascending within the wave).  No further
+//     barrier: the waves stream B independently.
 //  2. The block's active list (the waves' lists one after another), R rows
 //     at a time, by all 256 lanes together: lane tid owns chunks tid + 256 j
 //     (j < CPL) of every row, and holds its x' values for those chunks in
@@ -562,6 +577,7 @@ k_predict_t(const void* __restrict__ A, int r, int d, const float* __restrict__ 
 //     the listed rows.
 // cnt_blk[block] = active neurons of the block, cnt_blk[nb + block] = those
 // with h != 0.  pmask (if given) gets the predictor's mask byte per neuron.
+// Block b also writes its slice of x' to x_out / x_trace (if given).
 constexpr int K2_WAVES = 4;
 constexpr int K2_THREADS = K2_WAVES * WAVE;
 
@@ -596,6 +612,16 @@ __device__ __forceinline__ void load_xreg(XReg<WT, CPL>& xr, const float* __rest
       xr.v[j][e + 3] = v.w;
     }
   }
+}
+
+// x' = v inv in the registers, once the values have arrived.
+template <int WT, int CPL>
+__device__ __forceinline__ void xreg_scale(XReg<WT, CPL>& xr, float inv) {
+  constexpr int EPL = Tr<WT>::EPL;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) xr.v[j][e] *= inv;
 }
 
 // The Q4_0 block sums of the chunks, once their values have arrived.
@@ -648,10 +674,10 @@ __device__ __forceinline__ float chunk_dot_reg(uint4 c, float scale, const float
 template <int PT, int WT, int ACT, bool FUSE, int PCH, int CPL>
 __global__ void __launch_bounds__(K2_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const float* __restrict__ bias,
-        const float* __restrict__ t, int f, int r,
+        const float* __restrict__ t_part, int KS, const float* __restrict__ ss_in, int f, int r,
         const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc,
         const void* __restrict__ up_w, const uint16_t* __restrict__ up_sc,
-        const float* __restrict__ xcur, int d,
+        const float* __restrict__ vx, int d, float* __restrict__ x_out, float* __restrict__ x_trace,
         float* __restrict__ scores, uint8_t* __restrict__ pmask, int32_t* __restrict__ cnt_blk,
         int32_t* __restrict__ pair_id, float* __restrict__ pair_h, int cap) {
   constexpr int RB = 16 / PCH;                               // rows of B per batch
@@ -666,8 +692,9 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
   const int M = g < f ? (f - 1 - g) / NW + 1 : 0;            // neurons of this wave
   const int Mb = b < f ? (f - 1 - b) / NW + 1 : 0;           // wave 0 has the most: block-uniform trip count
   const int Mw = (f + NW - 1) / NW;                          // list capacity per wave (= Mb of block 0)
-  float* ts = smem + w * dma_pad(r);                         // this wave's own copy of t [dma_pad(r)]
-  int* act = reinterpret_cast<int*>(smem + K2_WAVES * dma_pad(r));   // [K2_WAVES][Mw] active lists
+  const int dpr = dma_pad(r);
+  float* ts = smem;                                          // the slices of t, then t [KS][dma_pad(r)]
+  int* act = reinterpret_cast<int*>(smem + (size_t)KS * dpr);   // [K2_WAVES][Mw] active lists
   __shared__ int nact[K2_WAVES];
   __shared__ float red[2][K2_WAVES][R * NMAT];
   const int pch = (r + PTW - 1) / PTW;
@@ -692,13 +719,57 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
     PI_ISSUE_FENCE();
   };
 
-  // t goes to LDS by LDS-DMA ahead of everything else; x' for the gathers to
-  // registers next (it is needed last); the rows of B after both, their
-  // addresses depending on an opaque zero so they cannot be hoisted.
-  dma_f32(ts, t, r, 0, 1, lane);
-  XReg<WT, CPL> xr;
-  if constexpr (FUSE) load_xreg<WT, CPL>(xr, xcur, nch, tid);
+  // The slices of t go to LDS by LDS-DMA ahead of everything else; the first
+  // rows of B next, their addresses depending on an opaque zero so they
+  // cannot be hoisted; v for the gathers to registers last (it is needed
+  // last).  The glue's scale inv = 1 / sqrt(mean(v^2) + 1e-6) comes from the
+  // slices' sums of squares (inv = 1 without a glue).
+  for (int k = 0; k < KS; ++k) dma_f32(ts + (size_t)k * dpr, t_part + (size_t)k * r, r, w, K2_WAVES, lane);
+  float inv = 1.f;
+  if (ss_in) {
+    float tot = 0.f;
+    for (int k = 0; k < KS; ++k) tot += ss_in[k];
+    inv = 1.0f / sqrtf(tot / (float)d + 1e-6f);
+  }
   issue(0, 0, opaque_zero());
+  XReg<WT, CPL> xr;
+  if constexpr (FUSE) load_xreg<WT, CPL>(xr, vx, nch, tid);
+  PI_ISSUE_FENCE();
+  // this block's slice of x' = v inv [kx0, kx1) for x_out / x_trace: its first
+  // K2_THREADS elements are loaded here and stored once inv is known
+  const int cx = (d + nb - 1) / nb, kx0 = min(d, b * cx), kx1 = min(d, kx0 + cx);
+  const bool wx = x_out || x_trace;
+  float vk = 0.f;
+  if (wx && kx0 + tid < kx1) vk = vx[kx0 + tid];
+  // The copies of t have arrived once no more than the loads issued after them
+  // (the RB*PCH chunks of B, the bias, the x' chunks) are outstanding; the
+  // barrier makes every wave's copies visible.
+  wait_vm_lds<RB * PCH + 1 + (FUSE ? CPL * EPL / 4 : 0)>();
+  __syncthreads();
+  if (KS > 1 || ss_in) {
+    // t = inv (t_0 + t_1 + ...), into the first slice
+    for (int i = 4 * tid; i < r; i += 4 * K2_THREADS) {
+      float4 a = *reinterpret_cast<const float4*>(ts + i);
+      for (int k = 1; k < KS; ++k) {
+        const float4 u = *reinterpret_cast<const float4*>(ts + (size_t)k * dpr + i);
+        a.x += u.x;
+        a.y += u.y;
+        a.z += u.z;
+        a.w += u.w;
+      }
+      a.x *= inv;
+      a.y *= inv;
+      a.z *= inv;
+      a.w *= inv;
+      *reinterpret_cast<float4*>(ts + i) = a;
+    }
+    __syncthreads();
+  }
+  if (wx && kx0 + tid < kx1) {
+    const float xk = ss_in ? vk * inv : vk;                  // the same product as the gathers'
+    if (x_out) x_out[kx0 + tid] = xk;
+    if (x_trace) x_trace[kx0 + tid] = xk;
+  }
 
   int n_w = 0;                                               // this wave's active neurons so far
   for (int m0 = 0; m0 < Mb; m0 += RB) {
@@ -757,6 +828,7 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
 
   int nz = 0;                                                // wave 0: neurons listed with h != 0
   if constexpr (FUSE) {
+    if (ss_in) xreg_scale<WT, CPL>(xr, inv);                 // x' = v inv
     xreg_sums<WT, CPL>(xr);
     const void* w0 = (ACT == ACT_REGLU) ? gate_w : up_w;
     const uint16_t* s0 = (ACT == ACT_REGLU) ? gate_sc : up_sc;
@@ -836,6 +908,12 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
     cnt_blk[b] = n;
     cnt_blk[nb + b] = nz;
   }
+  if (wx)                                                    // the rest of the slice (few blocks)
+    for (int k = kx0 + K2_THREADS + tid; k < kx1; k += K2_THREADS) {
+      const float xk = ss_in ? vx[k] * inv : vx[k];
+      if (x_out) x_out[k] = xk;
+      if (x_trace) x_trace[k] = xk;
+    }
 }
 
 // Up/gate over an explicit list (pi_sparse_ffn): h_list[j] for j < count, one
@@ -1171,7 +1249,7 @@ k_glue_out(const float* __restrict__ x, const float* __restrict__ y_part, int np
   extern __shared__ float vs[];
   __shared__ float red[16];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE, W = blockDim.x / WAVE;
-  float ss = stage_residual<4>(vs, x, y_part, np, d, tid, blockDim.x);
+  float ss = stage_residual(vs, x, y_part, np, d, tid, blockDim.x);
   ss = wave_sum(ss);
   if (lane == 0) red[w] = ss;
   __syncthreads();
