@@ -73,6 +73,7 @@ struct Dims {
 
 constexpr int kMaxParts = 8;       // neuron splits of the down projection (partial y vectors)
 constexpr int kK1MaxSplit = 4;     // column slices of the predictor's first product
+constexpr int kMaxTiles = 1024;    // column tiles of the down projection (at most 512 for d <= 16384)
 constexpr int kK2Grid = 512;   // two per compute unit of an MI355X
 
 int epl_of(int dt) { return dt == PI_F32 ? 4 : (dt == PI_F16 ? 8 : 32); }
@@ -88,7 +89,7 @@ size_t k2_pairs_max(int ffn) { return (size_t)k2_blocks_for(ffn) * k2_cap(ffn); 
 int bscore_blocks(int ffn) { return cdiv(ffn, pib::BM); }
 
 struct WsLayout {
-  size_t t, v, xbuf, ybuf, mask, pmask, h, pid, ph, cnt, misc;
+  size_t t, v, ss, tcnt, xbuf, ybuf, mask, pmask, h, pid, ph, cnt, misc;
   // batched path (batch > 1)
   size_t xh, xl, tpart, th, tl, mnm, ulist, hh, hl;
   size_t total;
@@ -105,7 +106,9 @@ WsLayout layout(const Dims& D, int batch) {
   w.xs = align_up(sizeof(float) * (size_t)D.d * batch);
   w.ys = align_up(sizeof(float) * (size_t)D.d * (batch > 1 ? pib::BD_SPLIT * kBatchM : kMaxParts));
   w.t = o;    o += align_up(sizeof(float) * (size_t)D.rmax * std::max(batch, kK1MaxSplit));
-  w.v = o;    o += align_up(sizeof(float) * ((size_t)D.d + kK1MaxSplit));   // v, then its slices' sums of squares
+  w.v = o;    o += align_up(sizeof(float) * (size_t)D.d);              // x' + y of a layer (batch 1)
+  w.ss = o;   o += align_up(sizeof(float) * kK1MaxSplit);              // its slices' sums of squares
+  w.tcnt = o; o += align_up(sizeof(int32_t) * kMaxTiles);             // the down projection's tile counters
   w.xbuf = o; o += w.xs * 2;
   w.ybuf = o; o += w.ys * 2;
   w.mask = o; o += align_up(fpad);                       // one byte per neuron (the union when batch > 1)
@@ -135,6 +138,8 @@ WsLayout layout(const Dims& D, int batch) {
 struct Ws {
   float* t;
   float* v;
+  float* ss;
+  int32_t* tcnt;
   float* x[2];
   float* y[2];
   uint8_t* mask;
@@ -155,6 +160,8 @@ Ws carve(void* base, const WsLayout& L) {
   Ws w{};
   w.t = reinterpret_cast<float*>(b + L.t);
   w.v = reinterpret_cast<float*>(b + L.v);
+  w.ss = reinterpret_cast<float*>(b + L.ss);
+  w.tcnt = reinterpret_cast<int32_t*>(b + L.tcnt);
   w.x[0] = reinterpret_cast<float*>(b + L.xbuf);
   w.x[1] = reinterpret_cast<float*>(b + L.xbuf + L.xs);
   w.y[0] = reinterpret_cast<float*>(b + L.ybuf);
@@ -255,27 +262,22 @@ K3Shape k3_shape(int d, int dt) {
   return s;
 }
 
-// The next layer's predictor kernel stages its column slice of x and of up to
-// k1_slots(n) partial y vectors (n floats each) in LDS at once (144 KiB of
-// it), the rest in later rounds.
-int k1_slots(int n) { return std::max(1, 147456 / (4 * dma_pad(n)) - 1); }
-
 // ---------------------------------------------------------------- dispatch
 struct K1Args {
-  const float* x_prev;
-  const float* y_prev;   // y_np partial vectors, or NULL (no glue)
-  int y_np;
-  float* v;              // v = x_prev + y_prev [d], then the slices' sums of squares [k1_split]
+  const float* v;        // the layer's input before the glue [d]
+  bool glue;             // normalise it (the sums of squares go to ss)
+  float* ss;             // [k1_split]
   float* t_part;         // [k1_split][rank]
+  int32_t* zero;         // counters to clear, or NULL
+  int n_zero;
 };
 
 template <int PT, int NCH>
 void launch_k1_t(const pi_layer* L, const K1Args& a, hipStream_t st) {
   const int ks = k1_split(L->rank), ds = L->d / ks;
-  const int slots = std::max(1, std::min(a.y_np, k1_slots(ds)));
   hipLaunchKernelGGL((k_predict_t<PT, NCH>), dim3(k1_blocks(L->rank)), dim3(K1_WAVES * WAVE),
-                     sizeof(float) * (size_t)dma_pad(ds) * (1 + (a.y_np > 0 ? slots : 0)), st, L->A, L->rank, L->d,
-                     ks, a.x_prev, a.y_prev, a.y_np, slots, a.v, a.v + L->d, a.t_part);
+                     sizeof(float) * (size_t)dma_pad(ds), st, L->A, L->rank, L->d, ks, a.v, a.glue ? 1 : 0, a.ss,
+                     a.t_part, a.zero, a.zero ? a.n_zero : 0);
 }
 
 template <int PT>
@@ -380,6 +382,11 @@ struct K3Args {
   int32_t* count_out;
   int32_t* count_out2;
   int32_t* nz_out;           // active neurons with h != 0, or NULL
+  int32_t* tile_cnt;         // per column tile counters, zero at launch (the last block of a tile adds
+                             // its partials), or NULL (partials only)
+  const float* x_res;        // v_out = x_res + y
+  float* y_out;              // y, or NULL
+  float* v_out;              // or NULL
 };
 
 template <int WT, int TWC, bool EXPL>
@@ -388,7 +395,8 @@ void launch_k3_t(const pi_layer* L, const K3Shape& sh, const K3Args& a, hipStrea
   const int xcd = (nblk % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((k_down<WT, TWC, EXPL>), dim3(nblk), dim3(K3_WAVES * WAVE), 0, st, L->downT.w,
                      L->downT.scale, L->ffn, L->d, sh.ct, sh.nc, xcd, a.pid, a.ph, a.cap, a.idx, a.count, a.h_list,
-                     L->b_down, a.y_part, a.cnt_blk, a.n_cnt_blk, a.count_out, a.count_out2, a.nz_out);
+                     L->b_down, a.y_part, a.cnt_blk, a.n_cnt_blk, a.count_out, a.count_out2, a.nz_out, a.tile_cnt,
+                     a.x_res, a.y_out, a.v_out);
 }
 
 template <int WT, bool EXPL>
@@ -625,19 +633,20 @@ pi_status run_stack(const pi_layer* layers, int32_t n_layers, const float* x, in
                        pib::BD_SPLIT, D.d, out);
     return launch_status();
   }
-  int np_prev = 0;
   for (int l = 0; l < n_layers; ++l) {
     const pi_layer* L = &layers[l];
     const pi_trace* tr = trace ? &trace[l] : nullptr;
-    const int cur = l & 1, prv = cur ^ 1;
-    mark(tr, 0, st);
+    const int cur = l & 1;
+    // v: the stack's input, then the previous layer's x' + y (written by its down projection)
     const bool glue = l > 0;
-    k1(L, K1Args{glue ? W.x[prv] : x, glue ? W.y[prv] : nullptr, glue ? np_prev : 0, W.v, W.t}, st);
+    const float* v = glue ? W.v : x;
+    mark(tr, 0, st);
+    k1(L, K1Args{v, glue, W.ss, W.t, W.tcnt, kMaxTiles}, st);
     mark(tr, 1, st);
     // the predictor's own mask goes to the record, or to W.pmask when only the
     // record's list asks for it
     uint8_t* pmask = tr ? (tr->mask ? tr->mask : (tr->idx ? W.pmask : nullptr)) : nullptr;
-    k2(L, true, K2Args{W.t, glue ? W.v + L->d : nullptr, glue ? W.v : x, W.x[cur], tr ? tr->x_in : nullptr,
+    k2(L, true, K2Args{W.t, glue ? W.ss : nullptr, v, W.x[cur], tr ? tr->x_in : nullptr,
                        tr ? tr->scores : nullptr, pmask, W.cnt, W.pid, W.ph}, st);
     mark(tr, 2, st);
     int32_t* c1 = counts ? counts + l : nullptr;
@@ -645,18 +654,13 @@ pi_status run_stack(const pi_layer* layers, int32_t n_layers, const float* x, in
     if (tr && tr->idx)   // ascending list of the predictor's mask, for the record
       hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, pmask, L->ffn, tr->idx,
                          tr->count ? tr->count : W.misc, nullptr, nullptr);
-    np_prev = k3<false>(L, K3Args{W.pid, W.ph, k2_cap(L->ffn), nullptr, nullptr, nullptr, W.y[cur], W.cnt,
-                                  k2_blocks(L), c1, c2,
-                                  nz_counts ? nz_counts + l : nullptr}, st);
+    k3<false>(L, K3Args{W.pid, W.ph, k2_cap(L->ffn), nullptr, nullptr, nullptr, W.y[0], W.cnt, k2_blocks(L), c1, c2,
+                        nz_counts ? nz_counts + l : nullptr, W.tcnt, W.x[cur], tr ? tr->y : nullptr, W.v},
+              st);
     mark(tr, 3, st);
-    if (tr && tr->y)     // the layer's y for the record: its partial vectors added in the glue's order
-      hipLaunchKernelGGL(k_finalize, dim3(cdiv(L->d, 256)), dim3(256), 0, st, W.y[cur], np_prev, tr->y, L->d);
   }
-  {
-    const int last = (n_layers - 1) & 1;
-    hipLaunchKernelGGL(k_glue_out, dim3(1), dim3(256), sizeof(float) * D.d, st, W.x[last], W.y[last], np_prev,
-                       out, D.d);
-  }
+  // out = glue(x' + y) of the last layer
+  hipLaunchKernelGGL(k_glue_out, dim3(1), dim3(256), sizeof(float) * D.d, st, W.v, nullptr, 0, out, D.d);
   return launch_status();
 }
 
@@ -743,7 +747,7 @@ pi_status pi_predict(const pi_layer* layer, const float* x, int32_t batch, float
     b_predict(layer, batch, W, scores, mask, idx, count, nullptr, nullptr, st);
     return launch_status();
   }
-  k1(layer, K1Args{x, nullptr, 0, W.v, W.t}, st);
+  k1(layer, K1Args{x, false, W.ss, W.t, nullptr, 0}, st);
   uint8_t* pm = mask ? mask : W.mask;
   k2(layer, false, K2Args{W.t, nullptr, nullptr, nullptr, nullptr, scores, pm, nullptr, nullptr, nullptr}, st);
   hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, pm, layer->ffn, idx, count, nullptr, nullptr);

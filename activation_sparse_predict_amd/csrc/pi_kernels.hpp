@@ -407,32 +407,26 @@ __device__ __forceinline__ void gather_rows(const void* __restrict__ w0, const u
 
 // ----------------------------------------------------------------------- K1
 // The predictor's first product in KS column slices: t_part[k][row] =
-// A[row, slice k] . v[slice k], where v = x_prev + y_prev (the residual sum,
-// y_prev given as y_np partial vectors added in order) or v = x_prev when
-// y_np == 0.  The glue's normalisation x' = v / sqrt(mean(v^2) + 1e-6) is a
-// scalar factor, so it is applied by the score kernel to the sum of the
-// slices' products; here the blocks of group 0 write v and their slice's
-// sum of squares ss[k] for it.
+// A[row, slice k] . v[slice k].  v is the layer's input before the glue (the
+// residual sum x + y that the previous layer's down projection wrote, or the
+// stack's input).  The glue's normalisation x' = v / sqrt(mean(v^2) + 1e-6)
+// is a scalar factor, so the score kernel applies it to the sum of the
+// slices' products; with a glue, the blocks of row group 0 write their
+// slice's sum of squares ss[k] for it.
 // Block b takes slice k = b % KS and rows 8 (b / KS) + w, one wave per row.
-// The slice of x_prev and the first `slots` partials go to LDS by LDS-DMA
-// first; the row segment of A (NCH chunks per lane per round) is issued after
-// them, its addresses depending on an opaque zero, so the residual sum waits
-// only for the copies and runs while the row is in flight.  Further partials
-// (when LDS holds fewer than y_np) are copied into the same slots a round at a
-// time.  Each thread adds the partials of its elements in registers
-// (y = ((y_0 + y_1) + y_2) + ...), then v = x_prev + y.  Every block of a slice
-// computes the same v with the same operation order.
-// The column split doubles (or quadruples) the blocks of a small rank, so the
-// read of A covers the whole chip, and divides the LDS a block stages.
+// The slice of v goes to LDS by LDS-DMA first; the row segment of A (NCH
+// chunks per lane per round) is issued after it, its addresses depending on an
+// opaque zero, so the sum of squares waits only for the copy and runs while
+// the row is in flight.  The column split doubles (or quadruples) the blocks
+// of a small rank, so the read of A covers the whole chip.
+// Block 0 also clears n_zero counters (the down projection's tile counters).
 constexpr int K1_WAVES = 8;
 constexpr int K1_THREADS = K1_WAVES * WAVE;
-constexpr int K1_MAXV = 8;           // float4 elements of a slice per thread (d / KS <= 16384)
 
 template <int PT, int NCH>
 __global__ void __launch_bounds__(K1_THREADS)
-k_predict_t(const void* __restrict__ A, int r, int d, int KS, const float* __restrict__ x_prev,
-            const float* __restrict__ y_prev, int y_np, int slots, float* __restrict__ v_out,
-            float* __restrict__ ss_out, float* __restrict__ t_part) {
+k_predict_t(const void* __restrict__ A, int r, int d, int KS, const float* __restrict__ v, int glue,
+            float* __restrict__ ss_out, float* __restrict__ t_part, int32_t* __restrict__ zero, int n_zero) {
   extern __shared__ float smem[];
   __shared__ float red[K1_WAVES];
   constexpr int EPL = Tr<PT>::EPL, TW = WAVE * EPL;
@@ -442,87 +436,38 @@ k_predict_t(const void* __restrict__ A, int r, int d, int KS, const float* __res
   const size_t rowc = (size_t)min(row, r - 1);       // a wave without a row reads row r-1 and discards it
   const int ds = d / KS, off = ks * ds;               // this block's columns [off, off + ds)
   const int nch = (ds + TW - 1) / TW;
-  const int dp = dma_pad(ds);
-  float* xs = smem;                                   // x_prev, then v [dp]
-  float* ys = smem + dp;                              // the y partials of a round [slots][dp]
+  float* xs = smem;                                   // v [dma_pad(ds)]
 
-  dma_f32(xs, x_prev + off, ds, w, K1_WAVES, lane);
-  const int n0 = min(y_np, slots);
-  for (int p = 0; p < n0; ++p)
-    dma_f32(ys + (size_t)p * dp, y_prev + (size_t)p * d + off, ds, w, K1_WAVES, lane);
+  if (blockIdx.x == 0)
+    for (int k = tid; k < n_zero; k += K1_THREADS) zero[k] = 0;
+  dma_f32(xs, v + off, ds, w, K1_WAVES, lane);
   const int z = opaque_zero();
   uint4 c[NCH];
 #pragma unroll
   for (int q = 0; q < NCH; ++q)
     c[q] = ld_chunk<PT>(A, rowc + z, d, off + min(min(q, nch - 1) * TW + lane * EPL, ds - EPL));
   PI_ISSUE_FENCE();
-  wait_vm_lds<NCH>();                                 // the copies, not the row
+  wait_vm_lds<NCH>();                                 // the copy, not the row
   __builtin_amdgcn_s_barrier();
 
-  const int nv = ds / 4;
-  if (y_np > 0) {
-    float4 y4[K1_MAXV];                               // this thread's elements k = tid + K1_THREADS j
-    for (int p0 = 0; p0 < y_np; p0 += slots) {
-      const int cnt = min(slots, y_np - p0);
-      if (p0 > 0) {                                   // this round's copies (issued behind the row)
-        wait_vm_lds<0>();
-        __builtin_amdgcn_s_barrier();
-      }
-#pragma unroll
-      for (int j = 0; j < K1_MAXV; ++j) {
-        const int k = tid + K1_THREADS * j;
-        if (k < nv) {
-          for (int q = 0; q < cnt; ++q) {
-            const float4 u = reinterpret_cast<const float4*>(ys + (size_t)q * dp)[k];
-            if (p0 + q == 0) {
-              y4[j] = u;
-            } else {
-              y4[j].x += u.x;
-              y4[j].y += u.y;
-              y4[j].z += u.z;
-              y4[j].w += u.w;
-            }
-          }
-        }
-      }
-      if (p0 + slots < y_np) {                        // the next round's partials, into the same slots
-        __syncthreads();
-        for (int q = 0; q < min(slots, y_np - p0 - slots); ++q)
-          dma_f32(ys + (size_t)q * dp, y_prev + (size_t)(p0 + slots + q) * d + off, ds, w, K1_WAVES, lane);
-      }
-    }
+  if (glue && grp == 0) {
     float ss = 0.f;
-    float4* x4 = reinterpret_cast<float4*>(xs);
-#pragma unroll
-    for (int j = 0; j < K1_MAXV; ++j) {
-      const int k = tid + K1_THREADS * j;
-      if (k < nv) {
-        float4 v = x4[k];
-        v.x += y4[j].x;
-        v.y += y4[j].y;
-        v.z += y4[j].z;
-        v.w += y4[j].w;
-        x4[k] = v;
-        if (grp == 0) {
-          reinterpret_cast<float4*>(v_out + off)[k] = v;
-          ss = fmaf(v.x, v.x, ss);
-          ss = fmaf(v.y, v.y, ss);
-          ss = fmaf(v.z, v.z, ss);
-          ss = fmaf(v.w, v.w, ss);
-        }
-      }
+    for (int k = tid; k < ds / 4; k += K1_THREADS) {
+      const float4 u = reinterpret_cast<const float4*>(xs)[k];
+      ss = fmaf(u.x, u.x, ss);
+      ss = fmaf(u.y, u.y, ss);
+      ss = fmaf(u.z, u.z, ss);
+      ss = fmaf(u.w, u.w, ss);
     }
-    if (grp == 0) {
-      ss = wave_sum(ss);
-      if (lane == 0) red[w] = ss;
-    }
-  }
-  __syncthreads();
-  if (y_np > 0 && grp == 0 && tid == 0) {
-    float tot = 0.f;
+    ss = wave_sum(ss);
+    if (lane == 0) red[w] = ss;
+    __syncthreads();
+    if (tid == 0) {
+      float tot = 0.f;
 #pragma unroll
-    for (int i = 0; i < K1_WAVES; ++i) tot += red[i];
-    ss_out[ks] = tot;
+      for (int i = 0; i < K1_WAVES; ++i) tot += red[i];
+      ss_out[ks] = tot;
+    }
   }
 
   float a = 0.f;
@@ -731,19 +676,20 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
     for (int k = 0; k < KS; ++k) tot += ss_in[k];
     inv = 1.0f / sqrtf(tot / (float)d + 1e-6f);
   }
-  issue(0, 0, opaque_zero());
-  XReg<WT, CPL> xr;
-  if constexpr (FUSE) load_xreg<WT, CPL>(xr, vx, nch, tid);
-  PI_ISSUE_FENCE();
   // this block's slice of x' = v inv [kx0, kx1) for x_out / x_trace: its first
-  // K2_THREADS elements are loaded here and stored once inv is known
+  // K2_THREADS elements are loaded with the copies and stored once they are in
   const int cx = (d + nb - 1) / nb, kx0 = min(d, b * cx), kx1 = min(d, kx0 + cx);
   const bool wx = x_out || x_trace;
   float vk = 0.f;
   if (wx && kx0 + tid < kx1) vk = vx[kx0 + tid];
-  // The copies of t have arrived once no more than the loads issued after them
-  // (the RB*PCH chunks of B, the bias, the x' chunks) are outstanding; the
-  // barrier makes every wave's copies visible.
+  PI_ISSUE_FENCE();
+  issue(0, 0, opaque_zero());
+  XReg<WT, CPL> xr;
+  if constexpr (FUSE) load_xreg<WT, CPL>(xr, vx, nch, tid);
+  PI_ISSUE_FENCE();
+  // The copies of t (and v's slice) have arrived once no more than the loads
+  // issued after them (the RB*PCH chunks of B, the bias, the x' chunks) are
+  // outstanding; the barrier makes every wave's copies visible.
   wait_vm_lds<RB * PCH + 1 + (FUSE ? CPL * EPL / 4 : 0)>();
   __syncthreads();
   if (KS > 1 || ss_in) {
@@ -972,6 +918,12 @@ k_up_list(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc,
 // column are summed inside each 16-lane row, then the rows of all waves in a
 // fixed order, and the tile's partial sums are written to y_part[nc][cols]
 // with plain stores.
+// With tile counters (zero at launch), the block that finishes a column tile
+// last -- the blocks store their partial tiles with device-coherent stores,
+// wait for them to be acknowledged and then count themselves with a
+// device-scope atomic -- adds the NC partial tiles in split order,
+// y = ((y_0 + y_1) + y_2) + ..., and writes y to y_out and x_res + y to v_out
+// (those given).
 constexpr int K3_WAVES = 8;
 constexpr int K3_CAP = 1024;     // list entries per wave held at once
 constexpr int K3_LOADS = 16;     // row segments per lane per HBM round trip (8 for Q4_0, whose
@@ -985,7 +937,8 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
        const int32_t* __restrict__ idx, const int32_t* __restrict__ count, const float* __restrict__ h_list,
        const float* __restrict__ b_down, float* __restrict__ y_part, const int32_t* __restrict__ cnt_blk,
        int n_cnt_blk, int32_t* __restrict__ count_out, int32_t* __restrict__ count_out2,
-       int32_t* __restrict__ nz_out) {
+       int32_t* __restrict__ nz_out, int32_t* __restrict__ tile_cnt, const float* __restrict__ x_res,
+       float* __restrict__ y_out, float* __restrict__ v_out) {
   constexpr int EPL = Tr<WT>::EPL;
   constexpr int RPW = WAVE / TWC;                 // rows per wave-wide load
   constexpr int TCOL = TWC * EPL;                 // columns per tile
@@ -1158,7 +1111,32 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
 #pragma unroll
     for (int i = 0; i < K3_WAVES * 4; ++i) v += rsum[(size_t)i * TCOL + cc];
     if (b_down && nc == 0) v += b_down[cg];
-    y_part[(size_t)nc * d + cg] = v;
+    if (tile_cnt)   // device-coherent store: read by the tile's last block, maybe on another XCD
+      __hip_atomic_store(&y_part[(size_t)nc * d + cg], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      y_part[(size_t)nc * d + cg] = v;
+  }
+  if (tile_cnt) {
+    // Every store of the partial tile is acknowledged (vmcnt 0) before the
+    // block is counted; the last block reads the partials with device-coherent
+    // loads.  This keeps the whole-L2 write-back and invalidation of an
+    // agent-scope release/acquire fence pair off the path.
+    __shared__ int last;
+    wait_vm_lds<0>();
+    __syncthreads();
+    if (tid == 0) last = __hip_atomic_fetch_add(&tile_cnt[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == NC - 1;
+    __syncthreads();
+    if (last) {
+      for (int cc = tid; cc < TCOL; cc += blockDim.x) {
+        const int cg = tile * TCOL + cc;
+        if (cg >= d) continue;
+        float y = __hip_atomic_load(&y_part[cg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int p = 1; p < NC; ++p)
+          y += __hip_atomic_load(&y_part[(size_t)p * d + cg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (y_out) y_out[cg] = y;
+        if (v_out) v_out[cg] = x_res[cg] + y;
+      }
+    }
   }
 }
 
