@@ -91,13 +91,14 @@ int bscore_blocks(int ffn) { return cdiv(ffn, pib::BM); }
 struct WsLayout {
   size_t t, v, ss, tcnt, xbuf, ybuf, mask, pmask, h, pid, ph, cnt, misc;
   // batched path (batch > 1)
-  size_t xh, xl, tpart, th, tl, mnm, ulist, hh, hl;
+  size_t xh, xl, tpart, th, tl, mnm, ulist, h32, rsc;
   size_t total;
   size_t xs, ys;   // sizes of one x / one y buffer
 };
 
 constexpr int kBatchM = pib::BM;      // padded batch rows of the batched GEMMs
 constexpr int kMaxKSplit = 16;        // K splits of the batched predictor's first GEMM
+static_assert(kMaxKSplit <= pib::BT_KS, "k_bsplit_t holds every split of a value");
 
 WsLayout layout(const Dims& D, int batch) {
   WsLayout w{};
@@ -128,8 +129,8 @@ WsLayout layout(const Dims& D, int batch) {
     w.tl = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * D.rmax);
     w.mnm = o;   o += align_up((size_t)kBatchM * D.fmax);
     w.ulist = o; o += align_up(sizeof(int32_t) * (size_t)D.fmax);
-    w.hh = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * pib::h_stride(D.fmax));
-    w.hl = o;    o += align_up(sizeof(uint16_t) * (size_t)kBatchM * pib::h_stride(D.fmax));
+    w.h32 = o;   o += align_up(sizeof(float) * (size_t)kBatchM * pib::h_stride(D.fmax));
+    w.rsc = o;   o += align_up(sizeof(float) * 3 * kBatchM);   // row scales of x and t, row maxima of h
   }
   w.total = o;
   return w;
@@ -149,7 +150,9 @@ struct Ws {
   float* ph;
   int32_t* cnt;
   int32_t* misc;
-  _Float16 *xh, *xl, *th, *tl, *hh, *hl;
+  _Float16 *xh, *xl, *th, *tl;
+  float *h32, *sx, *st;
+  uint32_t* hmax;
   float* tpart;
   uint8_t* mnm;
   int32_t* ulist;
@@ -181,8 +184,10 @@ Ws carve(void* base, const WsLayout& L) {
     w.tl = reinterpret_cast<_Float16*>(b + L.tl);
     w.mnm = reinterpret_cast<uint8_t*>(b + L.mnm);
     w.ulist = reinterpret_cast<int32_t*>(b + L.ulist);
-    w.hh = reinterpret_cast<_Float16*>(b + L.hh);
-    w.hl = reinterpret_cast<_Float16*>(b + L.hl);
+    w.h32 = reinterpret_cast<float*>(b + L.h32);
+    w.sx = reinterpret_cast<float*>(b + L.rsc);
+    w.st = w.sx + kBatchM;
+    w.hmax = reinterpret_cast<uint32_t*>(w.st + kBatchM);
   }
   return w;
 }
@@ -484,7 +489,7 @@ int bksplit(int r) { return std::max(1, std::min(kMaxKSplit, cdiv(256, cdiv(r, k
 void b_glue(const float* x_prev, const float* y_prev, int batch, int d, float* x_out, float* x_trace, const Ws& W,
             hipStream_t st) {
   hipLaunchKernelGGL(pib::k_bglue, dim3(kBatchM), dim3(pib::BG_T), 0, st, x_prev, y_prev,
-                     y_prev ? pib::BD_SPLIT : 0, batch, d, x_out, x_trace, W.xh, W.xl);
+                     y_prev ? pib::BD_SPLIT : 0, batch, d, x_out, x_trace, W.xh, W.xl, W.sx, W.hmax);
 }
 
 // per-sequence scores and masks, the union and its ascending list
@@ -518,17 +523,17 @@ void b_predict(const pi_layer* L, int batch, const Ws& W, float* scores, uint8_t
   else
     hipLaunchKernelGGL(pib::k_bpred1<DT_F32>, g1, dim3(256), 0, st, L->A, L->rank, L->d, ks, W.xh, W.xl, W.tpart);
   mark(tr, 2, st);
-  hipLaunchKernelGGL(pib::k_bsplit_t, dim3(cdiv(kBatchM * L->rank, 256)), dim3(256), 0, st, W.tpart, ks, L->rank,
-                     W.th, W.tl);
+  hipLaunchKernelGGL(pib::k_bsplit_t, dim3(kBatchM), dim3(pib::BT_T), 0, st, W.tpart, ks, L->rank, W.sx, W.th, W.tl,
+                     W.st);
   mark(tr, 3, st);
   const dim3 g2(bscore_blocks(L->ffn));
   const float* pb = L->pbias ? L->pbias : L->bias;
   if (L->p_dtype == PI_F16)
     hipLaunchKernelGGL(pib::k_bscore<DT_F16>, g2, dim3(256), 0, st, L->B, pb, L->ffn, L->rank, batch, W.th, W.tl,
-                       W.mnm, W.mask, W.cnt, scores, mask_out);
+                       W.st, W.mnm, W.mask, W.cnt, scores, mask_out);
   else
     hipLaunchKernelGGL(pib::k_bscore<DT_F32>, g2, dim3(256), 0, st, L->B, pb, L->ffn, L->rank, batch, W.th, W.tl,
-                       W.mnm, W.mask, W.cnt, scores, mask_out);
+                       W.st, W.mnm, W.mask, W.cnt, scores, mask_out);
   mark(tr, 4, st);
   hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, ulist, ucount, ucount2, ucount3);
   mark(tr, 5, st);
@@ -539,11 +544,11 @@ void b_ffn_t(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, co
              hipStream_t st, const pi_trace* tr) {
   hipLaunchKernelGGL((pib::k_bup<WT, ACT>), dim3(cdiv(L->ffn, kBatchM)), dim3(pib::BUP_W * WAVE), 0, st, L->gate.w,
                      L->gate.scale, L->up.w, L->up.scale, L->bias, L->ffn, L->d, W.xh, W.xl, ulist, ucount, W.mnm,
-                     W.hh, W.hl);
+                     W.sx, W.h32, W.hmax);
   mark(tr, 6, st);
   hipLaunchKernelGGL(pib::k_bdown<WT>, dim3(cdiv(L->d, kBatchM * pib::bd_tiles<WT>()) * pib::BD_SPLIT), dim3(256), 0,
                      st, L->downT.w,
-                     L->downT.scale, L->ffn, L->d, ulist, ucount, W.hh, W.hl, L->b_down, batch, y);
+                     L->downT.scale, L->ffn, L->d, ulist, ucount, W.h32, W.hmax, L->b_down, batch, y);
   mark(tr, 7, st);
 }
 

@@ -13,7 +13,11 @@
 // accumulation; fp16 and Q4_0 weights are exact in fp16 (Q4_0 as q - 8, its
 // scale applied in fp32).  So the matrix cores give fp32-level results: the
 // predictor's scores stay within the threshold band of the single-token path
-// and the FFN within the same tolerance.
+// and the FFN within the same tolerance.  Each activation row b is scaled by
+// a power of two s_b before the split, so that its largest magnitude lies in
+// [2^13, 2^14): no value overflows fp16 (65504) and small rows keep their lo
+// bits out of the fp16 subnormals.  A product's row b is then s_b times the
+// true one, and the consumer multiplies it by 1 / s_b, exactly.
 //
 // MFMA 32x32x16 f16 operand layout (lane l, e = 0..7): A[row l%32][k = 8*(l/32)
 // + e], B[k = 8*(l/32) + e][col l%32]; accumulator element 4g+v of lane l is
@@ -45,6 +49,15 @@ __host__ __device__ constexpr size_t aop(int row, int k) {
   return (size_t)(k >> 4) * 512 + (size_t)((k >> 3) & 1) * 256 + (size_t)row * 8 + (k & 7);
 }
 
+// The power of two s with m s in [2^13, 2^14) for a row of largest magnitude
+// m (1 for a zero or non-finite m).
+__device__ __forceinline__ float pow2_scale(float m) {
+  if (!(m > 0.f) || !__builtin_isfinite(m)) return 1.f;
+  int e;
+  (void)frexpf(m, &e);                     // m = f 2^e, f in [0.5, 1)
+  return ldexpf(1.f, min(max(14 - e, -120), 120));
+}
+
 // fp32 value -> (hi, lo) fp16 pair with hi + lo ~ v to about 22 bits
 __device__ __forceinline__ void split_f16(float v, _Float16* hi, _Float16* lo) {
   const _Float16 h = (_Float16)v;
@@ -73,19 +86,24 @@ __device__ __forceinline__ h8v q4_h8(uint4 c, int b0, bool hi_nib) {
 // ------------------------------------------------------------------- glue
 // One block per padded sequence row b < 32.  Rows b < B: x' = glue(x_prev[b],
 // sum of np partials y[p][b]) (np = 0: x' = x_prev[b]); x' goes to x_out[b]
-// (and x_trace[b]) in fp32 and to xh/xl row b (operand order) as fp16 hi/lo.  Rows b >= B are
-// written as zeros in xh/xl so that they contribute nothing to any product.
+// (and x_trace[b]) in fp32 and, times its row scale sx[b], to xh/xl row b
+// (operand order) as fp16 hi/lo.  Rows b >= B are written as zeros in xh/xl
+// so that they contribute nothing to any product.  Block b also clears the
+// row maximum hmax[b] of the layer's h.
 constexpr int BG_T = 1024;               // threads of a glue block
 constexpr int BG_V = 4;                  // float4 per thread held at once (d <= 16384)
 
 __global__ void __launch_bounds__(BG_T)
 k_bglue(const float* __restrict__ x_prev, const float* __restrict__ y_part, int np, int B, int d,
         float* __restrict__ x_out, float* __restrict__ x_trace, _Float16* __restrict__ xh,
-        _Float16* __restrict__ xl) {
+        _Float16* __restrict__ xl, float* __restrict__ sx, uint32_t* __restrict__ hmax) {
   __shared__ float red[BG_T / WAVE];
+  __shared__ float mred[BG_T / WAVE];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int nv = d / 4;
+  if (tid == 0) hmax[b] = 0u;
   if (b >= B) {
+    if (tid == 0) sx[b] = 1.f;
     for (int k = tid; k < d; k += blockDim.x) {
       xh[aop(b, k)] = (_Float16)0.f;
       xl[aop(b, k)] = (_Float16)0.f;
@@ -145,6 +163,20 @@ k_bglue(const float* __restrict__ x_prev, const float* __restrict__ y_part, int 
     for (int i = 0; i < BG_T / WAVE; ++i) tot += red[i];
     inv = 1.0f / sqrtf(tot / (float)d + 1e-6f);
   }
+  // the row's largest |x'| and its scale
+  float mx = 0.f;
+#pragma unroll
+  for (int j = 0; j < BG_V; ++j)
+    if (tid + BG_T * j < nv)
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[j].x * inv), fabsf(v[j].y * inv)), fmaxf(fabsf(v[j].z * inv), fabsf(v[j].w * inv))));
+  mx = wave_max(mx);
+  if (lane == 0) mred[w] = mx;
+  __syncthreads();
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < BG_T / WAVE; ++i) m = fmaxf(m, mred[i]);
+  const float sc = pow2_scale(m);
+  if (tid == 0) sx[b] = sc;
 #pragma unroll
   for (int j = 0; j < BG_V; ++j) {
     const int k4 = tid + BG_T * j;
@@ -154,7 +186,7 @@ k_bglue(const float* __restrict__ x_prev, const float* __restrict__ y_part, int 
     if (x_trace) reinterpret_cast<float4*>(x_trace + (size_t)b * d)[k4] = make_float4(o[0], o[1], o[2], o[3]);
     _Float16 hh[4], ll[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) split_f16(o[e], &hh[e], &ll[e]);
+    for (int e = 0; e < 4; ++e) split_f16(o[e] * sc, &hh[e], &ll[e]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       xh[aop(b, 4 * k4 + e)] = hh[e];
@@ -247,18 +279,54 @@ k_bpred1(const void* __restrict__ A, int r, int d, int ksplit, const _Float16* _
   }
 }
 
-// t = sum of the K-split partials (in order), as fp16 hi/lo [32][r] in operand order
-__global__ void __launch_bounds__(256)
-k_bsplit_t(const float* __restrict__ t_part, int ksplit, int r, _Float16* __restrict__ th,
-           _Float16* __restrict__ tl) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= BM * r) return;
-  float v = t_part[e];
-  for (int ks = 1; ks < ksplit; ++ks) v += t_part[(size_t)ks * BM * r + e];
-  _Float16 hh, ll;
-  split_f16(v, &hh, &ll);
-  th[aop(e / r, e % r)] = hh;
-  tl[aop(e / r, e % r)] = ll;
+// Row b of t (one block per padded row): the sum of the K-split partials (in
+// order) times 1 / sx[b], then times its own row scale st[b] as fp16 hi/lo
+// [32][r] in operand order.  Each thread issues all its partial loads before
+// the first add.
+constexpr int BT_T = 1024;
+constexpr int BT_V = 4;                  // values per thread (r <= 4096)
+constexpr int BT_KS = 16;                // most K splits
+
+__global__ void __launch_bounds__(BT_T)
+k_bsplit_t(const float* __restrict__ t_part, int ksplit, int r, const float* __restrict__ sx,
+           _Float16* __restrict__ th, _Float16* __restrict__ tl, float* __restrict__ st) {
+  __shared__ float mred[BT_T / WAVE];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const float ix = 1.f / sx[b];
+  float v[BT_V];
+  float mx = 0.f;
+#pragma unroll
+  for (int q = 0; q < BT_V; ++q) {
+    const int j = min(tid + BT_T * q, r - 1);
+    const size_t e = (size_t)b * r + j;
+    float p[BT_KS];
+#pragma unroll
+    for (int ks = 0; ks < BT_KS; ++ks) p[ks] = t_part[(size_t)min(ks, ksplit - 1) * BM * r + e];
+    float a = p[0];
+#pragma unroll
+    for (int ks = 1; ks < BT_KS; ++ks)
+      if (ks < ksplit) a += p[ks];
+    v[q] = a * ix;
+    if (tid + BT_T * q < r) mx = fmaxf(mx, fabsf(v[q]));
+  }
+  mx = wave_max(mx);
+  if (lane == 0) mred[w] = mx;
+  __syncthreads();
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < BT_T / WAVE; ++i) m = fmaxf(m, mred[i]);
+  const float sc = pow2_scale(m);
+  if (tid == 0) st[b] = sc;
+#pragma unroll
+  for (int q = 0; q < BT_V; ++q) {
+    const int j = tid + BT_T * q;
+    if (j < r) {
+      _Float16 hh, ll;
+      split_f16(v[q] * sc, &hh, &ll);
+      th[aop(b, j)] = hh;
+      tl[aop(b, j)] = ll;
+    }
+  }
 }
 
 // ------------------------------------------------------------ predictor 2
@@ -273,9 +341,9 @@ constexpr int BS_W = 4;
 template <int PT>
 __global__ void __launch_bounds__(BS_W * WAVE)
 k_bscore(const void* __restrict__ Bm, const float* __restrict__ pbias, int f, int r, int batch,
-         const _Float16* __restrict__ th, const _Float16* __restrict__ tl, uint8_t* __restrict__ m_nm,
-         uint8_t* __restrict__ u, int32_t* __restrict__ cnt_blk, float* __restrict__ scores,
-         uint8_t* __restrict__ mask_out) {
+         const _Float16* __restrict__ th, const _Float16* __restrict__ tl, const float* __restrict__ st,
+         uint8_t* __restrict__ m_nm, uint8_t* __restrict__ u, int32_t* __restrict__ cnt_blk,
+         float* __restrict__ scores, uint8_t* __restrict__ mask_out) {
   __shared__ float red[BS_W][BM * BM];
   __shared__ int cnt_w;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
@@ -304,7 +372,7 @@ k_bscore(const void* __restrict__ Bm, const float* __restrict__ pbias, int f, in
     float sacc = red[0][e];
 #pragma unroll
     for (int v = 1; v < BS_W; ++v) sacc += red[v][e];
-    const float sv = sacc + cb;
+    const float sv = sacc * (1.f / st[b]) + cb;          // the row's scale undone exactly
     const bool on = col_ok && b < batch && sv > 0.f;
     on_rows |= (on ? 1u : 0u) << b;
     if (col_ok) {
@@ -334,10 +402,11 @@ k_bscore(const void* __restrict__ Bm, const float* __restrict__ pbias, int f, in
 // z = X W^T over the union rows.  Block q covers union list entries [32 q,
 // 32 q + 32) (blocks past the union's end return); its BUP_W waves split K
 // into contiguous ranges and their partial tiles are summed through LDS in
-// wave order.  Epilogue: h[b] = m[i][b] ? act(z + bias) : 0, written as fp16
-// hi/lo to hh/hl as a [32][h_stride] operand-order matrix (row b, column j =
-// the neuron's position in the union list), in which the down projection
-// reads it as its A operand.
+// wave order.  Epilogue: z's row b times 1 / sx[b]; h[b] = m[i][b] ?
+// act(z + bias) : 0, written in fp32 to h32 as a [32][h_stride] operand-order
+// matrix (row b, column j = the neuron's position in the union list), in which
+// the down projection reads it as its A operand; hmax[b] collects the largest
+// |h[b]| (as the bits of a non-negative float, by atomic maximum).
 constexpr int BUP_W = 8;
 constexpr int BD_CH = 256;               // union positions per chunk of the down projection
 
@@ -350,10 +419,11 @@ __global__ void __launch_bounds__(BUP_W * WAVE)
 k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, const void* __restrict__ up_w,
       const uint16_t* __restrict__ up_sc, const float* __restrict__ bias, int f, int d,
       const _Float16* __restrict__ xh, const _Float16* __restrict__ xl, const int32_t* __restrict__ ulist,
-      const int32_t* __restrict__ ucount, const uint8_t* __restrict__ m_nm, _Float16* __restrict__ hh_out,
-      _Float16* __restrict__ hl_out) {
+      const int32_t* __restrict__ ucount, const uint8_t* __restrict__ m_nm, const float* __restrict__ sx,
+      float* __restrict__ h32, uint32_t* __restrict__ hmax) {
   constexpr int NMAT = act_nmat<ACT>();
   __shared__ float red[BUP_W][NMAT][BM * BM];
+  __shared__ uint32_t rmax[BM];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int col = lane % 32, half = lane / 32;
   const int n = min(max(*ucount, 0), f);
@@ -423,26 +493,28 @@ k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, con
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int v = 0; v < 4; ++v) red[w][mt][(8 * g + 4 * half + v) * BM + col] = acc[mt][4 * g + v];
+  if (tid < BM) rmax[tid] = 0u;
   __syncthreads();
   for (int e = tid; e < BM * BM; e += blockDim.x) {
     const int b = e / BM, c = e % BM;
     if (t0 + c >= n) continue;
+    const float ix = 1.f / sx[b];
     float z[NMAT];
 #pragma unroll
     for (int mt = 0; mt < NMAT; ++mt) {
       float s = 0.f;
 #pragma unroll
       for (int v = 0; v < BUP_W; ++v) s += red[v][mt][e];
-      z[mt] = s;
+      z[mt] = s * ix;
     }
     const int rw = ulist[t0 + c];
     float h = act_h<ACT>(z[0], bias[rw], z[NMAT - 1]);
     if (m_nm[(size_t)rw * BM + b] == 0) h = 0.f;
-    _Float16 a, l;
-    split_f16(h, &a, &l);
-    hh_out[aop(b, t0 + c)] = a;
-    hl_out[aop(b, t0 + c)] = l;
+    h32[aop(b, t0 + c)] = h;
+    atomicMax(&rmax[b], __float_as_uint(fabsf(h)));         // LDS atomic
   }
+  __syncthreads();
+  if (tid < BM && rmax[tid] != 0u) atomicMax(&hmax[tid], rmax[tid]);
 }
 
 // ------------------------------------------------------------------ down
@@ -454,7 +526,9 @@ k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, con
 // staged through LDS transposed to [column][position] -- each thread writes
 // four consecutive positions of a column at once -- as fp16 (fp32 weights
 // and Q4_0 weights times their block scale as hi + lo pairs); h is read
-// straight from its operand-order layout as the A operand.  Wave w runs K steps
+// straight from its operand-order layout and, times its row scale (from
+// hmax), split into the hi/lo A operands; the tile's row b is multiplied by
+// 1 / s_b at the end.  Wave w runs K steps
 // 4w .. 4w + 3 of a chunk.  The next chunk's global loads are in flight while
 // a chunk is processed; wave partials are summed in a fixed order.
 constexpr int BD_PAD = BD_CH + 8;        // padded position stride (halves) of a transposed column
@@ -468,8 +542,8 @@ template <int WT> constexpr int bd_tiles() { return WT == DT_F16 ? 2 : 1; }
 template <int WT>
 __global__ void __launch_bounds__(256)
 k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int f, int d,
-        const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount, const _Float16* __restrict__ hh_in,
-        const _Float16* __restrict__ hl_in, const float* __restrict__ b_down, int batch,
+        const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount, const float* __restrict__ h32,
+        const uint32_t* __restrict__ hmax, const float* __restrict__ b_down, int batch,
         float* __restrict__ y_part) {
   constexpr int NW = (WT == DT_F16) ? 1 : 2;      // weight tiles: hi (and lo for fp32 and Q4_0)
   constexpr int NT = bd_tiles<WT>();               // 32-column tiles of this block
@@ -498,6 +572,7 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
   const int nch = max(0, min(nch_all, ch0 + cps) - ch0);
   const int rg = tid / 4, cq = tid % 4;            // staging: positions 4 rg .. 4 rg + 3, columns 8 cq ..
   const int row_a = lane % 32, kh = 8 * (lane / 32);
+  const float hs = pow2_scale(__uint_as_float(hmax[row_a]));   // this lane's A row's scale
   f16v acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f16v{};
@@ -511,7 +586,7 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
   struct Stage {
     uint4 wv[NT][4], wv2[4]; // four rows' 16-byte pieces per tile (fp32: two each)
     float scale[4];
-    h8v ah[4], al[4];        // this wave's four K steps of h (hi, lo)
+    float4 hv[4][2];         // this wave's four K steps of h (8 values each)
   };
   auto fetch = [&](int c, Stage& st) __attribute__((always_inline)) {
     const int base = (ch0 + c) * BD_CH;
@@ -537,23 +612,28 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const int ks = base + 16 * (4 * w + s4);
-      st.ah[s4] = *reinterpret_cast<const h8v*>(hh_in + (size_t)(ks >> 4) * 512 + 8 * lane);
-      st.al[s4] = *reinterpret_cast<const h8v*>(hl_in + (size_t)(ks >> 4) * 512 + 8 * lane);
+      const float4* hp = reinterpret_cast<const float4*>(h32 + (size_t)(ks >> 4) * 512 + 8 * lane);
+      st.hv[s4][0] = hp[0];
+      st.hv[s4][1] = hp[1];
     }
   };
-  // h at positions past the list end is whatever an earlier call left there:
-  // zero it (the weights there are zero, but 0 * NaN is not)
-  auto clip_h = [&](Stage& st, int c) __attribute__((always_inline)) {
+  // The A operands of a chunk: h times the row scale as hi/lo.  h at positions
+  // past the list end is whatever an earlier call left there: it is zeroed
+  // (the weights there are zero, but 0 * NaN is not).
+  h8v ah[4], al[4];
+  auto make_a = [&](const Stage& st, int c) __attribute__((always_inline)) {
     const int base = (ch0 + c) * BD_CH;
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const int jj = base + 16 * (4 * w + s4) + kh;
+      const float hvv[8] = {st.hv[s4][0].x, st.hv[s4][0].y, st.hv[s4][0].z, st.hv[s4][0].w,
+                            st.hv[s4][1].x, st.hv[s4][1].y, st.hv[s4][1].z, st.hv[s4][1].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if (jj + e >= n) {
-          st.ah[s4][e] = (_Float16)0.f;
-          st.al[s4][e] = (_Float16)0.f;
-        }
+        _Float16 hi, lo;
+        split_f16(jj + e < n ? hvv[e] * hs : 0.f, &hi, &lo);
+        ah[s4][e] = hi;
+        al[s4][e] = lo;
       }
     }
   };
@@ -600,7 +680,7 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
   // chunk c: stage its weights, start the next chunk's loads, multiply
   auto step = [&](Stage& cur, Stage& nxt, int c) __attribute__((always_inline)) {
     stage_lds(cur, c);
-    clip_h(cur, c);
+    make_a(cur, c);
     if (c + 1 < nch) fetch(c + 1, nxt);
     __syncthreads();
     const int base = (ch0 + c) * BD_CH;
@@ -611,11 +691,11 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const h8v bw = *reinterpret_cast<const h8v*>(&wt[0][BM * nt + row_a][kb]);
-          acc[nt] = mfma(cur.ah[s4], bw, acc[nt]);
-          acc[nt] = mfma(cur.al[s4], bw, acc[nt]);
+          acc[nt] = mfma(ah[s4], bw, acc[nt]);
+          acc[nt] = mfma(al[s4], bw, acc[nt]);
           if constexpr (NW == 2) {
             const h8v bl = *reinterpret_cast<const h8v*>(&wt[1][BM * nt + row_a][kb]);
-            acc[nt] = mfma(cur.ah[s4], bl, acc[nt]);
+            acc[nt] = mfma(ah[s4], bl, acc[nt]);
           }
         }
       }
@@ -641,6 +721,7 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
     const int b = e / BM, c = e % BM, cg = c0 + BM * nt + c;
     if (b >= batch || cg >= d) continue;
     float v = red[0][nt][e] + red[1][nt][e] + red[2][nt][e] + red[3][nt][e];
+    v *= 1.f / pow2_scale(__uint_as_float(hmax[b]));       // the row's scale undone exactly
     if (b_down && split == 0) v += b_down[cg];
     y_part[((size_t)split * BM + b) * d + cg] = v;
   }

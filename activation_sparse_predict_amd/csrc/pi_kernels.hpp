@@ -109,6 +109,18 @@ __device__ __forceinline__ int wave_scan(int x) {
 
 // Sum over the wave, the same wave-uniform value in every lane.
 __device__ __forceinline__ float wave_sum(float v) { return lane_f(wave_scan(v), WAVE - 1); }
+
+// Maximum over the wave of non-negative values (a prefix maximum with the
+// same steps as wave_scan; lanes shifted in from outside read 0), in every lane.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<0x111>(x));
+  x = fmaxf(x, dpp_f<0x112>(x));
+  x = fmaxf(x, dpp_f<0x114>(x));
+  x = fmaxf(x, dpp_f<0x118>(x));
+  x = fmaxf(x, dpp_f<0x142, 0xa>(x));
+  x = fmaxf(x, dpp_f<0x143, 0xc>(x));
+  return lane_f(x, WAVE - 1);
+}
 __device__ __forceinline__ int wave_sum(int v) { return lane_i(wave_scan(v), WAVE - 1); }
 
 // Sum over the lanes that share lane % G (G = 1, 2, 4, 8 or 16): a scan with

@@ -108,7 +108,7 @@ def _rows(a):
     return np.atleast_2d(np.asarray(a))
 
 
-def replay_stack(host, trace, out, x0, w_dtype, act, band=BAND, end_to_end=True, seqs=None):
+def replay_stack(host, trace, out, x0, w_dtype, act, band=BAND, end_to_end=True, seqs=None, score_units=None):
     """Layer-local replay of a stack run.
 
     host: the layers (workload.LayerWeights); trace: per-layer dicts of numpy
@@ -117,7 +117,9 @@ def replay_stack(host, trace, out, x0, w_dtype, act, band=BAND, end_to_end=True,
     out: the GPU's stack output [nb][d]; x0: the stack input [nb][d].
     Every layer is gated, for every sequence or for the sequences in `seqs`
     (the union list is always checked against every sequence's mask).
-    Returns statistics.
+    score_units[l] (default 1) is the unit in which layer l's scores are
+    compared with the band: a layer fed with inputs of another magnitude has
+    scores of that magnitude.  Returns statistics.
     """
     tol = TOL[w_dtype]
     X0 = _rows(x0).astype(np.float32)
@@ -133,8 +135,9 @@ def replay_stack(host, trace, out, x0, w_dtype, act, band=BAND, end_to_end=True,
         assert np.all(np.isfinite(X)) and np.all(np.isfinite(yg))
         # predictor and threshold on the GPU's own layer input
         S = oracle.predictor_scores(h.A, h.B, oracle.predictor_bias(h), X)
+        u = 1.0 if score_units is None else float(score_units[l])
         for b in range(X.shape[0]):
-            s = check_scores_masks(S[b], scores[b], mask[b], band)
+            s = check_scores_masks(S[b] / u, scores[b].astype(np.float64) / u, mask[b], band)
             st["band"] += s["band"]
             st["band_flips"] += s["band_flips"]
             st["max_score_err"] = max(st["max_score_err"], s["max_score_err"])

@@ -236,3 +236,67 @@ def test_batch_maximum_ffn_every_neuron_active():
     for b in range(nb):
         check_y(out[b].cpu().numpy(), x_next[b], max(TOL[cfg.w_dtype], 1e-5))
 
+
+
+# ------------------------------------------------- activation range (fp16 split)
+def _scale_q4(m, factor):
+    """A Q4_0 matrix with every block scale multiplied by a power of two (exact in fp16)."""
+    s = m.scales.view(np.float16).astype(np.float32) * np.float32(factor)
+    return workload.Q4Matrix(m.nibbles, s.astype(np.float16).view(np.uint16))
+
+
+def test_batch_squared_relu_outputs_beyond_fp16_range():
+    """Q4_0 Squared ReLU at d = 12288 whose h exceeds the fp16 range (|h| > 65504):
+    the batched FFN splits each row of h into fp16 hi/lo after scaling it by a power
+    of two, so the stack still matches the oracle layer by layer."""
+    cfg = workload.CONFIGS[4].with_(act="relu2", d=12288, ffn=3001, rank=1024, n_layers=2)
+    nb = 8
+    say(f"[batch_h_range] q4 relu2 d={cfg.d} f={cfg.ffn} r={cfg.rank} batch {nb}, up scales x 64")
+    host = []
+    for l in range(cfg.n_layers):
+        lw = workload.make_layer(cfg, l, nthreads=16)
+        lw.up = _scale_q4(lw.up, 64.0)
+        host.append(lw)
+    X = workload.make_x(cfg, 2, seqs=nb)
+    # the first layer's h, from the oracle's own steps: its largest value is past fp16
+    ref = oracle.layer_forward(host[0], X)
+    act_rows = ref["idx"]
+    Z = oracle.decode_rows(host[0].up, act_rows) @ X.astype(np.float64).T + \
+        oracle.ffn_bias(host[0])[act_rows].astype(np.float64)[:, None]
+    hmax = float(np.max(np.maximum(Z, 0.0) ** 2 * ref["masks"][:, act_rows].T))
+    say(f"  layer 0: max h = {hmax:.3g}")
+    assert hmax > 65504.0
+    layers = [pi.DeviceLayer.upload(h, DEV) for h in host]
+    recs = traced_records(cfg.n_layers, nb, cfg.d, cfg.ffn)
+    out = torch.empty(nb, cfg.d, device=DEV)
+    pi.ffn_stack(layers, dev(X), out, trace=pi.make_trace(cfg.n_layers, recs), batch=nb)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    recs = to_host(recs)
+    assert np.all(np.isfinite(out))
+    st = replay_stack(host, recs, out, X, cfg.w_dtype, cfg.act)
+    say(f"  {st}")
+
+
+@pytest.mark.parametrize("factor", [1e6, 1e-12])
+def test_batch_caller_input_of_any_magnitude(factor):
+    """The stack's input enters the first layer without a glue: rows far above the fp16
+    range, or far below its normal range, are scaled by a power of two before their
+    fp16 split, so the first layer's scores and the whole stack stay in parity."""
+    cfg = SMALL["f16-relu"].with_(n_layers=2)
+    nb = 4
+    say(f"[batch_x_range] input x {factor:g}")
+    host = [workload.make_layer(cfg, l) for l in range(cfg.n_layers)]
+    # the first layer's scores scale with its input: scale its predictor bias with them
+    host[0].pbias = (oracle.predictor_bias(host[0]) * np.float32(factor)).astype(np.float32)
+    layers = [pi.DeviceLayer.upload(h, DEV) for h in host]
+    X = (workload.make_x(cfg, 5, seqs=nb) * np.float32(factor)).astype(np.float32)
+    recs = traced_records(cfg.n_layers, nb, cfg.d, cfg.ffn)
+    out = torch.empty(nb, cfg.d, device=DEV)
+    pi.ffn_stack(layers, dev(X), out, trace=pi.make_trace(cfg.n_layers, recs), batch=nb)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    recs = to_host(recs)
+    assert np.all(np.isfinite(out))
+    st = replay_stack(host, recs, out, X, cfg.w_dtype, cfg.act, score_units=[factor, 1.0])
+    say(f"  {st}")
