@@ -43,7 +43,8 @@ class PiLayer(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("ffn", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("p_dtype", ctypes.c_int32),
                 ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("bias", ctypes.c_void_p),
-                ("pbias", ctypes.c_void_p), ("gate", PiMat), ("up", PiMat), ("downT", PiMat), ("b_down", ctypes.c_void_p)]
+                ("pbias", ctypes.c_void_p), ("gate", PiMat), ("up", PiMat), ("downT", PiMat), ("b_down", ctypes.c_void_p),
+                ("hot", ctypes.c_int32)]
 
 
 class PiTrace(ctypes.Structure):
@@ -120,8 +121,9 @@ class DeviceLayer:
     """One layer's tensors resident on the GPU plus the matching pi_layer record."""
 
     def __init__(self, *, d, ffn, rank, act, w_dtype, p_dtype, A, B, bias, up, downT, gate=None,
-                 b_down=None, pbias=None):
+                 b_down=None, pbias=None, hot=0):
         self.d, self.ffn, self.rank = int(d), int(ffn), int(rank)
+        self.hot = int(hot)
         self.act, self.w_dtype, self.p_dtype = act, w_dtype, p_dtype
         self.A, self.B, self.bias, self.up, self.downT, self.gate, self.b_down = \
             A, B, bias, up, downT, gate, b_down
@@ -140,7 +142,7 @@ class DeviceLayer:
         return PiLayer(self.d, self.ffn, self.rank, _ACT[self.act], _DTYPE[self.w_dtype],
                        _DTYPE[self.p_dtype], _p(self.A), _p(self.B), _p(self.bias),
                        _p(self.pbias), self._mat(self.gate), self._mat(self.up), self._mat(self.downT),
-                       _p(self.b_down))
+                       _p(self.b_down), self.hot)
 
     @classmethod
     def upload(cls, lw, device="cuda") -> "DeviceLayer":
@@ -161,7 +163,7 @@ class DeviceLayer:
         return cls(d=cfg.d, ffn=cfg.ffn, rank=cfg.rank, act=cfg.act, w_dtype=cfg.w_dtype,
                    p_dtype=cfg.p_dtype, A=t(lw.A), B=t(lw.B), bias=t(lw.bias), up=t(lw.up),
                    downT=t(lw.downT), gate=t(lw.gate), b_down=t(lw.b_down),
-                   pbias=t(getattr(lw, "pbias", None)))
+                   pbias=t(getattr(lw, "pbias", None)), hot=int(getattr(lw, "hot", 0) or 0))
 
     def nbytes(self) -> int:
         tot = 0

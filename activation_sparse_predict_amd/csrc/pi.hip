@@ -53,6 +53,7 @@ pi_status check_layer(const pi_layer* L) {
   if (L->act == PI_REGLU && (s = check_mat(L->gate, L->w_dtype)) != PI_OK) return s;
   if (L->b_down && !aligned(L->b_down, 4)) return PI_EINVAL;
   if (L->pbias && !aligned(L->pbias, 16)) return PI_EINVAL;
+  if (L->hot < 0 || L->hot > L->ffn) return PI_EINVAL;
   return PI_OK;
 }
 
@@ -325,7 +326,7 @@ void launch_k2_t(const pi_layer* L, const K2Args& a, hipStream_t st) {
   hipLaunchKernelGGL((k_score<PT, WT, ACT, FUSE, PCH, CPL>), dim3(nb), dim3(K2_THREADS), lds, st,
                      L->B, L->pbias ? L->pbias : L->bias, L->bias, a.t_part, ks, a.ss, L->ffn, L->rank, L->gate.w,
                      L->gate.scale, L->up.w, L->up.scale, a.v, L->d, a.x_out, a.x_trace, a.scores, a.pmask, a.cnt,
-                     a.pid, a.ph, k2_cap(L->ffn));
+                     a.pid, a.ph, k2_cap(L->ffn), L->hot);
 }
 
 template <int PT, int WT, int ACT, int PCH>
@@ -530,10 +531,10 @@ void b_predict(const pi_layer* L, int batch, const Ws& W, float* scores, uint8_t
   const float* pb = L->pbias ? L->pbias : L->bias;
   if (L->p_dtype == PI_F16)
     hipLaunchKernelGGL(pib::k_bscore<DT_F16>, g2, dim3(256), 0, st, L->B, pb, L->ffn, L->rank, batch, W.th, W.tl,
-                       W.st, W.mnm, W.mask, W.cnt, scores, mask_out);
+                       W.st, W.mnm, W.mask, W.cnt, scores, mask_out, L->hot);
   else
     hipLaunchKernelGGL(pib::k_bscore<DT_F32>, g2, dim3(256), 0, st, L->B, pb, L->ffn, L->rank, batch, W.th, W.tl,
-                       W.st, W.mnm, W.mask, W.cnt, scores, mask_out);
+                       W.st, W.mnm, W.mask, W.cnt, scores, mask_out, L->hot);
   mark(tr, 4, st);
   hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, ulist, ucount, ucount2, ucount3);
   mark(tr, 5, st);

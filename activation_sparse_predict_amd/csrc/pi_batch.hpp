@@ -335,7 +335,10 @@ k_bsplit_t(const float* __restrict__ t_part, int ksplit, int r, const float* __r
 // in wave order); mask m[i][b] = (s > 0) for b < batch (0 for padded rows),
 // one byte each in neuron-major layout [ffn][32]; union u[i] = OR_b m[i][b];
 // the tile's union count to cnt_blk[block].  Optional outputs in
-// sequence-major layout: scores[b][i] and mask_out[b][i].
+// sequence-major layout: scores[b][i] and mask_out[b][i].  Neurons i < hot
+// (the hot-dense prefix) are on in every sequence without a score: a tile
+// wholly inside the prefix reads no row of B, and no score of the prefix is
+// written.
 constexpr int BS_W = 4;
 
 template <int PT>
@@ -343,7 +346,7 @@ __global__ void __launch_bounds__(BS_W * WAVE)
 k_bscore(const void* __restrict__ Bm, const float* __restrict__ pbias, int f, int r, int batch,
          const _Float16* __restrict__ th, const _Float16* __restrict__ tl, const float* __restrict__ st,
          uint8_t* __restrict__ m_nm, uint8_t* __restrict__ u, int32_t* __restrict__ cnt_blk,
-         float* __restrict__ scores, uint8_t* __restrict__ mask_out) {
+         float* __restrict__ scores, uint8_t* __restrict__ mask_out, int hot) {
   __shared__ float red[BS_W][BM * BM];
   __shared__ int cnt_w;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
@@ -352,7 +355,8 @@ k_bscore(const void* __restrict__ Bm, const float* __restrict__ pbias, int f, in
   const int i = min(i0 + col, f - 1);
   f16v acc = {};
   const int ns = r / 16, kbeg = 16 * (w * ns / BS_W), kend = 16 * ((w + 1) * ns / BS_W);
-  for (int k = kbeg; k < kend; k += 16 * KU) mfma_window<PT>(acc, th, tl, Bm, (size_t)i, r, k, kend, 16, lane);
+  if (i0 + BM > hot)                         // a tile wholly in the hot prefix reads no row of B
+    for (int k = kbeg; k < kend; k += 16 * KU) mfma_window<PT>(acc, th, tl, Bm, (size_t)i, r, k, kend, 16, lane);
 #pragma unroll
   for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -373,12 +377,12 @@ k_bscore(const void* __restrict__ Bm, const float* __restrict__ pbias, int f, in
 #pragma unroll
     for (int v = 1; v < BS_W; ++v) sacc += red[v][e];
     const float sv = sacc * (1.f / st[b]) + cb;          // the row's scale undone exactly
-    const bool on = col_ok && b < batch && sv > 0.f;
+    const bool on = col_ok && b < batch && (ii < hot || sv > 0.f);
     on_rows |= (on ? 1u : 0u) << b;
     if (col_ok) {
       m_nm[(size_t)ii * BM + b] = on ? 1 : 0;
       if (b < batch) {
-        if (scores) scores[(size_t)b * f + ii] = sv;
+        if (scores && ii >= hot) scores[(size_t)b * f + ii] = sv;
         if (mask_out) mask_out[(size_t)b * f + ii] = on ? 1 : 0;
       }
     }

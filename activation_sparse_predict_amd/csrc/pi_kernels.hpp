@@ -535,6 +535,8 @@ k_predict_t(const void* __restrict__ A, int r, int d, int KS, const float* __res
 // cnt_blk[block] = active neurons of the block, cnt_blk[nb + block] = those
 // with h != 0.  pmask (if given) gets the predictor's mask byte per neuron.
 // Block b also writes its slice of x' to x_out / x_trace (if given).
+// Hot-dense prefix: neurons i < hot are active without a prediction -- their
+// rows of B are not read, their scores not written, their mask bytes are 1.
 constexpr int K2_WAVES = 4;
 constexpr int K2_THREADS = K2_WAVES * WAVE;
 
@@ -636,7 +638,7 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
         const void* __restrict__ up_w, const uint16_t* __restrict__ up_sc,
         const float* __restrict__ vx, int d, float* __restrict__ x_out, float* __restrict__ x_trace,
         float* __restrict__ scores, uint8_t* __restrict__ pmask, int32_t* __restrict__ cnt_blk,
-        int32_t* __restrict__ pair_id, float* __restrict__ pair_h, int cap) {
+        int32_t* __restrict__ pair_id, float* __restrict__ pair_h, int cap, int hot) {
   constexpr int RB = 16 / PCH;                               // rows of B per batch
   constexpr int PEPL = Tr<PT>::EPL, PTW = WAVE * PEPL;
   constexpr int NMAT = act_nmat<ACT>();
@@ -649,6 +651,7 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
   const int M = g < f ? (f - 1 - g) / NW + 1 : 0;            // neurons of this wave
   const int Mb = b < f ? (f - 1 - b) / NW + 1 : 0;           // wave 0 has the most: block-uniform trip count
   const int Mw = (f + NW - 1) / NW;                          // list capacity per wave (= Mb of block 0)
+  const int mh = hot > g ? min(M, (hot - 1 - g) / NW + 1) : 0;   // the wave's neurons in the hot prefix
   const int dpr = dma_pad(r);
   float* ts = smem;                                          // the slices of t, then t [KS][dma_pad(r)]
   int* act = reinterpret_cast<int*>(smem + (size_t)KS * dpr);   // [K2_WAVES][Mw] active lists
@@ -695,7 +698,7 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
   float vk = 0.f;
   if (wx && kx0 + tid < kx1) vk = vx[kx0 + tid];
   PI_ISSUE_FENCE();
-  issue(0, 0, opaque_zero());
+  issue(mh, 0, opaque_zero());
   XReg<WT, CPL> xr;
   if constexpr (FUSE) load_xreg<WT, CPL>(xr, vx, nch, tid);
   PI_ISSUE_FENCE();
@@ -729,8 +732,13 @@ k_score(const void* __restrict__ Bm, const float* __restrict__ pbias, const floa
     if (x_trace) x_trace[kx0 + tid] = xk;
   }
 
-  int n_w = 0;                                               // this wave's active neurons so far
-  for (int m0 = 0; m0 < Mb; m0 += RB) {
+  // the hot prefix: active without a score (no row of B is read, no score written)
+  for (int m = lane; m < mh; m += WAVE) {
+    act[w * Mw + m] = g + NW * m;
+    if (pmask) pmask[g + NW * m] = 1;
+  }
+  int n_w = mh;                                              // this wave's active neurons so far
+  for (int m0 = mh; m0 < Mb; m0 += RB) {
     float acc[RB];
 #pragma unroll
     for (int u = 0; u < RB; ++u) acc[u] = 0.f;

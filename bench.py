@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--batch", type=int, default=1, help="sequences per decode step (1..32)")
     ap.add_argument("--layers", type=int, default=0, help="override the number of layers (0 = all)")
     ap.add_argument("--order", default="hot_first", choices=["hot_first", "identity"])
+    ap.add_argument("--hot", default="0",
+                    help="hot-dense prefix per layer: 0 (off), auto (the byte model's prefix, "
+                         "workload.hot_count) or a slot count")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="CPU oracle budget (the first layers of the first timed tokens); 0 = skip")
     ap.add_argument("--cpu-tokens", type=int, default=1, help="timed tokens the CPU oracle runs")
@@ -100,7 +103,7 @@ def sizes(cfg):
     return pb, wb, n_mat
 
 
-def kernel_bytes(cfg, batch, k, k_nz=None):
+def kernel_bytes(cfg, batch, k, k_nz=None, hot=0):
     """Algorithmic HBM bytes of one launch of each kernel of a layer, k active (union) neurons.
 
     Dense predictor (A, B) and its bias, the active rows of gate/up with their
@@ -110,6 +113,9 @@ def kernel_bytes(cfg, batch, k, k_nz=None):
     inactive neurons, scratch buffers and re-reads are not counted.  The
     per-kernel figures sum to the per-layer formula
     (r*d + f*r)*pb + 4f + k*((n_mat-1)*d*wb + 4) + k_nz*(d*wb + 4) + 8*d*B.
+    With a hot-dense prefix of `hot` slots, only the tail's rows of B and
+    predictor biases are read (f - hot rows at batch 1; at batch > 1 the
+    32-neuron tiles not wholly inside the prefix), and k includes the prefix.
     """
     pb, wb, n_mat = sizes(cfg)
     d, f, r = cfg.d, cfg.ffn, cfg.rank
@@ -117,16 +123,18 @@ def kernel_bytes(cfg, batch, k, k_nz=None):
     if k_nz is None:
         k_nz = k
     if batch == 1:
+        fp = f - hot
         return {"k_predict_t": r * d * pb + 8 * d,
-                "k_score": f * r * pb + 4 * f + k * (n_up * d * wb + 4),
+                "k_score": fp * r * pb + 4 * fp + k * (n_up * d * wb + 4),
                 "k_down": k_nz * d * wb + 4 * k_nz}
+    fp = f - 32 * (hot // 32)
     return {"k_bglue": 8 * d * batch, "k_bpred1": r * d * pb, "k_bsplit_t": 0,
-            "k_bscore": f * r * pb + 4 * f, "k_compact": 0,
+            "k_bscore": fp * r * pb + 4 * fp, "k_compact": 0,
             "k_bup": k * (n_up * d * wb + 4), "k_bdown": k * d * wb + 4 * k}
 
 
-def layer_bytes(cfg, k, batch=1, k_nz=None):
-    return float(sum(kernel_bytes(cfg, batch, k, k_nz).values()))
+def layer_bytes(cfg, k, batch=1, k_nz=None, hot=0):
+    return float(sum(kernel_bytes(cfg, batch, k, k_nz, hot).values()))
 
 
 def copy_bandwidth(torch, dev, stream, mib=1024, reps=5):
@@ -282,7 +290,8 @@ def summarize_traffic(fetch_csv, write_csv, counts_json, kernel, commands, out, 
     w_raw, _ = vals["WRITE_SIZE"][kernel]
     # every pass of the profiled program: the eager warm-up (token 0), then the tokens
     passes = [0] + list(range(len(cj["counts"])))
-    alg = statistics.mean(kernel_bytes(cfg, batch, cj["counts"][t][l], cj["nz_counts"][t][l])[kernel]
+    hots = cj.get("hots", [0] * cj["layers"])
+    alg = statistics.mean(kernel_bytes(cfg, batch, cj["counts"][t][l], cj["nz_counts"][t][l], hots[l])[kernel]
                           for t in passes for l in range(cj["layers"]))
     rd, wr = f_raw * f_scale * 1024, w_raw * w_scale * 1024
     tr = rd + wr
@@ -384,8 +393,11 @@ def main():
     cpu_seqs = [(W + t, b) for t in range(K) for b in range(B)][:max(1, args.cpu_tokens)]
     x_cpu = np.stack([xs_host[t][b] for t, b in cpu_seqs]).astype(np.float64) if args.cpu_seconds > 0 else None
     cpu_time, cpu_layers = 0.0, 0
+    hots = []
     for l in range(L):
         lw = workload.make_layer(cfg, l, order=args.order, nthreads=nthr)
+        lw.hot = workload.hot_count(cfg, lw.p_storage) if args.hot == "auto" else int(args.hot)
+        hots.append(lw.hot)
         layers.append(pi.DeviceLayer.upload(lw, dev))
         if x_cpu is not None and cpu_layers == l and cpu_time < args.cpu_seconds:
             tc0 = time.perf_counter()
@@ -471,7 +483,7 @@ def main():
             if not ev_full[t]:
                 pair_ends[key] = evs[0].elapsed_ms(evs[n_ev - 1])
                 continue
-            kb = kernel_bytes(cfg, B, int(cnt_rep[t, ev_layer[t]]), int(nz_rep[t, ev_layer[t]]))
+            kb = kernel_bytes(cfg, B, int(cnt_rep[t, ev_layer[t]]), int(nz_rep[t, ev_layer[t]]), hots[ev_layer[t]])
             iv = [evs[i].elapsed_ms(evs[i + 1]) for i in range(len(kernels))]
             pair_full[key] = sum(iv)
             for i, k in enumerate(kernels):
@@ -488,8 +500,9 @@ def main():
             json.dump({"workload": cfg.name, "config": args.config, "layers": L, "batch": B,
                        "warmup": W, "steps": K, "repeats": args.repeats, "calib_mb": args.calib_copy_mb,
                        "counts": counts.cpu().numpy().tolist(),
-                       "nz_counts": nz_counts.cpu().numpy().tolist()}, fh)
-    step_bytes = float(sum(layer_bytes(cfg, int(k), B, int(z)) for k, z in zip(cnt.ravel(), cnt_nz.ravel()))) / K
+                       "nz_counts": nz_counts.cpu().numpy().tolist(), "hots": hots}, fh)
+    step_bytes = float(sum(layer_bytes(cfg, int(cnt[t, l]), B, int(cnt_nz[t, l]), hots[l])
+                           for t in range(K) for l in range(L))) / K
     stack_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     copy_gbs = copy_bandwidth(torch, dev, stream)
     log(f"[bench] device copy in this run: {copy_gbs:.1f} GB/s (read + write); the step reaches "
@@ -582,7 +595,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "layers": L, "d": cfg.d, "ffn": cfg.ffn,
                    "rank": cfg.rank, "batch": B, "act": cfg.act, "w_dtype": cfg.w_dtype,
-                   "p_dtype": cfg.p_dtype, "order": args.order, "mean_active": mean_active,
+                   "p_dtype": cfg.p_dtype, "order": args.order, "hot_prefix": args.hot,
+                   "hot_mean": float(np.mean(hots)), "mean_active": mean_active,
                    "down_rows_read_share": nz_share,
                    "graphs": not args.eager, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": dk["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PI_ABI_VERSION 4
+#define PI_ABI_VERSION 5
 
 typedef enum {
   PI_OK = 0,
@@ -98,6 +98,15 @@ typedef struct {
   pi_mat downT;     /* [ffn][d]; row i is column i of W_down, so the down projection
                        over active neurons is a row gather too */
   const float* b_down; /* [d] or NULL */
+  int32_t hot;      /* hot-dense prefix, 0 <= hot <= ffn (else PI_EINVAL): storage slots
+                       [0, hot) -- the hottest neurons after the hot-first permutation --
+                       are active for every token and sequence without a prediction (their
+                       rows of B are never read, their scores are not written, their mask
+                       bytes are 1); only the cold tail [hot, ffn) is predicted and
+                       gathered.  0 = every neuron is predicted.  The on-GPU form of the
+                       hot/cold neuron split (PowerInfer repository README, "hot-activated
+                       neurons"; unite.ai article, "Neuronen-Platzierung und -Verwaltung";
+                       机器之心 article, hot/cold neuron paragraph). */
 } pi_layer;
 
 /* Optional per-layer record written by pi_ffn_stack (any field may be NULL). */

@@ -24,6 +24,14 @@ What it computes (per layer, per sequence b, x_b in R^d):
       ambiguity band.  The decision is taken on the score rounded to float32,
       the precision the GPU takes it in; rounding never changes the sign of a
       non-zero double.
+  hot prefix  m_i = 1 for storage slots i < hot, whatever s_i is     (``hot_prefix``)
+      Optional (hot = 0: off).  The hottest neurons are placed first by the
+      hot-first permutation and computed for every token without a
+      prediction -- the on-GPU form of the pages' hot/cold neuron split
+      (PowerInfer repository README, hot-activated neurons; unite.ai article,
+      "Neuronen-Platzierung und -Verwaltung"; 机器之心 article, hot/cold
+      paragraph).  Where the predictor would have switched such a neuron off,
+      its h = act(.) is added anyway, so the result changes there.
   list        ascending storage ids i with m_i = 1 (union over b)  (``active_list``)
       Only neuron ids are listed; weights are never converted into a sparse
       format (unite.ai, "Neuronenbewusster Operator").
@@ -111,6 +119,13 @@ def active_list(mask_1d) -> np.ndarray:
         if m:
             out.append(i)
     return np.asarray(out, dtype=np.int64)
+
+
+def hot_prefix(masks, hot: int) -> np.ndarray:
+    """Masks with the first ``hot`` storage slots on in every sequence."""
+    M = np.array(np.atleast_2d(masks), dtype=bool, copy=True)
+    M[:, :int(hot)] = True
+    return M
 
 
 def union_mask(masks) -> np.ndarray:
@@ -229,12 +244,16 @@ def layer_forward(layer, X, act: str | None = None) -> dict:
     """One layer for a batch of sequences X [nb][d].
 
     Returns scores (float64), masks (per sequence), the ascending union list,
-    its count and y (float64).
+    its count and y (float64).  A layer with ``hot`` > 0 has its first ``hot``
+    neurons on without a prediction (their scores are still returned).
     """
     act = act or _get(layer, "act") or _get(_get(layer, "cfg"), "act")
     X = np.atleast_2d(np.asarray(X, dtype=np.float64))
     S = predictor_scores(_get(layer, "A"), _get(layer, "B"), predictor_bias(layer), X)
     M = threshold(S)
+    hot = int(_get(layer, "hot") or 0)
+    if hot:
+        M = hot_prefix(M, hot)
     idx = active_list(union_mask(M))
     Y = sparse_ffn(act, _get(layer, "gate"), _get(layer, "up"), _get(layer, "downT"),
                    ffn_bias(layer), X, M, _get(layer, "b_down"))

@@ -119,7 +119,9 @@ def replay_stack(host, trace, out, x0, w_dtype, act, band=BAND, end_to_end=True,
     (the union list is always checked against every sequence's mask).
     score_units[l] (default 1) is the unit in which layer l's scores are
     compared with the band: a layer fed with inputs of another magnitude has
-    scores of that magnitude.  Returns statistics.
+    scores of that magnitude.  A layer with a hot-dense prefix (``hot`` > 0)
+    must have its first ``hot`` mask bytes set; their scores are not written by
+    the GPU and are not compared.  Returns statistics.
     """
     tol = TOL[w_dtype]
     X0 = _rows(x0).astype(np.float32)
@@ -136,8 +138,10 @@ def replay_stack(host, trace, out, x0, w_dtype, act, band=BAND, end_to_end=True,
         # predictor and threshold on the GPU's own layer input
         S = oracle.predictor_scores(h.A, h.B, oracle.predictor_bias(h), X)
         u = 1.0 if score_units is None else float(score_units[l])
+        hot = int(getattr(h, "hot", 0) or 0)
+        assert np.all(mask[:, :hot] == 1), "the hot prefix is on in every sequence"
         for b in range(X.shape[0]):
-            s = check_scores_masks(S[b] / u, scores[b].astype(np.float64) / u, mask[b], band)
+            s = check_scores_masks(S[b, hot:] / u, scores[b, hot:].astype(np.float64) / u, mask[b, hot:], band)
             st["band"] += s["band"]
             st["band_flips"] += s["band_flips"]
             st["max_score_err"] = max(st["max_score_err"], s["max_score_err"])

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(pi):
 
 
 def test_abi_version_and_status_strings(pi):
-    assert pi.abi_version() == 4
+    assert pi.abi_version() == 5
     assert pi.status_str(0) == "ok"
     assert "workspace" in pi.status_str(3)
 
@@ -56,7 +56,7 @@ def make_layer(pi, **kw):
     base.update(kw)
     L = pi.PiLayer(base["d"], base["ffn"], base["rank"], base["act"], base["w_dtype"],
                    base["p_dtype"], FAKE, FAKE, FAKE, None, pi.PiMat(None, None), pi.PiMat(FAKE, None),
-                   pi.PiMat(FAKE, None), None)
+                   pi.PiMat(FAKE, None), None, base.get("hot", 0))
     for k in ("gate", "up", "downT"):
         if k in kw:
             setattr(L, k, kw[k])
@@ -94,6 +94,7 @@ def test_workspace_bytes(pi):
     (dict(w_dtype=2), 1),                              # Q4_0 without scales
     (dict(d=16384 + 64), 2), (dict(rank=4096 + 64), 2),  # beyond the LDS staging limits
     (dict(ffn=(1 << 21) + 1), 2),                      # beyond the score kernel's LDS lists
+    (dict(hot=-1), 1), (dict(hot=1001), 1),             # hot prefix outside [0, ffn]
 ])
 def test_predict_rejects_bad_layers(pi, kw, status):
     assert predict(pi, make_layer(pi, **kw)) == status

@@ -103,3 +103,16 @@ def test_summarize_traffic(tmp_path):
     # passes: token 0 (warm-up), then tokens 0 and 1; layers 0 and 1
     alg = [bench.kernel_bytes(cfg, 1, counts[t][l], nz[t][l])["k_down"] for t in (0, 0, 1) for l in (0, 1)]
     assert float(kv["alg_bytes_per_launch"].strip("`")) == pytest.approx(sum(alg) / len(alg))
+
+
+def test_hot_prefix_bytes():
+    """A hot-dense prefix drops its rows of B and predictor biases from the score
+    kernel's bytes (batch 1: every prefix slot; batch > 1: whole 32-neuron tiles)."""
+    cfg = workload.CONFIGS[4]
+    pb = 2
+    a, b = bench.kernel_bytes(cfg, 1, 4000, 3900), bench.kernel_bytes(cfg, 1, 4000, 3900, hot=1109)
+    assert a["k_score"] - b["k_score"] == 1109 * (cfg.rank * pb + 4)
+    assert a["k_down"] == b["k_down"] and a["k_predict_t"] == b["k_predict_t"]
+    a, b = bench.kernel_bytes(cfg, 32, 5000), bench.kernel_bytes(cfg, 32, 5000, hot=77)
+    assert a["k_bscore"] - b["k_bscore"] == 64 * (cfg.rank * pb + 4)
+

@@ -300,3 +300,36 @@ def test_batch_caller_input_of_any_magnitude(factor):
     assert np.all(np.isfinite(out))
     st = replay_stack(host, recs, out, X, cfg.w_dtype, cfg.act, score_units=[factor, 1.0])
     say(f"  {st}")
+
+
+def test_batch_hot_prefix():
+    """Batched path with a hot-dense prefix: the prefix is on for every sequence (and
+    in the union), no prefix score is written, and the stack replays layer by layer."""
+    cfg = SMALL["q4-relu"].with_(n_layers=2)
+    nb, hot = 8, 77                      # a tile of 32 wholly hot, and one partly
+    say(f"[batch_hot] q4 relu batch {nb} hot {hot}")
+    host = [workload.make_layer(cfg, l) for l in range(cfg.n_layers)]
+    for h in host:
+        h.hot = hot
+    layers = [pi.DeviceLayer.upload(h, DEV) for h in host]
+    X = workload.make_x(cfg, 13, seqs=nb)
+    recs = traced_records(cfg.n_layers, nb, cfg.d, cfg.ffn)
+    for r in recs:
+        r["scores"].fill_(float("nan"))
+    out = torch.empty(nb, cfg.d, device=DEV)
+    pi.ffn_stack(layers, dev(X), out, trace=pi.make_trace(cfg.n_layers, recs), batch=nb)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    recs = to_host(recs)
+    for r in recs:
+        assert np.all(r["mask"][:, :hot] == 1) and not np.isfinite(r["scores"][:, :hot]).any()
+    st = replay_stack(host, recs, out, X, cfg.w_dtype, cfg.act)
+    say(f"  {st}")
+    # the batched predictor on its own
+    scores, mask, idx, count = run_predict(layers[0], X)
+    ref = oracle.layer_forward(host[0], X)
+    assert np.all(mask[:, :hot] == 1) and not np.isfinite(scores[:, :hot]).any()
+    for b in range(nb):
+        check_scores_masks(ref["scores"][b][hot:], scores[b][hot:], mask[b][hot:])
+    check_list(mask.astype(bool).any(axis=0), idx, count)
+

@@ -404,3 +404,51 @@ def test_maximum_width_and_rank(name):
     say(f"  count {count}, stack {st}")
     del layers
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------ hot-dense prefix
+@pytest.mark.parametrize("name,hot", [("q4-relu", 300), ("f16-reglu", 257), ("f16-relu2", 1)])
+def test_stack_hot_prefix(name, hot):
+    """Slots [0, hot) are on without a prediction in every layer: their mask bytes are
+    1, their scores are left untouched (the buffers start at 0), and each layer's y
+    is the oracle's on the GPU's own input and mask (which now includes the hot prefix)."""
+    cfg = SMALL[name]
+    say(f"[hot] {name} hot {hot}")
+    host = host_layers(cfg)
+    for h in host:
+        h.hot = hot
+    layers = [pi.DeviceLayer.upload(h, DEV) for h in host]
+    x = workload.make_x(cfg, 21)
+    out, trace = run_stack_traced(layers, x[0], cfg)
+    for t in trace:
+        assert np.all(t["mask"][:hot] == 1) and t["count"] >= hot
+        assert np.array_equal(t["idx"][:hot], np.arange(hot))
+        assert np.all(t["scores"][:hot] == 0)                     # untouched: left as the buffer's fill
+    st = replay_stack(host, trace, out, x, cfg.w_dtype, cfg.act)
+    say(f"  {st}")
+    # single-layer predictor: the same prefix, and the tail's scores
+    L = layers[0]
+    scores, mask, idx, count = run_predict(L, x[0])
+    assert np.all(mask[:hot] == 1) and np.all(scores[:hot] == 0)
+    ref = oracle.layer_forward(host[0], x)
+    check_scores_masks(ref["scores"][0][hot:], scores[hot:], mask[hot:])
+    check_list(mask.astype(bool), idx, count)
+
+
+@pytest.mark.timeout(600)
+def test_full_size_stack_hot_prefix():
+    """The OPT-175B-shaped Q4_0 stack with the byte model's hot prefix (hot_count)."""
+    cfg = workload.CONFIGS[4]
+    n_layers = 2
+    host = [workload.make_layer(cfg, l, nthreads=16) for l in range(n_layers)]
+    for h in host:
+        h.hot = workload.hot_count(cfg, h.p_storage)
+    say(f"[full_hot] config 4: {n_layers} layers, hot {[h.hot for h in host]}")
+    layers = [pi.DeviceLayer.upload(h, DEV) for h in host]
+    x = workload.make_x(cfg, 3)
+    out, trace = run_stack_traced(layers, x[0], cfg)
+    st = replay_stack(host, trace, out, x, cfg.w_dtype, cfg.act)
+    say(f"  counts {[t['count'] for t in trace]}; {st}")
+    del layers
+    torch.cuda.empty_cache()
+

@@ -41,7 +41,8 @@ def tiny_layer(rng, d, f, r, act="relu", scale=1.0, pbias=False):
 
 # ---------------------------------------------------------------- exact brute force
 def frac_layer(L, x):
-    """The layer in exact rational arithmetic, following the definitions step by step."""
+    """The layer in exact rational arithmetic, following the definitions step by step
+    (with a hot-dense prefix: slots i < L["hot"] are on whatever their score)."""
     A, B, bias = L["A"], L["B"], L["bias"]
     # the predictor's own output bias c where the layer has one, else b
     c = L.get("pbias") if L.get("pbias") is not None else bias
@@ -51,7 +52,8 @@ def frac_layer(L, x):
     t = [sum(Fraction(float(A[j, k])) * X[k] for k in range(d)) for j in range(r)]
     s = [Fraction(float(c[i])) + sum(Fraction(float(B[i, j])) * t[j] for j in range(r))
          for i in range(f)]
-    m = [v > 0 for v in s]
+    hot = int(L.get("hot", 0) or 0)
+    m = [i < hot or v > 0 for i, v in enumerate(s)]
     y = [Fraction(0)] * d
     for i in range(f):
         if not m[i]:
@@ -368,3 +370,46 @@ def test_planted_mistake_is_caught(monkeypatch, gen, name, fn):
         except (AssertionError, ValueError, IndexError):
             caught += 1
     assert caught > 0, f"no pin catches the planted mistake in {name}"
+
+
+# -------------------------------------------------------------- hot-dense prefix
+@pytest.mark.parametrize("act", ["relu", "reglu", "relu2"])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_hot_prefix_matches_exact_rationals(act, seed):
+    """Slots [0, hot) are on without a prediction; the tail follows the threshold.
+    The case is drawn so that the prefix holds a neuron the predictor switches off
+    whose activation is non-zero, i.e. the prefix changes y."""
+    rng = np.random.default_rng(100 + seed)
+    d, f, r = 12, 10, 5
+    for _ in range(200):
+        L = tiny_layer(rng, d, f, r, act)
+        x = (rng.integers(-64, 65, size=d) / 16.0).astype(np.float32)
+        L["hot"] = 4
+        s_ex, m_ex, y_ex = frac_layer(L, x)
+        plain = dict(L, hot=0)
+        _, m_plain, y_plain = frac_layer(plain, x)
+        if m_plain[:4] != [True] * 4 and y_ex != y_plain and any(m_plain[4:]) and not all(m_plain[4:]):
+            break
+    else:
+        pytest.skip("no case with a changed y found")
+    out = oracle.layer_forward(L, x[None, :])
+    np.testing.assert_allclose(out["scores"][0], [float(v) for v in s_ex], rtol=0, atol=1e-12)
+    assert out["masks"][0].tolist() == m_ex
+    assert out["masks"][0][:4].all()
+    assert out["idx"].tolist() == [i for i in range(f) if m_ex[i]]
+    y_ref = np.array([float(v) for v in y_ex])
+    np.testing.assert_allclose(out["y"][0], y_ref, rtol=0, atol=1e-11 * max(1.0, np.abs(y_ref).max()))
+
+
+def test_hot_prefix_over_every_neuron_is_the_dense_ffn():
+    """hot = ffn: every neuron is on, so y is the dense FFN (a plain product over all
+    neurons), whatever the predictor says."""
+    rng = np.random.default_rng(7)
+    d, f, r = 16, 24, 8
+    L = tiny_layer(rng, d, f, r, "reglu")
+    L["hot"] = f
+    X = rng.standard_normal((3, d))
+    out = oracle.layer_forward(L, X)
+    assert out["masks"].all() and out["count"] == f
+    dense = oracle.dense_ffn("reglu", L["gate"], L["up"], L["downT"], L["bias"], X)
+    np.testing.assert_allclose(out["y"], dense, rtol=1e-12, atol=1e-12)

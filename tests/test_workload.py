@@ -121,3 +121,15 @@ def test_fig8_fixture_is_readable():
     with open(os.path.join(GOLDEN, "fig8_fixture.json")) as fh:
         fx = json.load(fh)
     assert fx["ffn"] == 8 and fx["skipped_hot"] == [7]
+
+
+def test_hot_count_follows_the_byte_model(gen):
+    """The prefix ends at the first slot whose p is below 1 - r pb / (n_in d wb)."""
+    cfg = gen.CONFIGS[4]                       # Q4_0 ReLU: 1 - 1024*2 / (12288 * 18/32)
+    p_min = 1.0 - cfg.rank * 2.0 / (cfg.d * 18.0 / 32.0)
+    ps = np.array([0.9, 0.8, p_min + 1e-9, p_min - 1e-9, 0.9, 0.1])
+    assert gen.hot_count(cfg, ps) == 3
+    assert gen.hot_count(cfg, np.array([0.1, 0.9])) == 0
+    assert gen.hot_count(cfg, np.array([0.95, 0.99])) == 2
+    c1 = gen.CONFIGS[1]                        # ReGLU fp16: two input rows per neuron
+    assert gen.hot_count(c1, np.array([1.0 - 1024 * 2.0 / (2 * 4096 * 2.0) + 1e-9, 0.0])) == 1

@@ -261,6 +261,7 @@ class LayerWeights:
     gate: object = None    # ReGLU only
     b_down: Optional[np.ndarray] = None
     pbias: Optional[np.ndarray] = None   # float32 [ffn], storage order
+    hot: int = 0                         # hot-dense prefix length (storage slots [0, hot))
 
     @property
     def p_storage(self) -> np.ndarray:
@@ -318,3 +319,20 @@ def make_x(cfg: FFNConfig, token: int, seqs: int = 1, stream: int = 0) -> np.nda
 def make_tokens(cfg: FFNConfig, n_tokens: int, seqs: int = 1, first: int = 0) -> np.ndarray:
     """float32 [n_tokens][seqs][d]."""
     return np.stack([make_x(cfg, first + t, seqs) for t in range(n_tokens)])
+
+
+def hot_count(cfg: FFNConfig, p_storage: np.ndarray) -> int:
+    """Length of a hot-dense prefix for a layer: the leading storage slots
+    (hot-first order) whose firing probability makes computing them for every
+    token cheaper in bytes than predicting them.  Predicted, neuron i costs its
+    row of B (r * pb bytes) and, with probability p_i, its up/gate rows
+    (n_in * d * wb); computed for every token it costs those rows always (the
+    down row is read only when h != 0, either way).  So the prefix holds the
+    neurons with n_in * d * wb * (1 - p_i) < r * pb."""
+    pb = 4.0 if cfg.p_dtype == "f32" else 2.0
+    wb = {"f32": 4.0, "f16": 2.0, "q4_0": 18.0 / 32.0}[cfg.w_dtype]
+    n_in = 2 if cfg.act == "reglu" else 1
+    p_min = 1.0 - cfg.rank * pb / (n_in * cfg.d * wb)
+    ps = np.asarray(p_storage, dtype=np.float64)
+    below = np.flatnonzero(ps < p_min)
+    return int(below[0]) if below.size else int(ps.size)
