@@ -44,7 +44,7 @@ class PiLayer(ctypes.Structure):
                 ("act", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("p_dtype", ctypes.c_int32),
                 ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("bias", ctypes.c_void_p),
                 ("pbias", ctypes.c_void_p), ("gate", PiMat), ("up", PiMat), ("downT", PiMat), ("b_down", ctypes.c_void_p),
-                ("hot", ctypes.c_int32)]
+                ("hot", ctypes.c_int32), ("dense_frac", ctypes.c_float)]
 
 
 class PiTrace(ctypes.Structure):
@@ -121,9 +121,10 @@ class DeviceLayer:
     """One layer's tensors resident on the GPU plus the matching pi_layer record."""
 
     def __init__(self, *, d, ffn, rank, act, w_dtype, p_dtype, A, B, bias, up, downT, gate=None,
-                 b_down=None, pbias=None, hot=0):
+                 b_down=None, pbias=None, hot=0, dense_frac=0.0):
         self.d, self.ffn, self.rank = int(d), int(ffn), int(rank)
         self.hot = int(hot)
+        self.dense_frac = float(dense_frac)
         self.act, self.w_dtype, self.p_dtype = act, w_dtype, p_dtype
         self.A, self.B, self.bias, self.up, self.downT, self.gate, self.b_down = \
             A, B, bias, up, downT, gate, b_down
@@ -142,7 +143,7 @@ class DeviceLayer:
         return PiLayer(self.d, self.ffn, self.rank, _ACT[self.act], _DTYPE[self.w_dtype],
                        _DTYPE[self.p_dtype], _p(self.A), _p(self.B), _p(self.bias),
                        _p(self.pbias), self._mat(self.gate), self._mat(self.up), self._mat(self.downT),
-                       _p(self.b_down), self.hot)
+                       _p(self.b_down), self.hot, self.dense_frac)
 
     @classmethod
     def upload(cls, lw, device="cuda") -> "DeviceLayer":
@@ -163,7 +164,8 @@ class DeviceLayer:
         return cls(d=cfg.d, ffn=cfg.ffn, rank=cfg.rank, act=cfg.act, w_dtype=cfg.w_dtype,
                    p_dtype=cfg.p_dtype, A=t(lw.A), B=t(lw.B), bias=t(lw.bias), up=t(lw.up),
                    downT=t(lw.downT), gate=t(lw.gate), b_down=t(lw.b_down),
-                   pbias=t(getattr(lw, "pbias", None)), hot=int(getattr(lw, "hot", 0) or 0))
+                   pbias=t(getattr(lw, "pbias", None)), hot=int(getattr(lw, "hot", 0) or 0),
+                   dense_frac=float(getattr(lw, "dense_frac", 0.0) or 0.0))
 
     def nbytes(self) -> int:
         tot = 0

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -540,16 +541,23 @@ void b_predict(const pi_layer* L, int batch, const Ws& W, float* scores, uint8_t
   mark(tr, 5, st);
 }
 
+// The union size from which the batched FFN runs over every neuron.
+int dense_min(const pi_layer* L) {
+  const float fr = (L->dense_frac > 0.f) ? L->dense_frac : PI_DENSE_FRAC_DEFAULT;   // NaN: the default
+  if (fr > 1.f) return L->ffn + 1;
+  return std::max(1, (int)std::ceil((double)fr * L->ffn));
+}
+
 template <int WT, int ACT>
 void b_ffn_t(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, const int32_t* ucount, float* y,
              hipStream_t st, const pi_trace* tr) {
   hipLaunchKernelGGL((pib::k_bup<WT, ACT>), dim3(cdiv(L->ffn, kBatchM)), dim3(pib::BUP_W * WAVE), 0, st, L->gate.w,
                      L->gate.scale, L->up.w, L->up.scale, L->bias, L->ffn, L->d, W.xh, W.xl, ulist, ucount, W.mnm,
-                     W.sx, W.h32, W.hmax);
+                     W.sx, W.h32, W.hmax, dense_min(L));
   mark(tr, 6, st);
   hipLaunchKernelGGL(pib::k_bdown<WT>, dim3(cdiv(L->d, kBatchM * pib::bd_tiles<WT>()) * pib::BD_SPLIT), dim3(256), 0,
                      st, L->downT.w,
-                     L->downT.scale, L->ffn, L->d, ulist, ucount, W.h32, W.hmax, L->b_down, batch, y);
+                     L->downT.scale, L->ffn, L->d, ulist, ucount, W.h32, W.hmax, L->b_down, batch, y, dense_min(L));
   mark(tr, 7, st);
 }
 
@@ -778,7 +786,7 @@ pi_status pi_sparse_ffn(const pi_layer* layer, const float* x, int32_t batch, co
   if (batch > 1) {
     // the listed neurons become the union (ascending, each once) with the caller's per-sequence masks
     b_glue(x, nullptr, batch, layer->d, nullptr, nullptr, W, st);
-    hipLaunchKernelGGL(pib::k_bclear, dim3(cdiv(layer->ffn, 256)), dim3(256), 0, st, W.mask, layer->ffn);
+    hipLaunchKernelGGL(pib::k_bclear, dim3(cdiv(layer->ffn, 256)), dim3(256), 0, st, W.mask, W.mnm, layer->ffn);
     hipLaunchKernelGGL(pib::k_blist, dim3(cdiv(layer->ffn, 256)), dim3(256), 0, st, idx, count, layer->ffn, mask,
                        batch, W.mask, W.mnm);
     hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, layer->ffn, W.ulist, W.misc, nullptr, nullptr);

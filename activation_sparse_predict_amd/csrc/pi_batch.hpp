@@ -402,6 +402,16 @@ k_bscore(const void* __restrict__ Bm, const float* __restrict__ pbias, int f, in
   if (tid == 0 && cnt_blk) cnt_blk[blockIdx.x] = cnt_w;
 }
 
+// The rows the batched FFN runs over: the union list, or -- when the union
+// holds at least dense_min neurons -- every neuron in storage order (a dense
+// GEMM; neurons outside the union get h = 0 from their all-zero mask bytes).
+// Both FFN kernels take the same decision from the same device-resident count.
+__device__ __forceinline__ int ffn_rows(const int32_t* __restrict__ ucount, int f, int dense_min, bool* dense) {
+  const int n = min(max(*ucount, 0), f);
+  *dense = n >= dense_min;
+  return *dense ? f : n;
+}
+
 // ------------------------------------------------------------ up / gate
 // z = X W^T over the union rows.  Block q covers union list entries [32 q,
 // 32 q + 32) (blocks past the union's end return); its BUP_W waves split K
@@ -424,16 +434,17 @@ k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, con
       const uint16_t* __restrict__ up_sc, const float* __restrict__ bias, int f, int d,
       const _Float16* __restrict__ xh, const _Float16* __restrict__ xl, const int32_t* __restrict__ ulist,
       const int32_t* __restrict__ ucount, const uint8_t* __restrict__ m_nm, const float* __restrict__ sx,
-      float* __restrict__ h32, uint32_t* __restrict__ hmax) {
+      float* __restrict__ h32, uint32_t* __restrict__ hmax, int dense_min) {
   constexpr int NMAT = act_nmat<ACT>();
   __shared__ float red[BUP_W][NMAT][BM * BM];
   __shared__ uint32_t rmax[BM];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int col = lane % 32, half = lane / 32;
-  const int n = min(max(*ucount, 0), f);
+  bool dense;
+  const int n = ffn_rows(ucount, f, dense_min, &dense);
   const int t0 = blockIdx.x * BM;
   if (t0 >= n) return;                                        // block-uniform
-  const int row = ulist[min(t0 + col, n - 1)];
+  const int row = dense ? min(t0 + col, n - 1) : ulist[min(t0 + col, n - 1)];
   f16v acc[NMAT];
 #pragma unroll
   for (int mt = 0; mt < NMAT; ++mt) acc[mt] = f16v{};
@@ -511,7 +522,7 @@ k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, con
       for (int v = 0; v < BUP_W; ++v) s += red[v][mt][e];
       z[mt] = s * ix;
     }
-    const int rw = ulist[t0 + c];
+    const int rw = dense ? t0 + c : ulist[t0 + c];
     float h = act_h<ACT>(z[0], bias[rw], z[NMAT - 1]);
     if (m_nm[(size_t)rw * BM + b] == 0) h = 0.f;
     h32[aop(b, t0 + c)] = h;
@@ -548,7 +559,7 @@ __global__ void __launch_bounds__(256)
 k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int f, int d,
         const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount, const float* __restrict__ h32,
         const uint32_t* __restrict__ hmax, const float* __restrict__ b_down, int batch,
-        float* __restrict__ y_part) {
+        float* __restrict__ y_part, int dense_min) {
   constexpr int NW = (WT == DT_F16) ? 1 : 2;      // weight tiles: hi (and lo for fp32 and Q4_0)
   constexpr int NT = bd_tiles<WT>();               // 32-column tiles of this block
   // The weight tiles [NW][column][position] and, after the last chunk, the
@@ -570,7 +581,8 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
   const bool xcd = WT != DT_Q4 && nblk % 8 == 0;
   const int lb = xcd ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)blockIdx.x / 8 : (int)blockIdx.x;
   const int c0 = (lb % ntile) * NT * BM, split = lb / ntile;
-  const int n = min(max(*ucount, 0), f);
+  bool dense;
+  const int n = ffn_rows(ucount, f, dense_min, &dense);
   const int nch_all = (n + BD_CH - 1) / BD_CH, cps = (nch_all + BD_SPLIT - 1) / BD_SPLIT;
   const int ch0 = split * cps;                     // this split's chunks [ch0, ch0 + nch)
   const int nch = max(0, min(nch_all, ch0 + cps) - ch0);
@@ -583,7 +595,7 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
   // the split's list entries, so that no weight load waits for a list load
   {
     const int p0 = ch0 * BD_CH, np_ = min(n, (ch0 + nch) * BD_CH) - p0;
-    for (int q = tid; q < np_; q += blockDim.x) rows_l[q] = ulist[p0 + q];
+    for (int q = tid; q < np_; q += blockDim.x) rows_l[q] = dense ? p0 + q : ulist[p0 + q];
     __syncthreads();
   }
 
@@ -740,11 +752,17 @@ __global__ void k_bsum_y(const float* __restrict__ y_part, int batch, int d, flo
   y[e] = v;
 }
 
-// Explicit-list input of the batched FFN: u[i] = 1 for listed i (others 0,
-// cleared by k_bclear first) and m_nm[i][b] = mask[b][i] for b < batch.
-__global__ void k_bclear(uint8_t* __restrict__ u, int f) {
+// Explicit-list input of the batched FFN: u[i] = 1 for listed i and m_nm[i][b]
+// = mask[b][i] for b < batch; k_bclear first clears u and every row of m_nm
+// (a dense run reads the mask bytes of every neuron).
+__global__ void k_bclear(uint8_t* __restrict__ u, uint8_t* __restrict__ m_nm, int f) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < f) u[i] = 0;
+  if (i < f) {
+    u[i] = 0;
+    uint4* m = reinterpret_cast<uint4*>(m_nm + (size_t)i * BM);
+    m[0] = make_uint4(0, 0, 0, 0);
+    m[1] = make_uint4(0, 0, 0, 0);
+  }
 }
 __global__ void k_blist(const int32_t* __restrict__ idx, const int32_t* __restrict__ count, int f,
                         const uint8_t* __restrict__ mask, int batch, uint8_t* __restrict__ u,

@@ -73,6 +73,12 @@ def parse():
     ap.add_argument("--hot", default="0",
                     help="hot-dense prefix per layer: 0 (off), auto (the byte model's prefix, "
                          "workload.hot_count) or a slot count")
+    ap.add_argument("--dense-sweep", action="store_true",
+                    help="time the batched FFN (pi_sparse_ffn at --batch) over an explicit union of "
+                         "growing size, gathered and dense, and print the table (one layer of --config)")
+    ap.add_argument("--dense-frac", type=float, default=0.0,
+                    help="batch > 1: union fraction from which the FFN runs over every neuron "
+                         "(0 = the library's default, above 1 = never)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="CPU oracle budget (the first layers of the first timed tokens); 0 = skip")
     ap.add_argument("--cpu-tokens", type=int, default=1, help="timed tokens the CPU oracle runs")
@@ -330,8 +336,66 @@ def summarize_traffic(fetch_csv, write_csv, counts_json, kernel, commands, out, 
         sys.stdout.write(text)
 
 
+def dense_sweep(args):
+    """Gathered against dense batched FFN on one layer: for union fractions u, an
+    explicit ascending union of round(u f) random neurons, each sequence's mask a
+    random half of it; pi_sparse_ffn with dense_frac above 1 (gathered rows) and
+    tiny (every neuron), the median of `reps` timed calls each."""
+    import numpy as np
+    import torch
+    import activation_sparse_predict_amd as pi
+    import workload
+    cfg = workload.CONFIGS[args.config]
+    B = max(2, args.batch)
+    dev = torch.device("cuda:0")
+    lw = workload.make_layer(cfg, 0, nthreads=16)
+    L = pi.DeviceLayer.upload(lw, dev)
+    del lw
+    f, d = cfg.ffn, cfg.d
+    rng = np.random.default_rng(7)
+    x = torch.from_numpy(workload.make_x(cfg, 0, seqs=B)).to(dev)
+    y = torch.empty(B, d, device=dev)
+    ws = pi.alloc_workspace(L, B)
+    stream = torch.cuda.current_stream()
+    _, wb, n_mat = sizes(cfg)
+    rows = []
+    for u in (0.3, 0.5, 0.7, 0.8, 0.9, 0.95, 1.0):
+        k = max(1, int(round(u * f)))
+        idx = np.sort(rng.choice(f, size=k, replace=False)).astype(np.int32)
+        mask = np.zeros((B, f), np.uint8)
+        mask[:, idx] = rng.random((B, k)) < 0.5
+        idx_t = torch.from_numpy(idx).to(dev)
+        cnt_t = torch.tensor([k], dtype=torch.int32, device=dev)
+        mask_t = torch.from_numpy(mask).to(dev)
+        res = {}
+        for tag, frac in (("gathered", 2.0), ("dense", 1e-6)):
+            L.struct.dense_frac = frac
+            for _ in range(3):
+                pi.sparse_ffn(L, x, idx_t, cnt_t, y, mask=mask_t, ws=ws, batch=B)
+            times = []
+            for _ in range(args.repeats * 4):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                pi.sparse_ffn(L, x, idx_t, cnt_t, y, mask=mask_t, ws=ws, batch=B)
+                e1.record(stream)
+                e1.synchronize()
+                times.append(e0.elapsed_time(e1) * 1e3)
+            res[tag] = sorted(times)[len(times) // 2]
+        ub = k * (n_mat * d * wb + 8)
+        rows.append((u, k, res["gathered"], res["dense"], ub / res["gathered"] / 1e3, ub / res["dense"] / 1e3))
+        log(f"[sweep] union {u:.2f} ({k} of {f}): gathered {res['gathered']:.1f} us, dense {res['dense']:.1f} us")
+    print(f"# batched FFN, {cfg.name}, batch {B}: pi_sparse_ffn over an explicit union, median us")
+    print("| union | rows | gathered us | dense us | gathered GB/s (union bytes) | dense GB/s (union bytes) |")
+    print("|---|---|---|---|---|---|")
+    for u, k, g, dn, gg, dg in rows:
+        print(f"| {u:.2f} | {k} | {g:.1f} | {dn:.1f} | {gg:.0f} | {dg:.0f} |")
+
+
 def main():
     args = parse()
+    if args.dense_sweep:
+        dense_sweep(args)
+        return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.title or args.summarize_trace, args.command, args.out)
         return
@@ -397,6 +461,7 @@ def main():
     for l in range(L):
         lw = workload.make_layer(cfg, l, order=args.order, nthreads=nthr)
         lw.hot = workload.hot_count(cfg, lw.p_storage) if args.hot == "auto" else int(args.hot)
+        lw.dense_frac = args.dense_frac
         hots.append(lw.hot)
         layers.append(pi.DeviceLayer.upload(lw, dev))
         if x_cpu is not None and cpu_layers == l and cpu_time < args.cpu_seconds:
@@ -596,6 +661,7 @@ def main():
         "config": {"workload": cfg.name, "layers": L, "d": cfg.d, "ffn": cfg.ffn,
                    "rank": cfg.rank, "batch": B, "act": cfg.act, "w_dtype": cfg.w_dtype,
                    "p_dtype": cfg.p_dtype, "order": args.order, "hot_prefix": args.hot,
+                   "dense_frac": args.dense_frac,
                    "hot_mean": float(np.mean(hots)), "mean_active": mean_active,
                    "down_rows_read_share": nz_share,
                    "graphs": not args.eager, "parallelism": "none (1 GPU)"},

@@ -53,7 +53,11 @@
 extern "C" {
 #endif
 
-#define PI_ABI_VERSION 5
+#define PI_ABI_VERSION 6
+
+/* Union fraction at and above which the batched FFN runs over every neuron
+ * when pi_layer.dense_frac is 0 (see pi_layer.dense_frac). */
+#define PI_DENSE_FRAC_DEFAULT 0.9f
 
 typedef enum {
   PI_OK = 0,
@@ -107,6 +111,13 @@ typedef struct {
                        hot/cold neuron split (PowerInfer repository README, "hot-activated
                        neurons"; unite.ai article, "Neuronen-Platzierung und -Verwaltung";
                        机器之心 article, hot/cold neuron paragraph). */
+  float dense_frac; /* batch > 1: when the union of the sequences' masks holds at least
+                       dense_frac * ffn neurons, the up/gate and down GEMMs run over every
+                       neuron in storage order instead of the gathered union rows (a
+                       neuron outside the union gets h = 0, so the result is the same).
+                       As the batch grows the union tends to every neuron (机器之心
+                       article, Fig. 14 paragraph).  0 (or NaN) = the library's default
+                       (PI_DENSE_FRAC_DEFAULT); a value above 1 = never. */
 } pi_layer;
 
 /* Optional per-layer record written by pi_ffn_stack (any field may be NULL). */

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(pi):
 
 
 def test_abi_version_and_status_strings(pi):
-    assert pi.abi_version() == 5
+    assert pi.abi_version() == 6
     assert pi.status_str(0) == "ok"
     assert "workspace" in pi.status_str(3)
 
@@ -56,7 +56,7 @@ def make_layer(pi, **kw):
     base.update(kw)
     L = pi.PiLayer(base["d"], base["ffn"], base["rank"], base["act"], base["w_dtype"],
                    base["p_dtype"], FAKE, FAKE, FAKE, None, pi.PiMat(None, None), pi.PiMat(FAKE, None),
-                   pi.PiMat(FAKE, None), None, base.get("hot", 0))
+                   pi.PiMat(FAKE, None), None, base.get("hot", 0), base.get("dense_frac", 0.0))
     for k in ("gate", "up", "downT"):
         if k in kw:
             setattr(L, k, kw[k])

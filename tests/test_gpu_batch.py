@@ -333,3 +333,46 @@ def test_batch_hot_prefix():
         check_scores_masks(ref["scores"][b][hot:], scores[b][hot:], mask[b][hot:])
     check_list(mask.astype(bool).any(axis=0), idx, count)
 
+
+
+# ------------------------------------------- dense fallback at a large union
+def _high_union_layer(cfg, layer, shift):
+    lw = workload.make_layer(cfg, layer)
+    lw.pbias = (oracle.predictor_bias(lw) + np.float32(shift)).astype(np.float32)
+    return lw
+
+
+@pytest.mark.parametrize("name", ["f16-relu", "q4-reglu", "f32-relu"])
+def test_batch_dense_fallback(name):
+    """Above the union threshold the batched FFN runs over every neuron in storage order
+    (neurons outside the union get h = 0): forced on (dense_frac tiny) and off (above 1),
+    both agree with the oracle, through the stack and through pi_sparse_ffn with an
+    explicit list (whose other neurons' mask bytes must read as 0)."""
+    cfg = SMALL[name].with_(n_layers=2)
+    nb = 8
+    say(f"[batch_dense] {name} batch {nb}")
+    host = [_high_union_layer(cfg, l, 1.0) for l in range(cfg.n_layers)]
+    X = workload.make_x(cfg, 17, seqs=nb)
+    ref0 = oracle.layer_forward(host[0], X)
+    say(f"  layer 0 union {ref0['count']} of {cfg.ffn}")
+    for tag, frac in (("dense", 1e-6), ("gathered", 2.0)):
+        for h in host:
+            h.dense_frac = frac
+        layers = [pi.DeviceLayer.upload(h, DEV) for h in host]
+        recs = traced_records(cfg.n_layers, nb, cfg.d, cfg.ffn)
+        out = torch.empty(nb, cfg.d, device=DEV)
+        pi.ffn_stack(layers, dev(X), out, trace=pi.make_trace(cfg.n_layers, recs), batch=nb)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        recs = to_host(recs)
+        st = replay_stack(host, recs, out, X, cfg.w_dtype, cfg.act)
+        say(f"  {tag}: {st}")
+        # explicit list: a third of the union, in its own order, with per-sequence masks
+        M = ref0["masks"].copy()
+        keep = ref0["idx"][::3]
+        Mk = np.zeros_like(M)
+        Mk[:, keep] = M[:, keep]
+        Y = run_sparse_ffn(layers[0], X, keep[::-1].copy(), Mk)
+        Yr = oracle.sparse_ffn(cfg.act, host[0].gate, host[0].up, host[0].downT, oracle.ffn_bias(host[0]), X, Mk)
+        for b in range(nb):
+            check_y(Y[b], Yr[b], TOL[cfg.w_dtype])

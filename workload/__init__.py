@@ -262,6 +262,7 @@ class LayerWeights:
     b_down: Optional[np.ndarray] = None
     pbias: Optional[np.ndarray] = None   # float32 [ffn], storage order
     hot: int = 0                         # hot-dense prefix length (storage slots [0, hot))
+    dense_frac: float = 0.0              # batched FFN over every neuron from this union fraction (0: default)
 
     @property
     def p_storage(self) -> np.ndarray:
