@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--hot", default="0",
                     help="hot-dense prefix per layer: 0 (off), auto (the byte model's prefix, "
                          "workload.hot_count) or a slot count")
+    ap.add_argument("--predictor-study", action="store_true",
+                    help="CPU only: recall / precision of rank-r SVD predictors against the true "
+                         "activations, for several singular spectra (activation_sparse_predict_amd.sizing)")
     ap.add_argument("--dense-sweep", action="store_true",
                     help="time the batched FFN (pi_sparse_ffn at --batch) over an explicit union of "
                          "growing size, gathered and dense, and print the table (one layer of --config)")
@@ -393,6 +396,16 @@ def dense_sweep(args):
 
 def main():
     args = parse()
+    if args.predictor_study:
+        from activation_sparse_predict_amd import sizing
+        t0 = time.time()
+        for d, f in ((1024, 4096), (4096, 11008)):
+            rows = sizing.study(d=d, f=f, ranks=(16, 64, 256, 1024), alphas=(0.0, 0.5, 1.0))
+            print(f"# predictor sizing, d={d}, f={f}, mean firing rate 0.1, 256 tokens (fp16 predictor and up)")
+            print(sizing.table(rows))
+            print()
+        log(f"[study] {time.time() - t0:.1f} s")
+        return
     if args.dense_sweep:
         dense_sweep(args)
         return
