@@ -289,7 +289,7 @@ def summarize_traffic(fetch_csv, write_csv, counts_json, kernel, commands, out, 
         per = {}
         for r in _csv_rows(path):
             kn = _col(r, "Kernel_Name")
-            key = "calib" if "elementwise" in kn else (kernel if kernel in _short(kn) else None)
+            key = "calib" if "neg_kernel" in kn else (kernel if kernel in _short(kn) else None)
             if key is not None:
                 per.setdefault(key, []).append(float(_col(r, "Counter_Value")))
         vals[name] = {k: (statistics.mean(v), len(v)) for k, v in per.items()}

@@ -91,10 +91,13 @@ def test_summarize_traffic(tmp_path):
     cj.write_text(json.dumps({"config": 1, "layers": 2, "batch": 1, "calib_mb": 1024, "counts": counts,
                               "nz_counts": nz}))
     hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
-    # the fetch counter reads half of the calibration map's bytes: scale 2
-    _write_csv(tmp_path / "f.csv", hdr, [["elementwise_kernel<neg>", "FETCH_SIZE", 524288]] * 3 +
+    # the fetch counter reads half of the calibration map's bytes: scale 2; other
+    # elementwise kernels of the program (fills) are not the calibration map
+    neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(at::TensorIteratorBase&)>"
+    fill = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>>"
+    _write_csv(tmp_path / "f.csv", hdr, [[neg, "FETCH_SIZE", 524288]] * 3 + [[fill, "FETCH_SIZE", 7.0]] +
                [["void pik::k_down<1, 4, false>(int)", "FETCH_SIZE", 1000.0]] * 6)
-    _write_csv(tmp_path / "w.csv", hdr, [["elementwise_kernel<neg>", "WRITE_SIZE", 1048576]] * 3 +
+    _write_csv(tmp_path / "w.csv", hdr, [[neg, "WRITE_SIZE", 1048576]] * 3 + [[fill, "WRITE_SIZE", 9.0]] +
                [["void pik::k_down<1, 4, false>(int)", "WRITE_SIZE", 10.0]] * 6)
     out = tmp_path / "t.md"
     bench.summarize_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(cj), "k_down", ["c"], str(out))
