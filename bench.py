@@ -97,6 +97,10 @@ def parse():
                     help="summarize FETCH_SIZE / WRITE_SIZE counter CSVs of one kernel (no GPU); "
                          "with --kernel, --command, --out")
     ap.add_argument("--kernel", default="", help="kernel name for --summarize-traffic")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV", default=None,
+                    help="per-launch means of rocprofv3 --pmc counter CSVs for --kernels")
+    ap.add_argument("--kernels", default="", help="comma-separated kernel names for --summarize-counters")
+    ap.add_argument("--trace", default="", help="kernel-trace CSV of the same program (--summarize-counters)")
     ap.add_argument("--source-rev", default="",
                     help="git revision whose HIP sources the counter run used (default: the working tree)")
     ap.add_argument("--title", default="", help="heading of a summary")
@@ -226,6 +230,52 @@ def _col(row, *names, default=None):
 def _short(name):
     """Kernel name without its argument list."""
     return name.split("(")[0].strip()
+
+
+def summarize_counters(paths, kernels, trace_csv, title, commands, out):
+    """Per-launch means of every counter in rocprofv3 --pmc CSVs for each kernel whose
+    name contains one of `kernels`; with a kernel-trace CSV of the same program, the
+    MFMA rate SQ_INSTS_VALU_MFMA_MOPS_F16 * 512 flop per mean launch duration and its
+    share of the dense fp16 peak (2.5 PFLOP/s)."""
+    import statistics
+    vals = {}
+    for path in paths:
+        for r in _csv_rows(path):
+            kn = _short(_col(r, "Kernel_Name"))
+            k = next((k for k in kernels if k in kn), None)
+            if k is not None:
+                vals.setdefault(k, {}).setdefault(_col(r, "Counter_Name"), []).append(float(_col(r, "Counter_Value")))
+    dur = {}
+    if trace_csv:
+        for r in _csv_rows(trace_csv):
+            kn = _short(_col(r, "Kernel_Name", "Name"))
+            k = next((k for k in kernels if k in kn), None)
+            if k is not None:
+                dur.setdefault(k, []).append(float(_col(r, "End_Timestamp")) - float(_col(r, "Start_Timestamp")))
+    L = [f"# Counters: {title}", "", "Commands (from the repository root on the GPU box):", "", "```"]
+    L += commands + ["```", "", "Summarized by `python bench.py --summarize-counters`: per-launch means.", ""]
+    names = sorted({c for k in vals for c in vals[k]})
+    L.append("| kernel | launches | " + " | ".join(names) + " | mean us | MFMA TFLOP/s (fp16) | of 2.5 PFLOP/s |")
+    L.append("|---|---|" + "---|" * len(names) + "---|---|---|")
+    for k in kernels:
+        if k not in vals:
+            continue
+        v = vals[k]
+        n = max(len(x) for x in v.values())
+        row = [f"`{k}`", str(n)] + [f"{statistics.mean(v[c]):.4g}" if c in v else "" for c in names]
+        us = statistics.mean(dur[k]) / 1e3 if dur.get(k) else None
+        mops = statistics.mean(v["SQ_INSTS_VALU_MFMA_MOPS_F16"]) if "SQ_INSTS_VALU_MFMA_MOPS_F16" in v else None
+        busy, gui = v.get("SQ_VALU_MFMA_BUSY_CYCLES"), v.get("GRBM_GUI_ACTIVE")
+        row.append(f"{us:.2f}" if us else "")
+        row.append(f"{mops * 512 / (us * 1e-6) / 1e12:.1f}" if (us and mops is not None) else "")
+        row.append(f"{mops * 512 / (us * 1e-6) / 2.5e15:.3f}" if (us and mops is not None) else "")
+        L.append("| " + " | ".join(row) + " |")
+    text = "\n".join(L) + "\n"
+    if out:
+        with open(out, "w") as fh:
+            fh.write(text)
+    else:
+        print(text, end="")
 
 
 def summarize_trace(path, title, commands, out):
@@ -411,6 +461,10 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.title or args.summarize_trace, args.command, args.out)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, [k for k in args.kernels.split(",") if k], args.trace,
+                           args.title, args.command, args.out)
         return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.kernel, args.command, args.out, args.source_rev)
