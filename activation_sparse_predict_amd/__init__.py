@@ -58,11 +58,14 @@ LAYER_KERNELS = {1: ("k_predict_t", "k_score", "k_down"),
                  2: ("k_bglue", "k_bpred1", "k_bsplit_t", "k_bscore", "k_compact", "k_bup", "k_bdown")}
 
 
+# the layout of the structures above; the library must report the same version
+ABI_VERSION = 6
+
 _lib = None
 
 
 def lib():
-    """Load libpi.so (raises if it is not built)."""
+    """Load libpi.so (raises if it is not built, or built from another ABI version)."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
@@ -83,6 +86,10 @@ def lib():
         L.pi_ffn_stack_static.argtypes = [P, I32, P, I32, P, P, P, P, P]
         L.pi_ffn_stack_static.restype = ctypes.c_int
         L.pi_last_hip_error.restype = ctypes.c_char_p
+        got = int(L.pi_abi_version())
+        if got != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {got}, this binding expects {ABI_VERSION} "
+                               "(rebuild with __graft_entry__.build())")
         _lib = L
     return _lib
 
@@ -255,7 +262,7 @@ def ffn_stack(layers, x, out, counts=None, trace=None, ws=None, batch: int = 1, 
     Stack(layers, batch, ws)(x, out, counts, trace, stream, nz_counts)
 
 
-STATIC_WORKSPACE_BYTES = 48 << 20   # PI_STATIC_WORKSPACE_BYTES
+STATIC_WORKSPACE_BYTES = 96 << 20   # PI_STATIC_WORKSPACE_BYTES
 
 
 def ffn_stack_static(layers, x, out, counts=None, trace=None, batch: int = 1, stream=None, nz_counts=None):

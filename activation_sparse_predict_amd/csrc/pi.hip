@@ -71,6 +71,7 @@ pi_status check_batched_ffn(const pi_layer* L, int32_t batch) {
 // -------------------------------------------------------------- workspace
 struct Dims {
   int d = 0, fmax = 0, rmax = 0;
+  int zmat = 0;      // z vectors of the Q4_0 K-split up GEMM: 0 without Q4_0 layers, else 1 (2 with ReGLU)
 };
 
 constexpr int kMaxParts = 8;       // neuron splits of the down projection (partial y vectors)
@@ -93,7 +94,7 @@ int bscore_blocks(int ffn) { return cdiv(ffn, pib::BM); }
 struct WsLayout {
   size_t t, v, ss, tcnt, xbuf, ybuf, mask, pmask, h, pid, ph, cnt, misc;
   // batched path (batch > 1)
-  size_t xh, xl, tpart, th, tl, mnm, ulist, h32, rsc;
+  size_t xh, xl, tpart, th, tl, mnm, ulist, h32, rsc, zpart;
   size_t total;
   size_t xs, ys;   // sizes of one x / one y buffer
 };
@@ -133,6 +134,8 @@ WsLayout layout(const Dims& D, int batch) {
     w.ulist = o; o += align_up(sizeof(int32_t) * (size_t)D.fmax);
     w.h32 = o;   o += align_up(sizeof(float) * (size_t)kBatchM * pib::h_stride(D.fmax));
     w.rsc = o;   o += align_up(sizeof(float) * 3 * kBatchM);   // row scales of x and t, row maxima of h
+    // the K splits of the Q4_0 up GEMM's z [KS][nmat][ffn padded to 32][32]
+    w.zpart = o; o += align_up(sizeof(float) * (size_t)pib::bu_ks(D.d) * D.zmat * cdiv(D.fmax, kBatchM) * kBatchM * kBatchM);
   }
   w.total = o;
   return w;
@@ -153,7 +156,7 @@ struct Ws {
   int32_t* cnt;
   int32_t* misc;
   _Float16 *xh, *xl, *th, *tl;
-  float *h32, *sx, *st;
+  float *h32, *sx, *st, *zpart;
   uint32_t* hmax;
   float* tpart;
   uint8_t* mnm;
@@ -190,6 +193,7 @@ Ws carve(void* base, const WsLayout& L) {
     w.sx = reinterpret_cast<float*>(b + L.rsc);
     w.st = w.sx + kBatchM;
     w.hmax = reinterpret_cast<uint32_t*>(w.st + kBatchM);
+    w.zpart = reinterpret_cast<float*>(b + L.zpart);
   }
   return w;
 }
@@ -202,6 +206,7 @@ bool dims_of(const pi_layer* layers, int32_t n, Dims* D) {
     D->d = layers[0].d;
     D->fmax = std::max(D->fmax, layers[i].ffn);
     D->rmax = std::max(D->rmax, layers[i].rank);
+    if (layers[i].w_dtype == PI_Q4_0) D->zmat = std::max(D->zmat, layers[i].act == PI_REGLU ? 2 : 1);
   }
   return true;
 }
@@ -537,7 +542,9 @@ void b_predict(const pi_layer* L, int batch, const Ws& W, float* scores, uint8_t
     hipLaunchKernelGGL(pib::k_bscore<DT_F32>, g2, dim3(256), 0, st, L->B, pb, L->ffn, L->rank, batch, W.th, W.tl,
                        W.st, W.mnm, W.mask, W.cnt, scores, mask_out, L->hot);
   mark(tr, 4, st);
-  hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, L->ffn, ulist, ucount, ucount2, ucount3);
+  // the union list from the score kernel's union bytes and per-tile counts (multi-block, no atomics)
+  hipLaunchKernelGGL(pib::k_bcompact, dim3(cdiv(bscore_blocks(L->ffn), 256)), dim3(256), 0, st, W.mask, W.cnt,
+                     L->ffn, ulist, ucount, ucount2, ucount3);
   mark(tr, 5, st);
 }
 
@@ -551,9 +558,21 @@ int dense_min(const pi_layer* L) {
 template <int WT, int ACT>
 void b_ffn_t(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, const int32_t* ucount, float* y,
              hipStream_t st, const pi_trace* tr) {
-  hipLaunchKernelGGL((pib::k_bup<WT, ACT>), dim3(cdiv(L->ffn, kBatchM)), dim3(pib::BUP_W * WAVE), 0, st, L->gate.w,
-                     L->gate.scale, L->up.w, L->up.scale, L->bias, L->ffn, L->d, W.xh, W.xl, ulist, ucount, W.mnm,
-                     W.sx, W.h32, W.hmax, dense_min(L));
+  if constexpr (WT != DT_Q4) {
+    hipLaunchKernelGGL((pib::k_bup<WT, ACT>), dim3(cdiv(L->ffn, kBatchM)), dim3(pib::BUP_W * WAVE), 0, st,
+                       L->gate.w, L->gate.scale, L->up.w, L->up.scale, L->bias, L->ffn, L->d, W.xh, W.xl, ulist,
+                       ucount, W.mnm, W.sx, W.h32, W.hmax, dense_min(L));
+  } else {
+    // Q4_0: K-split up GEMM on the batch operand staged in LDS, then the splits' sum and the
+    // activation (for fp16 weights the one-pass GEMM over the whole K measured faster)
+    const int ks = pib::bu_ks(L->d);
+    const int groups = cdiv(cdiv(L->ffn, kBatchM), pib::BU_TPB);
+    hipLaunchKernelGGL((pib::k_bup2<WT, act_nmat<ACT>()>), dim3(groups * ks), dim3(512), 0, st, L->gate.w,
+                       L->gate.scale, L->up.w, L->up.scale, L->ffn, L->d, ks, W.xh, W.xl, ulist, ucount, dense_min(L),
+                       W.zpart);
+    hipLaunchKernelGGL((pib::k_bup_epi<ACT>), dim3(cdiv(L->ffn, 256 / kBatchM)), dim3(256), 0, st, W.zpart, ks,
+                       L->ffn, ulist, ucount, dense_min(L), L->bias, W.mnm, W.sx, W.h32, W.hmax);
+  }
   mark(tr, 6, st);
   hipLaunchKernelGGL(pib::k_bdown<WT>, dim3(cdiv(L->d, kBatchM * pib::bd_tiles<WT>()) * pib::BD_SPLIT), dim3(256), 0,
                      st, L->downT.w,
@@ -750,7 +769,7 @@ pi_status pi_predict(const pi_layer* layer, const float* x, int32_t batch, float
   if ((s = check_batch(batch)) != PI_OK) return s;
   if (!x || !aligned(x, 16) || !idx || !count) return PI_EINVAL;
   if (batch > 1 && !mask) return PI_EINVAL;
-  Dims D{layer->d, layer->ffn, layer->rank};
+  Dims D{layer->d, layer->ffn, layer->rank, layer->act == PI_REGLU ? 2 : 1};
   const WsLayout WL = layout(D, batch);
   if (!ws || ws_bytes < WL.total || !aligned(ws, kAlign)) return PI_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -777,7 +796,7 @@ pi_status pi_sparse_ffn(const pi_layer* layer, const float* x, int32_t batch, co
   if ((s = check_batched_ffn(layer, batch)) != PI_OK) return s;
   if (!x || !aligned(x, 16) || !idx || !count || !y) return PI_EINVAL;
   if ((batch == 1) != (mask == nullptr)) return PI_EINVAL;
-  Dims D{layer->d, layer->ffn, layer->rank};
+  Dims D{layer->d, layer->ffn, layer->rank, layer->act == PI_REGLU ? 2 : 1};
   const WsLayout WL = layout(D, batch);
   if (!ws || ws_bytes < WL.total || !aligned(ws, kAlign)) return PI_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -68,17 +68,26 @@ __device__ __forceinline__ void split_f16(float v, _Float16* hi, _Float16* lo) {
 // 8 fp16 (16 bytes) of an fp16 matrix as an MFMA operand
 __device__ __forceinline__ h8v as_h8(uint4 c) { return __builtin_bit_cast(h8v, c); }
 
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
 // 8 weights of a Q4_0 chunk as (q - 8) in fp16, exact: nibbles of bytes
-// [b0, b0+8), low (hi_nib = false) or high nibble
+// [b0, b0+8) (b0 = 0 or 8), low (hi_nib = false) or high nibble.  Two bytes at a
+// time go to the low bits of two 16-bit lanes (a byte permute), the nibble is
+// masked into the mantissa of the fp16 1024 (0x6400 | q = 1024 + q), and 1032 is
+// subtracted from both lanes at once: four operations per pair of weights.
 __device__ __forceinline__ h8v q4_h8(uint4 c, int b0, bool hi_nib) {
-  const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
+  const uint32_t wd[2] = {b0 ? c.z : c.x, b0 ? c.w : c.y};
+  const h2v off = {(_Float16)1032.f, (_Float16)1032.f};
   h8v r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int byte_i = b0 + e;
-    const uint32_t byte = (wd[byte_i >> 2] >> (8 * (byte_i & 3))) & 0xFFu;
-    const int q = hi_nib ? (int)(byte >> 4) : (int)(byte & 15u);
-    r[e] = (_Float16)(q - 8);
+  for (int k = 0; k < 4; ++k) {
+    // bytes 2 (k % 2) and 2 (k % 2) + 1 of word k / 2 into the low bytes of two 16-bit lanes
+    uint32_t p = __builtin_amdgcn_perm(0u, wd[k >> 1], (k & 1) ? 0x0c030c02u : 0x0c010c00u);
+    if (hi_nib) p >>= 4;
+    const uint32_t v = (p & 0x000F000Fu) | 0x64006400u;
+    const h2v h = __builtin_bit_cast(h2v, v) - off;
+    r[2 * k] = h[0];
+    r[2 * k + 1] = h[1];
   }
   return r;
 }
@@ -530,6 +539,225 @@ k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, con
   }
   __syncthreads();
   if (tid < BM && rmax[tid] != 0u) atomicMax(&hmax[tid], rmax[tid]);
+}
+
+// ---------------------------------------------- up / gate, K-split (Q4_0)
+// z = X W^T over the union rows with the batch operand staged in LDS once per
+// block and used for BU_TPB row tiles.  Block id = g KS + s: row tiles
+// [g BU_TPB, (g + 1) BU_TPB) of the union list and K split s (the blocks of
+// one split land on one XCD when KS = 8, so its X slice stays in that L2).
+// The split's K range is walked in chunks of KC: the chunk of X (fp16 hi and
+// lo, operand order) goes to LDS by LDS-DMA while each wave loads its weights
+// for it; wave w takes row tile w % BU_TPB and half w / BU_TPB of the chunk.
+// The two halves' tiles are added in LDS, and the split's partial z goes to
+// z_part[s][m][position][b] (b fastest).  k_bup_epi adds the splits in order
+// and applies the activation.
+constexpr int BU_TPB = 4;                // row tiles (32 union rows each) per block
+constexpr int BU_KSMAX = 8;              // K splits (partial z vectors)
+__host__ __device__ constexpr int bu_kc(int nmat) { return 512 / nmat; }   // K per staged chunk
+// K splits for width d: the largest power of two <= BU_KSMAX that leaves whole chunks of
+// 64 values per split
+__host__ __device__ constexpr int bu_ks(int d) {
+  return (d % (8 * 64) == 0) ? 8 : (d % (4 * 64) == 0) ? 4 : (d % (2 * 64) == 0) ? 2 : 1;
+}
+
+template <int WT, int NMAT>
+__global__ void __launch_bounds__(512)
+k_bup2(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, const void* __restrict__ up_w,
+       const uint16_t* __restrict__ up_sc, int f, int d, int KS, const _Float16* __restrict__ xh,
+       const _Float16* __restrict__ xl, const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount,
+       int dense_min, float* __restrict__ z_part) {
+  static_assert(WT == DT_Q4, "fp16 and fp32 weights take k_bup (one pass over K measured faster)");
+  constexpr int KC = bu_kc(NMAT), KH = KC / 2;      // chunk, and the half a wave takes
+  static_assert(KH % 32 == 0, "whole Q4_0 blocks per half chunk");
+  __shared__ __attribute__((aligned(16))) _Float16 xs[2][bu_kc(1) / 16 * 512];   // hi, lo [K step][512]
+  float* red = reinterpret_cast<float*>(&xs[0][0]);                       // after the chunks: [8][NMAT][BM*BM]
+  static_assert(sizeof(float) * 8 * NMAT * BM * BM <= sizeof(xs), "red fits");
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const int col = lane % 32, half = lane / 32;
+  const int g = blockIdx.x / KS, s = blockIdx.x % KS;
+  bool dense;
+  const int n = ffn_rows(ucount, f, dense_min, &dense);
+  const int t0 = g * BU_TPB * BM;
+  if (t0 >= n) return;                                        // block-uniform
+  const int tl = w % BU_TPB, kp = w / BU_TPB;                 // this wave's row tile and chunk half
+  const int pos = min(t0 + tl * BM + col, n - 1);
+  const size_t row = (size_t)(dense ? pos : ulist[pos]);
+  const int ksz = d / KS, kbeg = s * ksz;
+  f16v acc[NMAT];
+#pragma unroll
+  for (int mt = 0; mt < NMAT; ++mt) acc[mt] = f16v{};
+  for (int kc = kbeg; kc < kbeg + ksz; kc += KC) {
+    const int kcn = min(KC, kbeg + ksz - kc);                 // a multiple of 64
+    // the chunk of X: K steps kc/16 .. (kc + kcn)/16 of hi and lo, 1 KB each
+    __syncthreads();                                          // the previous chunk is consumed
+    for (int p = w; p < 2 * (kcn / 16); p += 8) {
+      const int hl = p & 1, st = p >> 1;
+      const _Float16* src = (hl ? xl : xh) + (size_t)(kc / 16 + st) * 512;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 8 * lane),
+                                       (__attribute__((address_space(3))) void*)(&xs[hl][st * 512]), 16, 0, 0);
+    }
+    const int kw = kc + kp * (kcn / 2), kwn = kcn / 2;        // this wave's half
+    constexpr int QB = KH / 32;
+    uint4 cq[NMAT][QB];
+    float sc[NMAT][QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int kb = kw + 32 * min(qb, kwn / 32 - 1);
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt) {
+        const void* wp = (NMAT == 2 && mt == 0) ? gate_w : up_w;
+        const uint16_t* sp = (NMAT == 2 && mt == 0) ? gate_sc : up_sc;
+        cq[mt][qb] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(wp) + row * (d / 2) + kb / 2);
+        sc[mt][qb] = (float)__builtin_bit_cast(_Float16, sp[row * (d / 32) + kb / 32]);
+      }
+    }
+    PI_ISSUE_FENCE();
+    wait_vm_lds<0>();
+    __syncthreads();                                        // every wave's part of the chunk is in LDS
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (32 * qb >= kwn) continue;
+      const int st0 = (kw - kc) / 16 + 2 * qb;              // K step within the chunk
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt) {
+        f16v p = {};
+#pragma unroll
+        for (int stp = 0; stp < 2; ++stp) {
+          const h8v bw = q4_h8(cq[mt][qb], 8 * half, stp == 1);
+          const h8v ah = *reinterpret_cast<const h8v*>(&xs[0][(st0 + stp) * 512 + 8 * lane]);
+          const h8v al = *reinterpret_cast<const h8v*>(&xs[1][(st0 + stp) * 512 + 8 * lane]);
+          p = mfma(ah, bw, p);
+          p = mfma(al, bw, p);
+        }
+#pragma unroll
+        for (int x = 0; x < 16; ++x) acc[mt][x] = fmaf(sc[mt][qb], p[x], acc[mt][x]);
+      }
+    }
+  }
+  __syncthreads();                                            // the last chunk is consumed: reuse its LDS
+#pragma unroll
+  for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[((size_t)w * NMAT + mt) * BM * BM + (8 * g4 + 4 * half + v) * BM + col] = acc[mt][4 * g4 + v];
+  __syncthreads();
+  // the two halves of each tile, in order, to z_part[s][mt][position][b]
+  const size_t fpad = (size_t)(f + BM - 1) / BM * BM;
+  for (int e = tid; e < BU_TPB * NMAT * BM * BM; e += blockDim.x) {
+    const int b = e % BM, c = (e / BM) % BM, mt = (e / (BM * BM)) % NMAT, t = e / (NMAT * BM * BM);
+    const int p = t0 + t * BM + c;
+    if (p >= n) continue;
+    const float v = red[((size_t)t * NMAT + mt) * BM * BM + b * BM + c] +
+                    red[((size_t)(t + BU_TPB) * NMAT + mt) * BM * BM + b * BM + c];
+    z_part[(((size_t)s * NMAT + mt) * fpad + p) * BM + b] = v;
+  }
+}
+
+// h from the K splits of z: position j of the union list (8 per block), row b
+// (b fastest): z = (sum of the KS partials in split order) / sx[b]; h = m ? act(z
+// + bias) : 0, written in fp32 to h32 in operand order; hmax[b] collects the
+// largest |h[b]|.
+template <int ACT>
+__global__ void __launch_bounds__(256)
+k_bup_epi(const float* __restrict__ z_part, int KS, int f, const int32_t* __restrict__ ulist,
+          const int32_t* __restrict__ ucount, int dense_min, const float* __restrict__ bias,
+          const uint8_t* __restrict__ m_nm, const float* __restrict__ sx, float* __restrict__ h32,
+          uint32_t* __restrict__ hmax) {
+  constexpr int NMAT = act_nmat<ACT>();
+  __shared__ uint32_t rmax[BM];
+  const int tid = threadIdx.x, b = tid % BM;
+  const int j = blockIdx.x * (256 / BM) + tid / BM;
+  bool dense;
+  const int n = ffn_rows(ucount, f, dense_min, &dense);
+  if ((int)blockIdx.x * (256 / BM) >= n) return;              // block-uniform
+  if (tid < BM) rmax[tid] = 0u;
+  __syncthreads();
+  if (j < n) {
+    const size_t fpad = (size_t)(f + BM - 1) / BM * BM;
+    const int rw = dense ? j : ulist[j];
+    const float ix = 1.f / sx[b];
+    float z[NMAT];
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt) {
+      float a = z_part[((size_t)mt * fpad + j) * BM + b];
+      for (int s2 = 1; s2 < KS; ++s2) a += z_part[(((size_t)s2 * NMAT + mt) * fpad + j) * BM + b];
+      z[mt] = a * ix;
+    }
+    float h = act_h<ACT>(z[0], bias[rw], z[NMAT - 1]);
+    if (m_nm[(size_t)rw * BM + b] == 0) h = 0.f;
+    h32[aop(b, j)] = h;
+    atomicMax(&rmax[b], __float_as_uint(fabsf(h)));          // LDS atomic
+  }
+  __syncthreads();
+  if (tid < BM && rmax[tid] != 0u) atomicMax(&hmax[tid], rmax[tid]);
+}
+
+// ------------------------------------------------------ union compaction
+// The ascending union list from the score kernel's per-tile union bytes u and
+// counts (one per 32-neuron tile), in one pass without atomics: block b takes
+// tiles [256 b, 256 b + 256); it adds the counts of all earlier tiles (a few KB
+// read from L2) and scans its own, and each thread writes the union neurons of
+// one tile at its offset.  Every load is issued before the first use, so the
+// kernel is one round trip.  *count (and count2, count3 if given) = the total,
+// from block 0 (which adds every tile's count).
+__global__ void __launch_bounds__(256)
+k_bcompact(const uint8_t* __restrict__ u, const int32_t* __restrict__ tile_cnt, int f, int32_t* __restrict__ list,
+           int32_t* __restrict__ count, int32_t* __restrict__ count2, int32_t* __restrict__ count3) {
+  constexpr int BC_PRE = 8;                  // earlier tile counts per thread (f <= 65536: 2048 tiles)
+  __shared__ int red[2][4];
+  __shared__ int wtot[4];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const int ntiles = (f + BM - 1) / BM;
+  const int t0 = blockIdx.x * 256, t = t0 + tid;
+  // every load first: the earlier tiles' counts (block 0: all counts, for the
+  // total), this tile's count and its 32 union bytes
+  const int span = blockIdx.x == 0 ? ntiles : t0;
+  int pre[BC_PRE];
+#pragma unroll
+  for (int q = 0; q < BC_PRE; ++q) {
+    const int k = tid + 256 * q;
+    pre[q] = k < span ? tile_cnt[k] : 0;
+  }
+  const int c = t < ntiles ? tile_cnt[t] : 0;
+  uint4 ub[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  if (t < ntiles && (t + 1) * BM <= f) {
+    ub[0] = reinterpret_cast<const uint4*>(u + (size_t)t * BM)[0];
+    ub[1] = reinterpret_cast<const uint4*>(u + (size_t)t * BM)[1];
+  }
+  int sp = 0;
+#pragma unroll
+  for (int q = 0; q < BC_PRE; ++q) sp += pre[q];
+  sp = wave_sum(sp);
+  const int inc = wave_scan(c);
+  if (lane == 0) red[0][w] = sp;
+  if (lane == WAVE - 1) wtot[w] = inc;
+  __syncthreads();
+  const int spb = red[0][0] + red[0][1] + red[0][2] + red[0][3];   // block 0: the total
+  const int before = blockIdx.x == 0 ? 0 : spb;
+  int off = before + inc - c;
+  for (int v = 0; v < w; ++v) off += wtot[v];
+  if (t < ntiles && c > 0) {
+    const int i0 = t * BM;
+    if (i0 + BM <= f) {
+      const uint32_t wd[8] = {ub[0].x, ub[0].y, ub[0].z, ub[0].w, ub[1].x, ub[1].y, ub[1].z, ub[1].w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((wd[q] >> (8 * e)) & 0xFFu) list[off++] = i0 + 4 * q + e;
+      }
+    } else {
+      for (int k = 0; k < f - i0; ++k)                        // the ragged last tile, bytewise
+        if (u[i0 + k]) list[off++] = i0 + k;
+    }
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    *count = spb;
+    if (count2) *count2 = spb;
+    if (count3) *count3 = spb;
+  }
 }
 
 // ------------------------------------------------------------------ down

@@ -133,7 +133,8 @@ typedef struct {
    * i < n_events.  Kernels of a layer, in order -- batch 1: predictor GEMV 1
    * with the glue, scores with the fused up/gate gather, down projection;
    * batch > 1: glue, predictor GEMM 1, its split sum, scores and union, union
-   * compaction, up/gate GEMM, down GEMM.  Record-only kernels of the trace
+   * compaction, up/gate GEMM (for Q4_0 weights its K-split GEMM and the
+   * epilogue that adds the splits, as one interval), down GEMM.  Record-only kernels of the trace
    * (list compaction, the sum of y's partial vectors) are not counted. */
   void** events;
   int32_t n_events;
@@ -206,12 +207,13 @@ pi_status pi_ffn_stack(const pi_layer* layers, int32_t n_layers, const float* x,
  * first call with that device current).
  * Returns PI_EWORKSPACE, before any HIP call, when
  * pi_workspace_bytes(layers, n_layers, batch) exceeds PI_STATIC_WORKSPACE_BYTES
- * (48 MiB covers batch 1 at every accepted shape and batch 2..32 up to
- * d = 12288 with ffn = 49152 and rank = 1024).  Every call on one GPU shares that GPU's array: calls that
+ * (96 MiB covers batch 1 at every accepted shape, and batch 2..32 up to
+ * d = 12288 with ffn = 49152 and rank = 1024 for every layer but ReGLU with
+ * Q4_0 weights, which needs 135 MiB there).  Every call on one GPU shares that GPU's array: calls that
  * overlap on one GPU (other streams, other threads) race and give undefined
  * results; calls ordered on one stream are independent.
  */
-#define PI_STATIC_WORKSPACE_BYTES (48u << 20)
+#define PI_STATIC_WORKSPACE_BYTES (96u << 20)
 pi_status pi_ffn_stack_static(const pi_layer* layers, int32_t n_layers, const float* x, int32_t batch,
                               float* out, int32_t* counts, int32_t* nz_counts, const pi_trace* trace,
                               void* stream);

@@ -44,6 +44,9 @@ def test_library_exports_every_declared_symbol(pi):
 
 def test_abi_version_and_status_strings(pi):
     assert pi.abi_version() == 6
+    # the binding's version is the header's
+    hdr = open(os.path.join(ROOT, "include", "pi.h")).read()
+    assert re.search(r"#define PI_ABI_VERSION (\d+)", hdr).group(1) == str(pi.ABI_VERSION) == "6"
     assert pi.status_str(0) == "ok"
     assert "workspace" in pi.status_str(3)
 
@@ -190,13 +193,32 @@ def test_static_stack_checks_come_before_any_hip_call(pi):
                                    None) == 1
     assert lib.pi_ffn_stack_static(ctypes.cast(one, ctypes.c_void_p), 1, FAKE, 33, FAKE, None, None, None,
                                    None) == 1
-    big = make_layer(pi, d=16384, rank=4096, ffn=65536)   # the largest batched shape
+    q4 = pi.PiMat(FAKE, FAKE)
+    big = make_layer(pi, d=16384, rank=4096, ffn=65536, act=pi.PI_REGLU, w_dtype=pi.PI_Q4_0, gate=q4, up=q4,
+                     downT=q4)                             # the largest batched shape
     assert ws_bytes(pi, big, batch=32) > pi.STATIC_WORKSPACE_BYTES
     arr = (pi.PiLayer * 1)(big)
     assert lib.pi_ffn_stack_static(ctypes.cast(arr, ctypes.c_void_p), 1, FAKE, 32, FAKE, None, None, None,
                                    None) == 3
     # batch 1 at the largest accepted ffn fits
     assert 0 < ws_bytes(pi, make_layer(pi, d=16384, rank=4096, ffn=1 << 21)) <= pi.STATIC_WORKSPACE_BYTES
+
+
+@pytest.mark.parametrize("act,wt,fits", [("RELU", "Q4_0", True), ("RELU2", "Q4_0", True), ("RELU", "F32", True),
+                                         ("REGLU", "F16", True), ("REGLU", "F32", True), ("REGLU", "Q4_0", False)])
+def test_static_workspace_coverage_stated_in_the_header(pi, act, wt, fits):
+    """At d = 12288, ffn = 49152, rank = 1024 and batch 2..32 the fixed array holds every
+    layer but ReGLU with Q4_0 weights (the K-split up GEMM's partial z for two matrices)."""
+    sc = FAKE if wt == "Q4_0" else None
+    mats = {k: pi.PiMat(FAKE, sc) for k in ("up", "downT")}
+    if act == "REGLU":
+        mats["gate"] = pi.PiMat(FAKE, sc)
+    L = make_layer(pi, d=12288, ffn=49152, rank=1024, act=getattr(pi, "PI_" + act), w_dtype=getattr(pi, "PI_" + wt),
+                   p_dtype=pi.PI_F32 if wt == "F32" else pi.PI_F16, **mats)
+    for b in (1, 2, 8, 32):
+        n = ws_bytes(pi, L, batch=b)
+        assert n > 0
+        assert (n <= pi.STATIC_WORKSPACE_BYTES) == (fits or b == 1), (b, n)
 
 
 def test_static_workspace_size_matches_the_header(pi):
