@@ -108,7 +108,7 @@ WsLayout layout(const Dims& D, int batch) {
   size_t o = 0;
   const size_t fpad = (size_t)cdiv(D.fmax, 16) * 16;
   w.xs = align_up(sizeof(float) * (size_t)D.d * batch);
-  w.ys = align_up(sizeof(float) * (size_t)D.d * (batch > 1 ? pib::BD_SPLIT * kBatchM : kMaxParts));
+  w.ys = align_up(sizeof(float) * (size_t)D.d * (batch > 1 ? pib::bd_splits(D.d) * kBatchM : kMaxParts));
   w.t = o;    o += align_up(sizeof(float) * (size_t)D.rmax * std::max(batch, kK1MaxSplit));
   w.v = o;    o += align_up(sizeof(float) * (size_t)D.d);              // x' + y of a layer (batch 1)
   w.ss = o;   o += align_up(sizeof(float) * kK1MaxSplit);              // its slices' sums of squares
@@ -496,7 +496,7 @@ int bksplit(int r) { return std::max(1, std::min(kMaxKSplit, cdiv(256, cdiv(r, k
 void b_glue(const float* x_prev, const float* y_prev, int batch, int d, float* x_out, float* x_trace, const Ws& W,
             hipStream_t st) {
   hipLaunchKernelGGL(pib::k_bglue, dim3(kBatchM), dim3(pib::BG_T), 0, st, x_prev, y_prev,
-                     y_prev ? pib::BD_SPLIT : 0, batch, d, x_out, x_trace, W.xh, W.xl, W.sx, W.hmax);
+                     y_prev ? pib::bd_splits(d) : 0, batch, d, x_out, x_trace, W.xh, W.xl, W.sx, W.hmax);
 }
 
 // per-sequence scores and masks, the union and its ascending list
@@ -574,14 +574,14 @@ void b_ffn_t(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, co
                        L->ffn, ulist, ucount, dense_min(L), L->bias, W.mnm, W.sx, W.h32, W.hmax);
   }
   mark(tr, 6, st);
-  hipLaunchKernelGGL(pib::k_bdown<WT>, dim3(cdiv(L->d, kBatchM * pib::bd_tiles<WT>()) * pib::BD_SPLIT), dim3(256), 0,
-                     st, L->downT.w,
-                     L->downT.scale, L->ffn, L->d, ulist, ucount, W.h32, W.hmax, L->b_down, batch, y, dense_min(L));
+  hipLaunchKernelGGL(pib::k_bdown<WT>, dim3(cdiv(L->d, pib::BD_COLS) * pib::bd_splits(L->d)), dim3(512), 0, st,
+                     L->downT.w, L->downT.scale, L->ffn, L->d, ulist, ucount, W.h32, W.hmax, L->b_down, batch, y,
+                     dense_min(L), pib::bd_splits(L->d));
   mark(tr, 7, st);
 }
 
-// the FFN over the union list for every sequence: BD_SPLIT partial vectors
-// y_part [BD_SPLIT][32][d] (rows b < batch written)
+// the FFN over the union list for every sequence: bd_splits(d) partial vectors
+// y_part [bd_splits(d)][32][d] (rows b < batch written)
 template <int WT>
 void b_ffn_w(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, const int32_t* ucount, float* y,
              hipStream_t st, const pi_trace* tr) {
@@ -658,12 +658,13 @@ pi_status run_stack(const pi_layer* layers, int32_t n_layers, const float* x, in
                            tr->count ? tr->count : W.misc + 1, nullptr, nullptr);
       b_ffn(L, batch, W, W.ulist, W.misc, W.y[cur], st, tr);
       if (tr && tr->y)   // the layer's y for the record: its partial vectors added in order
-        hipLaunchKernelGGL(pib::k_bsum_y, dim3(cdiv(batch * L->d, 256)), dim3(256), 0, st, W.y[cur], batch, L->d,
+        hipLaunchKernelGGL(pib::k_bsum_y, dim3(cdiv(batch * L->d, 256)), dim3(256), 0, st, W.y[cur],
+                           pib::bd_splits(L->d), batch, L->d,
                            tr->y);
     }
     const int last = (n_layers - 1) & 1;
     hipLaunchKernelGGL(pib::k_bglue_out, dim3(batch), dim3(256), sizeof(float) * D.d, st, W.x[last], W.y[last],
-                       pib::BD_SPLIT, D.d, out);
+                       pib::bd_splits(D.d), D.d, out);
     return launch_status();
   }
   for (int l = 0; l < n_layers; ++l) {
@@ -769,7 +770,8 @@ pi_status pi_predict(const pi_layer* layer, const float* x, int32_t batch, float
   if ((s = check_batch(batch)) != PI_OK) return s;
   if (!x || !aligned(x, 16) || !idx || !count) return PI_EINVAL;
   if (batch > 1 && !mask) return PI_EINVAL;
-  Dims D{layer->d, layer->ffn, layer->rank, layer->act == PI_REGLU ? 2 : 1};
+  Dims D;
+  dims_of(layer, 1, &D);                 // the layer is valid (checked above)
   const WsLayout WL = layout(D, batch);
   if (!ws || ws_bytes < WL.total || !aligned(ws, kAlign)) return PI_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -796,7 +798,8 @@ pi_status pi_sparse_ffn(const pi_layer* layer, const float* x, int32_t batch, co
   if ((s = check_batched_ffn(layer, batch)) != PI_OK) return s;
   if (!x || !aligned(x, 16) || !idx || !count || !y) return PI_EINVAL;
   if ((batch == 1) != (mask == nullptr)) return PI_EINVAL;
-  Dims D{layer->d, layer->ffn, layer->rank, layer->act == PI_REGLU ? 2 : 1};
+  Dims D;
+  dims_of(layer, 1, &D);                 // the layer is valid (checked above)
   const WsLayout WL = layout(D, batch);
   if (!ws || ws_bytes < WL.total || !aligned(ws, kAlign)) return PI_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -810,7 +813,8 @@ pi_status pi_sparse_ffn(const pi_layer* layer, const float* x, int32_t batch, co
                        batch, W.mask, W.mnm);
     hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, W.mask, layer->ffn, W.ulist, W.misc, nullptr, nullptr);
     b_ffn(layer, batch, W, W.ulist, W.misc, W.y[0], st);
-    hipLaunchKernelGGL(pib::k_bsum_y, dim3(cdiv(batch * layer->d, 256)), dim3(256), 0, st, W.y[0], batch, layer->d,
+    hipLaunchKernelGGL(pib::k_bsum_y, dim3(cdiv(batch * layer->d, 256)), dim3(256), 0, st, W.y[0],
+                       pib::bd_splits(layer->d), batch, layer->d,
                        y);
     return launch_status();
   }

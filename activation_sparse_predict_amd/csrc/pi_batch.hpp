@@ -131,18 +131,27 @@ k_bglue(const float* __restrict__ x_prev, const float* __restrict__ y_part, int 
 #pragma unroll
     for (int j = 0; j < BG_V; ++j)
       y[j] = reinterpret_cast<const float4*>(y_part + (size_t)b * d)[min(tid + BG_T * j, nv - 1)];
-    for (int p = 1; p < np; ++p) {
-      float4 u[BG_V];
+    // the other partials, four at a time: all their loads before the first add,
+    // added in partial order (partials past np are read clamped and dropped)
+    constexpr int GP = 4;
+    for (int p0 = 1; p0 < np; p0 += GP) {
+      float4 u[GP][BG_V];
 #pragma unroll
-      for (int j = 0; j < BG_V; ++j)
-        u[j] = reinterpret_cast<const float4*>(y_part + p * ystride + (size_t)b * d)[min(tid + BG_T * j, nv - 1)];
+      for (int g = 0; g < GP; ++g)
 #pragma unroll
-      for (int j = 0; j < BG_V; ++j) {
-        y[j].x += u[j].x;
-        y[j].y += u[j].y;
-        y[j].z += u[j].z;
-        y[j].w += u[j].w;
-      }
+        for (int j = 0; j < BG_V; ++j)
+          u[g][j] = reinterpret_cast<const float4*>(y_part + min(p0 + g, np - 1) * ystride +
+                                                    (size_t)b * d)[min(tid + BG_T * j, nv - 1)];
+#pragma unroll
+      for (int g = 0; g < GP; ++g)
+#pragma unroll
+        for (int j = 0; j < BG_V; ++j) {
+          const bool on = p0 + g < np;
+          y[j].x += on ? u[g][j].x : 0.f;
+          y[j].y += on ? u[g][j].y : 0.f;
+          y[j].z += on ? u[g][j].z : 0.f;
+          y[j].w += on ? u[g][j].w : 0.f;
+        }
     }
 #pragma unroll
     for (int j = 0; j < BG_V; ++j) {
@@ -431,7 +440,7 @@ __device__ __forceinline__ int ffn_rows(const int32_t* __restrict__ ucount, int 
 // the down projection reads it as its A operand; hmax[b] collects the largest
 // |h[b]| (as the bits of a non-negative float, by atomic maximum).
 constexpr int BUP_W = 8;
-constexpr int BD_CH = 256;               // union positions per chunk of the down projection
+constexpr int BD_CH = 128;               // union positions per chunk of the down projection
 
 // K extent (halves) of the h operand: whole chunks, so that a chunk's
 // reads stay inside the buffer
@@ -599,26 +608,38 @@ k_bup2(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, co
     }
     const int kw = kc + kp * (kcn / 2), kwn = kcn / 2;        // this wave's half
     constexpr int QB = KH / 32;
+    // the row's nibbles for the half chunk (one 16-byte block per load) and its block
+    // scales two at a time: aligned words from the even block a0 = kw / 32 rounded
+    // down (d / 32 is even, so a word lies wholly inside the row or wholly past it,
+    // then clamped to the row's last word and not used); block kw / 32 + qb is
+    // half (o + qb) & 1 of word (o + qb) / 2, o = kw / 32 - a0
+    const int a0 = (kw / 32) & ~1, o = (kw / 32) & 1;
     uint4 cq[NMAT][QB];
-    float sc[NMAT][QB];
+    uint32_t scw[NMAT][QB / 2 + 1];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int kb = kw + 32 * min(qb, kwn / 32 - 1);
+    for (int mt = 0; mt < NMAT; ++mt) {
+      const void* wp = (NMAT == 2 && mt == 0) ? gate_w : up_w;
+      const uint16_t* sp = (NMAT == 2 && mt == 0) ? gate_sc : up_sc;
 #pragma unroll
-      for (int mt = 0; mt < NMAT; ++mt) {
-        const void* wp = (NMAT == 2 && mt == 0) ? gate_w : up_w;
-        const uint16_t* sp = (NMAT == 2 && mt == 0) ? gate_sc : up_sc;
+      for (int qb = 0; qb < QB; ++qb) {
+        const int kb = kw + 32 * min(qb, kwn / 32 - 1);
         cq[mt][qb] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(wp) + row * (d / 2) + kb / 2);
-        sc[mt][qb] = (float)__builtin_bit_cast(_Float16, sp[row * (d / 32) + kb / 32]);
       }
+#pragma unroll
+      for (int p = 0; p <= QB / 2; ++p)
+        scw[mt][p] = *reinterpret_cast<const uint32_t*>(sp + row * (d / 32) + min(a0 + 2 * p, d / 32 - 2));
     }
     PI_ISSUE_FENCE();
     wait_vm_lds<0>();
     __syncthreads();                                        // every wave's part of the chunk is in LDS
+    // every block of the half chunk is multiplied (blocks past a short last
+    // chunk read clamped weights and LDS steps inside xs, and are dropped by a
+    // select): a branch around the use would sink the loads into it, one HBM
+    // round trip per block
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      if (32 * qb >= kwn) continue;
-      const int st0 = (kw - kc) / 16 + 2 * qb;              // K step within the chunk
+      const bool valid = 32 * qb < kwn;
+      const int st0 = (kw - kc) / 16 + 2 * min(qb, kwn / 32 - 1);   // K step within the chunk
 #pragma unroll
       for (int mt = 0; mt < NMAT; ++mt) {
         f16v p = {};
@@ -630,8 +651,10 @@ k_bup2(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, co
           p = mfma(ah, bw, p);
           p = mfma(al, bw, p);
         }
+        const uint32_t wd = o ? scw[mt][(qb + 1) / 2] : scw[mt][qb / 2];
+        const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> (16 * ((o + qb) & 1))));
 #pragma unroll
-        for (int x = 0; x < 16; ++x) acc[mt][x] = fmaf(sc[mt][qb], p[x], acc[mt][x]);
+        for (int x = 0; x < 16; ++x) acc[mt][x] = valid ? fmaf(sc, p[x], acc[mt][x]) : acc[mt][x];
       }
     }
   }
@@ -761,222 +784,242 @@ k_bcompact(const uint8_t* __restrict__ u, const int32_t* __restrict__ tile_cnt, 
 }
 
 // ------------------------------------------------------------------ down
-// y[b][c] = sum over union positions j of h[b][j] downT[u_j][c].  Block = NT
-// column tiles of 32 columns (bd_tiles) and one of BD_SPLIT splits of the union list,
-// whose partial sums go to y_part[split][b][c] (b < batch; the consumer adds
-// the splits in order, b_down rides on split 0).  A split's share of the
-// list is taken in chunks of BD_CH positions.  The weights of a chunk are
-// staged through LDS transposed to [column][position] -- each thread writes
-// four consecutive positions of a column at once -- as fp16 (fp32 weights
-// and Q4_0 weights times their block scale as hi + lo pairs); h is read
-// straight from its operand-order layout and, times its row scale (from
-// hmax), split into the hi/lo A operands; the tile's row b is multiplied by
-// 1 / s_b at the end.  Wave w runs K steps
-// 4w .. 4w + 3 of a chunk.  The next chunk's global loads are in flight while
-// a chunk is processed; wave partials are summed in a fixed order.
+// y[b][c] = sum over union positions j of h[b][j] downT[u_j][c].  Block =
+// one group of BD_COLS = 256 columns (wave w owns the 32-column tile w) and
+// one of bd_splits(d) splits of the union list; a split's share is taken in
+// chunks of BD_CH positions, and its partial sums go to y_part[split][b][c]
+// (b < batch; the consumer adds the splits in order, b_down rides on split 0).
+// Per chunk the block stages, in LDS,
+//  - the A operands once for all eight tiles: h (read in its operand-order
+//    layout) times the row scale from hmax, split into fp16 hi/lo;
+//  - each tile's weights transposed to [column][position] as fp16 (fp32 and
+//    Q4_0 weights -- times their block scale -- as hi + lo pairs).
+// Every thread converts four positions of eight columns in each of its two
+// items (adjacent tiles) and writes each column's values in pairs.  The next chunk's
+// weights and h, and the row ids of the chunk after it, are in flight while a
+// chunk is converted and multiplied.  Blocks that read a whole 128-byte line
+// (or several) of every row they gather, and h once per 256 columns instead
+// of once per 32 or 64.
+constexpr int BD_COLS = 256;             // columns per block (eight 32-column tiles, one per wave)
 constexpr int BD_PAD = BD_CH + 8;        // padded position stride (halves) of a transposed column
-constexpr int BD_SPLIT = 8;              // splits of the union list (partial y vectors)
-constexpr int BD_MAXF = 65536;           // largest ffn of the batched path: a split's list fits in LDS
-constexpr int BD_ROWS = BD_MAXF / BD_SPLIT;
-// 32-column tiles per block: two for fp16 (a whole 128-byte line of every row
-// per block, and half the blocks re-reading the split's h), one otherwise
-template <int WT> constexpr int bd_tiles() { return WT == DT_F16 ? 2 : 1; }
+constexpr int BD_MAXSPLIT = 16;          // most splits of the union list (partial y vectors)
+constexpr int BD_MAXF = 65536;           // largest ffn of the batched path
+// splits of the union list for width d: about one block per compute unit
+__host__ __device__ constexpr int bd_splits(int d) {
+  return (256 / ((d + BD_COLS - 1) / BD_COLS)) < 1 ? 1
+         : (256 / ((d + BD_COLS - 1) / BD_COLS)) > BD_MAXSPLIT ? BD_MAXSPLIT
+                                                              : 256 / ((d + BD_COLS - 1) / BD_COLS);
+}
 
 template <int WT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int f, int d,
         const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount, const float* __restrict__ h32,
         const uint32_t* __restrict__ hmax, const float* __restrict__ b_down, int batch,
-        float* __restrict__ y_part, int dense_min) {
-  constexpr int NW = (WT == DT_F16) ? 1 : 2;      // weight tiles: hi (and lo for fp32 and Q4_0)
-  constexpr int NT = bd_tiles<WT>();               // 32-column tiles of this block
-  // The weight tiles [NW][column][position] and, after the last chunk, the
-  // waves' partial sums [4][NT][BM * BM] share one buffer, so two blocks fit
-  // on a CU.
-  constexpr size_t WT_BYTES = sizeof(_Float16) * NW * NT * BM * BD_PAD, RED_BYTES = sizeof(float) * 4 * NT * BM * BM;
-  __shared__ __attribute__((aligned(16))) unsigned char bd_smem[WT_BYTES > RED_BYTES ? WT_BYTES : RED_BYTES];
-  auto& wt = *reinterpret_cast<_Float16(*)[NW][NT * BM][BD_PAD]>(bd_smem);
-  auto& red = *reinterpret_cast<float(*)[4][NT][BM * BM]>(bd_smem);
-  __shared__ int rows_l[BD_ROWS];                 // this split's share of the union list
+        float* __restrict__ y_part, int dense_min, int nsplit) {
+  constexpr int NW = (WT == DT_F16) ? 1 : 2;       // weight operands: hi (and lo for fp32 and Q4_0)
+  constexpr int NWV = 2 * (WT == DT_F32 ? 2 : 1);  // 16-byte pieces per row segment of 8 columns, times items
+  __shared__ __attribute__((aligned(16))) _Float16 wt[NW][BD_COLS][BD_PAD];
+  __shared__ __attribute__((aligned(16))) _Float16 as[2][BD_CH / 16][512];
+  __shared__ float rsc[BM];                        // 1 / row scale of h, per batch row
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  const int ntile = (d + NT * BM - 1) / (NT * BM);
-  // XCD-aware order for fp16/fp32: the hardware deals block ids to the 8 XCDs
-  // round-robin, so logical block L = (id % 8) * (nblk / 8) + id / 8 puts
-  // adjacent column tiles on one XCD and its L2.  For Q4_0, whose 8 tiles per
-  // 128-byte line would all land on one XCD, it measured 16% slower and is
-  // not used.
-  const int nblk = gridDim.x;
-  const bool xcd = WT != DT_Q4 && nblk % 8 == 0;
-  const int lb = xcd ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)blockIdx.x / 8 : (int)blockIdx.x;
-  const int c0 = (lb % ntile) * NT * BM, split = lb / ntile;
+  const int ngroup = (d + BD_COLS - 1) / BD_COLS;
+  const int c0 = (int)(blockIdx.x % ngroup) * BD_COLS, split = (int)blockIdx.x / ngroup;
   bool dense;
   const int n = ffn_rows(ucount, f, dense_min, &dense);
-  const int nch_all = (n + BD_CH - 1) / BD_CH, cps = (nch_all + BD_SPLIT - 1) / BD_SPLIT;
+  const int nch_all = (n + BD_CH - 1) / BD_CH, cps = (nch_all + nsplit - 1) / nsplit;
   const int ch0 = split * cps;                     // this split's chunks [ch0, ch0 + nch)
   const int nch = max(0, min(nch_all, ch0 + cps) - ch0);
-  const int rg = tid / 4, cq = tid % 4;            // staging: positions 4 rg .. 4 rg + 3, columns 8 cq ..
-  const int row_a = lane % 32, kh = 8 * (lane / 32);
-  const float hs = pow2_scale(__uint_as_float(hmax[row_a]));   // this lane's A row's scale
-  f16v acc[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f16v{};
-  // the split's list entries, so that no weight load waits for a list load
-  {
-    const int p0 = ch0 * BD_CH, np_ = min(n, (ch0 + nch) * BD_CH) - p0;
-    for (int q = tid; q < np_; q += blockDim.x) rows_l[q] = dense ? p0 + q : ulist[p0 + q];
-    __syncthreads();
-  }
+  const int pg = tid & 31;                         // staging: chunk positions 4 pg .. 4 pg + 3
+  const float hs = pow2_scale(__uint_as_float(hmax[lane & 31]));   // A staging: this lane's batch row
+  if (tid < BM) rsc[tid] = 1.f / pow2_scale(__uint_as_float(hmax[tid]));
+  f16v acc = {};
 
-  struct Stage {
-    uint4 wv[NT][4], wv2[4]; // four rows' 16-byte pieces per tile (fp32: two each)
-    float scale[4];
-    float4 hv[4][2];         // this wave's four K steps of h (8 values each)
+  // the row ids of chunk c's positions 4 pg + q (clamped into the list)
+  auto load_ids = [&](int c, int (&id)[4]) __attribute__((always_inline)) {
+    const int base = (ch0 + c) * BD_CH;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) id[q] = ulist[max(0, min(base + 4 * pg + q, n - 1))];
   };
-  auto fetch = [&](int c, Stage& st) __attribute__((always_inline)) {
+  // Items of a thread: i = 0, 1 are the adjacent tiles 2 (t >> 7) + i (t = tid), in
+  // both at columns 8 cq .. 8 cq + 7 with cq = (t >> 5) & 3, so a row's two
+  // Q4_0 block scales are one aligned 4-byte word (d / 32 is even).
+  struct Stage {
+    uint4 wv[2][4][NWV / 2];  // items x four rows: 16 bytes (fp32: 32) of each row segment
+    uint32_t sc[4];           // Q4_0: the two tiles' block scales of each row (fp16 bits)
+    float4 hv[2];             // 8 values of h for the A operands
+  };
+  auto fetch = [&](int c, const int (&id)[4], Stage& st) __attribute__((always_inline)) {
     const int base = (ch0 + c) * BD_CH;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int e = min(base + 4 * rg + q, n - 1);
-      const int row = rows_l[e - ch0 * BD_CH];
-      st.scale[q] = 1.f;
-      if constexpr (WT == DT_F16) {
+      const size_t row = (size_t)(dense ? max(0, min(base + 4 * pg + q, n - 1)) : id[q]);
+      if constexpr (WT == DT_Q4)   // a pair wholly past d is clamped to the row's last pair (dropped)
+        st.sc[q] = *reinterpret_cast<const uint32_t*>(down_sc + row * (d / 32) +
+                                                      min(c0 / 32 + 2 * (tid >> 7), d / 32 - 2));
+      else
+        st.sc[q] = 0u;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          st.wv[nt][q] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(downT) + (size_t)row * d + c0 +
-                                                         BM * nt + 8 * cq);
-      } else if constexpr (WT == DT_F32) {
-        const float* fp = static_cast<const float*>(downT) + (size_t)row * d + c0 + 8 * cq;
-        st.wv[0][q] = *reinterpret_cast<const uint4*>(fp);
-        st.wv2[q] = *reinterpret_cast<const uint4*>(fp + 4);
-      } else {
-        st.wv[0][q] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(downT) + (size_t)row * (d / 2) + c0 / 2);
-        st.scale[q] = (float)__builtin_bit_cast(_Float16, down_sc[(size_t)row * (d / 32) + c0 / 32]);
-      }
-    }
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int ks = base + 16 * (4 * w + s4);
-      const float4* hp = reinterpret_cast<const float4*>(h32 + (size_t)(ks >> 4) * 512 + 8 * lane);
-      st.hv[s4][0] = hp[0];
-      st.hv[s4][1] = hp[1];
-    }
-  };
-  // The A operands of a chunk: h times the row scale as hi/lo.  h at positions
-  // past the list end is whatever an earlier call left there: it is zeroed
-  // (the weights there are zero, but 0 * NaN is not).
-  h8v ah[4], al[4];
-  auto make_a = [&](const Stage& st, int c) __attribute__((always_inline)) {
-    const int base = (ch0 + c) * BD_CH;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int jj = base + 16 * (4 * w + s4) + kh;
-      const float hvv[8] = {st.hv[s4][0].x, st.hv[s4][0].y, st.hv[s4][0].z, st.hv[s4][0].w,
-                            st.hv[s4][1].x, st.hv[s4][1].y, st.hv[s4][1].z, st.hv[s4][1].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        _Float16 hi, lo;
-        split_f16(jj + e < n ? hvv[e] * hs : 0.f, &hi, &lo);
-        ah[s4][e] = hi;
-        al[s4][e] = lo;
-      }
-    }
-  };
-  auto stage_lds = [&](const Stage& st, int c) __attribute__((always_inline)) {
-    const int base = (ch0 + c) * BD_CH;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float v[4][8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bool ok = base + 4 * rg + q < n;
-        if constexpr (WT == DT_F16) {
-          const h8v hv = as_h8(st.wv[nt][q]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[q][e] = ok ? (float)hv[e] : 0.f;
-        } else if constexpr (WT == DT_F32) {
-          const float a[8] = {__uint_as_float(st.wv[0][q].x), __uint_as_float(st.wv[0][q].y),
-                              __uint_as_float(st.wv[0][q].z), __uint_as_float(st.wv[0][q].w),
-                              __uint_as_float(st.wv2[q].x), __uint_as_float(st.wv2[q].y),
-                              __uint_as_float(st.wv2[q].z), __uint_as_float(st.wv2[q].w)};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[q][e] = ok ? a[e] : 0.f;
+      for (int i = 0; i < 2; ++i) {
+        const int tile = 2 * (tid >> 7) + i;
+        if constexpr (WT == DT_Q4) {
+          const int cb = min(c0 + BM * tile, d - BM);               // the tile's Q4_0 block (clamped)
+          st.wv[i][q][0] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(downT) + row * (d / 2) + cb / 2);
         } else {
-          // columns 8cq..8cq+7 of the 32-weight block: low nibbles of bytes 0..15 are
-          // weights 0..15, high nibbles weights 16..31
-          const h8v qv = q4_h8(st.wv[0][q], 8 * (cq & 1), cq >= 2);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[q][e] = ok ? st.scale[q] * (float)qv[e] : 0.f;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        _Float16 hi[4], lo[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) split_f16(v[q][e], &hi[q], &lo[q]);
-        typedef _Float16 h4v __attribute__((ext_vector_type(4)));
-        *reinterpret_cast<h4v*>(&wt[0][BM * nt + 8 * cq + e][4 * rg]) = h4v{hi[0], hi[1], hi[2], hi[3]};
-        if constexpr (NW == 2)
-          *reinterpret_cast<h4v*>(&wt[1][BM * nt + 8 * cq + e][4 * rg]) = h4v{lo[0], lo[1], lo[2], lo[3]};
-      }
-    }
-  };
-
-  // chunk c: stage its weights, start the next chunk's loads, multiply
-  auto step = [&](Stage& cur, Stage& nxt, int c) __attribute__((always_inline)) {
-    stage_lds(cur, c);
-    make_a(cur, c);
-    if (c + 1 < nch) fetch(c + 1, nxt);
-    __syncthreads();
-    const int base = (ch0 + c) * BD_CH;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int kb = 16 * (4 * w + s4) + kh;
-      if (base + 16 * (4 * w + s4) < n) {         // wave-uniform: a step wholly past the end is skipped
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const h8v bw = *reinterpret_cast<const h8v*>(&wt[0][BM * nt + row_a][kb]);
-          acc[nt] = mfma(ah[s4], bw, acc[nt]);
-          acc[nt] = mfma(al[s4], bw, acc[nt]);
-          if constexpr (NW == 2) {
-            const h8v bl = *reinterpret_cast<const h8v*>(&wt[1][BM * nt + row_a][kb]);
-            acc[nt] = mfma(ah[s4], bl, acc[nt]);
+          const int col = min(c0 + BM * tile + 8 * ((tid >> 5) & 3), d - 8);
+          if constexpr (WT == DT_F16) {
+            st.wv[i][q][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(downT) + row * d + col);
+          } else {
+            const float* fp = static_cast<const float*>(downT) + row * d + col;
+            st.wv[i][q][0] = *reinterpret_cast<const uint4*>(fp);
+            st.wv[i][q][1] = *reinterpret_cast<const uint4*>(fp + 4);
           }
         }
       }
     }
+    const float4* hp = reinterpret_cast<const float4*>(h32 + (size_t)((ch0 + c) * (BD_CH / 16) + w) * 512 + 8 * lane);
+    st.hv[0] = hp[0];
+    st.hv[1] = hp[1];
+  };
+  // a chunk's operands into LDS; positions past the list end and columns past d are zero
+  // (h there is whatever an earlier call left: 0 * NaN is not zero)
+  auto convert = [&](const Stage& st, int c) __attribute__((always_inline)) {
+    const int base = (ch0 + c) * BD_CH;
+    typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int tile = 2 * (tid >> 7) + i, cq = (tid >> 5) & 3;
+      const bool okc = c0 + BM * tile + 8 * cq < d;
+      _Float16* dst0 = &wt[0][BM * tile + 8 * cq][4 * pg];
+      if constexpr (WT == DT_F32) {
+        float v[4][8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bool ok = okc && c < nch && base + 4 * pg + q < n;
+          const float a8[8] = {__uint_as_float(st.wv[i][q][0].x), __uint_as_float(st.wv[i][q][0].y),
+                               __uint_as_float(st.wv[i][q][0].z), __uint_as_float(st.wv[i][q][0].w),
+                               __uint_as_float(st.wv[i][q][1].x), __uint_as_float(st.wv[i][q][1].y),
+                               __uint_as_float(st.wv[i][q][1].z), __uint_as_float(st.wv[i][q][1].w)};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[q][e] = ok ? a8[e] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          _Float16 hi[4], lo[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) split_f16(v[q][e], &hi[q], &lo[q]);
+          *reinterpret_cast<h4v*>(dst0 + e * BD_PAD) = h4v{hi[0], hi[1], hi[2], hi[3]};
+          *reinterpret_cast<h4v*>(&wt[NW - 1][BM * tile + 8 * cq + e][4 * pg]) = h4v{lo[0], lo[1], lo[2], lo[3]};
+        }
+      } else {
+        // fp16: the weights themselves; Q4_0: (q - 8) exact in fp16 times the block
+        // scale as hi = fl16(q s) and lo = fl16(q s - hi) (one packed multiply and one
+        // packed fused multiply-add: q s - hi needs at most 4 significant bits).  Two
+        // rows at a time, each column's pair of positions written at once.
+#pragma unroll
+        for (int rp = 0; rp < 4; rp += 2) {
+          h8v hi[2], lo[2];
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2) {
+            const int q = rp + q2;
+            // zeroed by an AND with a mask (a select here becomes a branch that the
+            // compiler places next to the loads, with a wait for all of them)
+            const uint32_t m = 0u - (uint32_t)(okc && c < nch && base + 4 * pg + q < n);
+            if constexpr (WT == DT_F16) {
+              const uint4 wv = st.wv[i][q][0];
+              hi[q2] = as_h8(make_uint4(wv.x & m, wv.y & m, wv.z & m, wv.w & m));
+            } else {
+              const h8v qv = q4_h8(st.wv[i][q][0], 8 * (cq & 1), cq >= 2);
+              const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)((st.sc[q] >> (16 * i)) & m));
+              const h8v s8 = {sv, sv, sv, sv, sv, sv, sv, sv};
+              hi[q2] = qv * s8;
+              lo[q2] = __builtin_elementwise_fma(qv, s8, -hi[q2]);
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            *reinterpret_cast<h2v*>(dst0 + e * BD_PAD + rp) = h2v{hi[0][e], hi[1][e]};
+            if constexpr (NW == 2)
+              *reinterpret_cast<h2v*>(&wt[NW - 1][BM * tile + 8 * cq + e][4 * pg + rp]) = h2v{lo[0][e], lo[1][e]};
+          }
+        }
+      }
+    }
+    // A operands: K step w of the chunk, operand slot lane (batch row lane % 32)
+    const int jj = base + 16 * w + 8 * (lane / 32);
+    const float hv8[8] = {st.hv[0].x, st.hv[0].y, st.hv[0].z, st.hv[0].w,
+                          st.hv[1].x, st.hv[1].y, st.hv[1].z, st.hv[1].w};
+    h8v ahi, alo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      _Float16 hi, lo;
+      split_f16(c < nch && jj + e < n ? hv8[e] * hs : 0.f, &hi, &lo);
+      ahi[e] = hi;
+      alo[e] = lo;
+    }
+    *reinterpret_cast<h8v*>(&as[0][w][8 * lane]) = ahi;
+    *reinterpret_cast<h8v*>(&as[1][w][8 * lane]) = alo;
+  };
+
+  // chunk c: the next chunk's loads, its operands into LDS, the products.  No
+  // branch: the loop runs whole pairs of chunks, a chunk past the split's end
+  // converts to zeros, and the loads past the end repeat the last chunk
+  // (clamped) -- a branch around a use lets the compiler sink loads and
+  // operand math into it, after the next chunk's loads, and then wait for
+  // those too.
+  auto step = [&](const Stage& cur, Stage& nxt, const int (&id_next)[4], int (&id_after)[4], int c)
+      __attribute__((always_inline)) {
+    fetch(min(c + 1, nch - 1), id_next, nxt);      // in flight while this chunk is converted and multiplied
+    convert(cur, c);
+    load_ids(min(c + 2, nch - 1), id_after);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < BD_CH / 16; ++ks) {
+      const int kb = 16 * ks + 8 * (lane / 32);
+      const h8v ah = *reinterpret_cast<const h8v*>(&as[0][ks][8 * lane]);
+      const h8v al = *reinterpret_cast<const h8v*>(&as[1][ks][8 * lane]);
+      const h8v bw = *reinterpret_cast<const h8v*>(&wt[0][BM * w + (lane & 31)][kb]);
+      acc = mfma(ah, bw, acc);
+      acc = mfma(al, bw, acc);
+      if constexpr (NW == 2) {
+        const h8v bl = *reinterpret_cast<const h8v*>(&wt[1][BM * w + (lane & 31)][kb]);
+        acc = mfma(ah, bl, acc);
+      }
+    }
     __syncthreads();
   };
+  int id_a[4], id_b[4];
   Stage s0, s1;
-  if (nch > 0) fetch(0, s0);
-  for (int c = 0; c < nch; c += 2) {
-    step(s0, s1, c);
-    if (c + 1 < nch) step(s1, s0, c + 1);
+  if (nch > 0) {
+    load_ids(0, id_a);
+    fetch(0, id_a, s0);
+    load_ids(min(1, nch - 1), id_b);
   }
-  const int col = lane % 32, half = lane / 32;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int c = 0; c < nch; c += 2) {
+    step(s0, s1, id_b, id_a, c);
+    step(s1, s0, id_a, id_b, c + 1);
+  }
+  __syncthreads();                                 // rsc is written
+  // lane holds column c0 + 32 w + lane % 32, batch rows 8 g + 4 (lane / 32) + v
+  const int cg = c0 + BM * w + (lane & 31);
+  if (cg < d) {
+    const float bd = (b_down && split == 0) ? b_down[cg] : 0.f;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[w][nt][(8 * g + 4 * half + v) * BM + col] = acc[nt][4 * g + v];
-  __syncthreads();
-  for (int e2 = tid; e2 < NT * BM * BM; e2 += blockDim.x) {
-    const int nt = e2 / (BM * BM), e = e2 % (BM * BM);
-    const int b = e / BM, c = e % BM, cg = c0 + BM * nt + c;
-    if (b >= batch || cg >= d) continue;
-    float v = red[0][nt][e] + red[1][nt][e] + red[2][nt][e] + red[3][nt][e];
-    v *= 1.f / pow2_scale(__uint_as_float(hmax[b]));       // the row's scale undone exactly
-    if (b_down && split == 0) v += b_down[cg];
-    y_part[((size_t)split * BM + b) * d + cg] = v;
+      for (int v = 0; v < 4; ++v) {
+        const int b = 8 * g + 4 * (lane / 32) + v;
+        if (b < batch) y_part[((size_t)split * BM + b) * d + cg] = acc[4 * g + v] * rsc[b] + bd;
+      }
   }
 }
 
-// y[b] = the BD_SPLIT partial vectors of k_bdown added in order (b < batch)
-__global__ void k_bsum_y(const float* __restrict__ y_part, int batch, int d, float* __restrict__ y) {
+// y[b] = the np partial vectors of k_bdown added in order (b < batch)
+__global__ void k_bsum_y(const float* __restrict__ y_part, int np, int batch, int d, float* __restrict__ y) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= batch * d) return;
   float v = y_part[e];
-  for (int p = 1; p < BD_SPLIT; ++p) v += y_part[(size_t)p * BM * d + e];
+  for (int p = 1; p < np; ++p) v += y_part[(size_t)p * BM * d + e];
   y[e] = v;
 }
 
