@@ -89,7 +89,7 @@ int k2_blocks_max(int ffn) { return k2_blocks_for(ffn); }
 int k2_cap(int ffn) { return K2_WAVES * cdiv(ffn, k2_blocks_for(ffn) * K2_WAVES); }
 size_t k2_pairs_max(int ffn) { return (size_t)k2_blocks_for(ffn) * k2_cap(ffn); }
 // blocks of the batched score kernel: one tile of 32 neurons each
-int bscore_blocks(int ffn) { return cdiv(ffn, pib::BM); }
+int bscore_blocks(int ffn) { return cdiv(ffn, pib::BM); }   // 32-neuron tiles of the batched score kernel
 
 struct WsLayout {
   size_t t, v, ss, tcnt, xbuf, ybuf, mask, pmask, h, pid, ph, cnt, misc;
@@ -533,7 +533,7 @@ void b_predict(const pi_layer* L, int batch, const Ws& W, float* scores, uint8_t
   hipLaunchKernelGGL(pib::k_bsplit_t, dim3(kBatchM), dim3(pib::BT_T), 0, st, W.tpart, ks, L->rank, W.sx, W.th, W.tl,
                      W.st);
   mark(tr, 3, st);
-  const dim3 g2(bscore_blocks(L->ffn));
+  const dim3 g2(cdiv(L->ffn, pib::BS_T * pib::BM));
   const float* pb = L->pbias ? L->pbias : L->bias;
   if (L->p_dtype == PI_F16)
     hipLaunchKernelGGL(pib::k_bscore<DT_F16>, g2, dim3(256), 0, st, L->B, pb, L->ffn, L->rank, batch, W.th, W.tl,

@@ -348,76 +348,150 @@ k_bsplit_t(const float* __restrict__ t_part, int ksplit, int r, const float* __r
 }
 
 // ------------------------------------------------------------ predictor 2
-// s[b][i] = c_i + sum_k t[b][k] B[i][k] for one tile of 32 neurons per block,
-// its 4 waves splitting K into contiguous ranges (partials summed through LDS
-// in wave order); mask m[i][b] = (s > 0) for b < batch (0 for padded rows),
-// one byte each in neuron-major layout [ffn][32]; union u[i] = OR_b m[i][b];
-// the tile's union count to cnt_blk[block].  Optional outputs in
-// sequence-major layout: scores[b][i] and mask_out[b][i].  Neurons i < hot
-// (the hot-dense prefix) are on in every sequence without a score: a tile
-// wholly inside the prefix reads no row of B, and no score of the prefix is
-// written.
-constexpr int BS_W = 4;
+// s[b][i] = c_i + sum_k t[b][k] B[i][k] for BS_T tiles of 32 neurons per block:
+// its 4 waves split K into contiguous ranges and each multiplies its range of t
+// (hi/lo, read once per block instead of once per tile) with the rows of all the
+// block's tiles; the partials are summed through LDS in wave order.  Mask
+// m[i][b] = (s > 0) for b < batch (0 for padded rows), one byte each in
+// neuron-major layout [ffn][32]; union u[i] = OR_b m[i][b]; each tile's union
+// count to cnt_blk[tile].  Optional outputs in sequence-major layout:
+// scores[b][i] and mask_out[b][i].  Neurons i < hot (the hot-dense prefix) are on
+// in every sequence without a score: a block wholly inside the prefix reads no
+// row of B, and no score of the prefix is written.
+constexpr int BS_W = 4;                  // waves (K split)
+constexpr int BS_T = 4;                  // 32-neuron tiles per block
 
 template <int PT>
-__global__ void __launch_bounds__(BS_W * WAVE)
+__global__ void __launch_bounds__(BS_W * WAVE) __attribute__((amdgpu_waves_per_eu(2)))
 k_bscore(const void* __restrict__ Bm, const float* __restrict__ pbias, int f, int r, int batch,
          const _Float16* __restrict__ th, const _Float16* __restrict__ tl, const float* __restrict__ st,
          uint8_t* __restrict__ m_nm, uint8_t* __restrict__ u, int32_t* __restrict__ cnt_blk,
          float* __restrict__ scores, uint8_t* __restrict__ mask_out, int hot) {
-  __shared__ float red[BS_W][BM * BM];
-  __shared__ int cnt_w;
+  constexpr int KS_U = PT == DT_F32 ? 2 : 4;         // K steps per batch of loads
+  constexpr int WV = PT == DT_F32 ? 2 : 1;           // 16-byte pieces per 8 weights
+  __shared__ float red[BS_W][BS_T][BM * BM];
+  __shared__ uint32_t onr[BS_T][BS_W * WAVE];
+  __shared__ int cnt_t[BS_T];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int col = lane % 32, half = lane / 32;
-  const int i0 = blockIdx.x * BM;
-  const int i = min(i0 + col, f - 1);
-  f16v acc = {};
+  const int i0 = blockIdx.x * BS_T * BM;
+  f16v acc[BS_T];
+#pragma unroll
+  for (int t = 0; t < BS_T; ++t) acc[t] = f16v{};
   const int ns = r / 16, kbeg = 16 * (w * ns / BS_W), kend = 16 * ((w + 1) * ns / BS_W);
-  if (i0 + BM > hot)                         // a tile wholly in the hot prefix reads no row of B
-    for (int k = kbeg; k < kend; k += 16 * KU) mfma_window<PT>(acc, th, tl, Bm, (size_t)i, r, k, kend, 16, lane);
+  // the epilogue's predictor biases and row scales, loaded ahead of the products
+  const int c = tid % BM;
+  float cbv[BS_T], stv[BM / 8];
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+  for (int t = 0; t < BS_T; ++t) cbv[t] = pbias[min(i0 + BM * t + c, f - 1)];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[w][(8 * g + 4 * half + v) * BM + col] = acc[4 * g + v];
-  if (tid == 0) cnt_w = 0;
-  __syncthreads();
-  // thread (neuron c = tid % 32, batch rows bq = tid / 32 .. step 8): 256 threads
-  // cover the 32 x 32 tile four rows each
-  const int c = tid % BM, ii = i0 + c;
-  const bool col_ok = ii < f;
-  const float cb = pbias[min(ii, f - 1)];
-  uint32_t on_rows = 0;
+  for (int q = 0; q < BM / 8; ++q) stv[q] = st[tid / BM + 8 * q];
+  if (i0 + BS_T * BM > hot) {                // block-uniform: a block wholly in the hot prefix reads no row of B
+    for (int k = kbeg; k < kend; k += 16 * KS_U) {
+      h8v ah[KS_U], al[KS_U];
+      uint4 bv[BS_T][KS_U][WV];
 #pragma unroll
-  for (int q = 0; q < BM / 8; ++q) {
-    const int b = tid / BM + 8 * q;
-    const int e = b * BM + c;
-    float sacc = red[0][e];
+      for (int uu = 0; uu < KS_U; ++uu) {
+        const int ks = min(k + 16 * uu, kend - 16), kk = ks + 8 * half;
+        const size_t xo = (size_t)(ks >> 4) * 512 + 8 * lane;
+        ah[uu] = *reinterpret_cast<const h8v*>(th + xo);
+        al[uu] = *reinterpret_cast<const h8v*>(tl + xo);
 #pragma unroll
-    for (int v = 1; v < BS_W; ++v) sacc += red[v][e];
-    const float sv = sacc * (1.f / st[b]) + cb;          // the row's scale undone exactly
-    const bool on = col_ok && b < batch && (ii < hot || sv > 0.f);
-    on_rows |= (on ? 1u : 0u) << b;
-    if (col_ok) {
-      m_nm[(size_t)ii * BM + b] = on ? 1 : 0;
-      if (b < batch) {
-        if (scores && ii >= hot) scores[(size_t)b * f + ii] = sv;
-        if (mask_out) mask_out[(size_t)b * f + ii] = on ? 1 : 0;
+        for (int t = 0; t < BS_T; ++t) {
+          const size_t row = (size_t)min(i0 + BM * t + col, f - 1);
+          if constexpr (PT == DT_F16) {
+            bv[t][uu][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(Bm) + row * r + kk);
+          } else {
+            const float* fp = static_cast<const float*>(Bm) + row * r + kk;
+            bv[t][uu][0] = *reinterpret_cast<const uint4*>(fp);
+            bv[t][uu][1] = *reinterpret_cast<const uint4*>(fp + 4);
+          }
+        }
+      }
+      PI_ISSUE_FENCE();
+      const h8v z8 = {};
+#pragma unroll
+      for (int uu = 0; uu < KS_U; ++uu) {
+        const bool ok = k + 16 * uu < kend;
+        const h8v a = ok ? ah[uu] : z8, l = ok ? al[uu] : z8;
+#pragma unroll
+        for (int t = 0; t < BS_T; ++t) {
+          if constexpr (PT == DT_F16) {
+            const h8v bw = as_h8(bv[t][uu][0]);
+            acc[t] = mfma(a, bw, acc[t]);
+            acc[t] = mfma(l, bw, acc[t]);
+          } else {
+            const float v[8] = {__uint_as_float(bv[t][uu][0].x), __uint_as_float(bv[t][uu][0].y),
+                                __uint_as_float(bv[t][uu][0].z), __uint_as_float(bv[t][uu][0].w),
+                                __uint_as_float(bv[t][uu][1].x), __uint_as_float(bv[t][uu][1].y),
+                                __uint_as_float(bv[t][uu][1].z), __uint_as_float(bv[t][uu][1].w)};
+            h8v bh, bl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              _Float16 hh, ll;
+              split_f16(v[e], &hh, &ll);
+              bh[e] = hh;
+              bl[e] = ll;
+            }
+            acc[t] = mfma(a, bh, acc[t]);
+            acc[t] = mfma(l, bh, acc[t]);
+            acc[t] = mfma(a, bl, acc[t]);
+          }
+        }
       }
     }
   }
-  __syncthreads();                          // red is reused below for the union bits
-  reinterpret_cast<uint32_t*>(red[0])[tid] = on_rows;
-  __syncthreads();
-  if (tid < BM) {
-    uint32_t all = 0;
 #pragma unroll
-    for (int q = 0; q < (BS_W * WAVE) / BM; ++q) all |= reinterpret_cast<const uint32_t*>(red[0])[tid + BM * q];
-    const bool un = all != 0;
-    if (col_ok) u[ii] = un ? 1 : 0;
-    if (col_ok && un) atomicAdd(&cnt_w, 1);   // LDS atomic
+  for (int t = 0; t < BS_T; ++t)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[w][t][(8 * g + 4 * half + v) * BM + col] = acc[t][4 * g + v];
+  if (tid < BS_T) cnt_t[tid] = 0;
+  __syncthreads();
+  // per tile, thread (neuron c = tid % 32, batch rows tid / 32 + 8 q): 256 threads
+  // cover the 32 x 32 tile four rows each
+#pragma unroll
+  for (int t = 0; t < BS_T; ++t) {
+    const int ii = i0 + BM * t + c;
+    const bool col_ok = ii < f;
+    const float cb = cbv[t];
+    uint32_t on_rows = 0;
+#pragma unroll
+    for (int q = 0; q < BM / 8; ++q) {
+      const int b = tid / BM + 8 * q;
+      const int e = b * BM + c;
+      float sacc = red[0][t][e];
+#pragma unroll
+      for (int v = 1; v < BS_W; ++v) sacc += red[v][t][e];
+      const float sv = sacc * (1.f / stv[q]) + cb;         // the row's scale undone exactly
+      const bool on = col_ok && b < batch && (ii < hot || sv > 0.f);
+      on_rows |= (on ? 1u : 0u) << b;
+      if (col_ok) {
+        m_nm[(size_t)ii * BM + b] = on ? 1 : 0;
+        if (b < batch) {
+          if (scores && ii >= hot) scores[(size_t)b * f + ii] = sv;
+          if (mask_out) mask_out[(size_t)b * f + ii] = on ? 1 : 0;
+        }
+      }
+    }
+    onr[t][tid] = on_rows;
   }
   __syncthreads();
-  if (tid == 0 && cnt_blk) cnt_blk[blockIdx.x] = cnt_w;
+  if (tid < BS_T * BM) {
+    const int t = tid / BM, ii = i0 + BM * t + c;
+    uint32_t all = 0;
+#pragma unroll
+    for (int q = 0; q < (BS_W * WAVE) / BM; ++q) all |= onr[t][c + BM * q];
+    const bool un = all != 0;
+    if (ii < f) u[ii] = un ? 1 : 0;
+    if (ii < f && un) atomicAdd(&cnt_t[t], 1);   // LDS atomic
+  }
+  __syncthreads();
+  if (tid < BS_T && cnt_blk) {
+    const int tile = blockIdx.x * BS_T + tid;
+    if (tile < (f + BM - 1) / BM) cnt_blk[tile] = cnt_t[tid];
+  }
 }
 
 // The rows the batched FFN runs over: the union list, or -- when the union

@@ -110,12 +110,14 @@ def test_summarize_traffic(tmp_path):
 
 def test_hot_prefix_bytes():
     """A hot-dense prefix drops its rows of B and predictor biases from the score
-    kernel's bytes (batch 1: every prefix slot; batch > 1: whole 32-neuron tiles)."""
+    kernel's bytes (batch 1: every prefix slot; batch > 1: whole 128-neuron blocks)."""
     cfg = workload.CONFIGS[4]
     pb = 2
     a, b = bench.kernel_bytes(cfg, 1, 4000, 3900), bench.kernel_bytes(cfg, 1, 4000, 3900, hot=1109)
     assert a["k_score"] - b["k_score"] == 1109 * (cfg.rank * pb + 4)
     assert a["k_down"] == b["k_down"] and a["k_predict_t"] == b["k_predict_t"]
     a, b = bench.kernel_bytes(cfg, 32, 5000), bench.kernel_bytes(cfg, 32, 5000, hot=77)
-    assert a["k_bscore"] - b["k_bscore"] == 64 * (cfg.rank * pb + 4)
+    assert a["k_bscore"] == b["k_bscore"]
+    a, b = bench.kernel_bytes(cfg, 32, 5000), bench.kernel_bytes(cfg, 32, 5000, hot=300)
+    assert a["k_bscore"] - b["k_bscore"] == 256 * (cfg.rank * pb + 4)
 
