@@ -100,6 +100,10 @@ struct WsLayout {
 };
 
 constexpr int kBatchM = pib::BM;      // padded batch rows of the batched GEMMs
+// blocks of the batched up GEMMs, which loop over the union's tiles (a multiple of
+// every K-split count, so a block of the K-split GEMM keeps its split)
+constexpr int kUpGrid = 512;
+static_assert(kUpGrid % pib::BU_KSMAX == 0, "blocks keep their K split");
 constexpr int kMaxKSplit = 16;        // K splits of the batched predictor's first GEMM
 static_assert(kMaxKSplit <= pib::BT_KS, "k_bsplit_t holds every split of a value");
 
@@ -559,7 +563,8 @@ template <int WT, int ACT>
 void b_ffn_t(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, const int32_t* ucount, float* y,
              hipStream_t st, const pi_trace* tr) {
   if constexpr (WT != DT_Q4) {
-    hipLaunchKernelGGL((pib::k_bup<WT, ACT>), dim3(cdiv(L->ffn, kBatchM)), dim3(pib::BUP_W * WAVE), 0, st,
+    hipLaunchKernelGGL((pib::k_bup<WT, ACT>), dim3(std::min(cdiv(L->ffn, kBatchM), kUpGrid)), dim3(pib::BUP_W * WAVE),
+                       0, st,
                        L->gate.w, L->gate.scale, L->up.w, L->up.scale, L->bias, L->ffn, L->d, W.xh, W.xl, ulist,
                        ucount, W.mnm, W.sx, W.h32, W.hmax, dense_min(L));
   } else {
@@ -567,10 +572,12 @@ void b_ffn_t(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, co
     // activation (for fp16 weights the one-pass GEMM over the whole K measured faster)
     const int ks = pib::bu_ks(L->d);
     const int groups = cdiv(cdiv(L->ffn, kBatchM), pib::BU_TPB);
-    hipLaunchKernelGGL((pib::k_bup2<WT, act_nmat<ACT>()>), dim3(groups * ks), dim3(512), 0, st, L->gate.w,
+    hipLaunchKernelGGL((pib::k_bup2<WT, act_nmat<ACT>()>), dim3(std::min(groups * ks, kUpGrid)), dim3(512), 0, st,
+                       L->gate.w,
                        L->gate.scale, L->up.w, L->up.scale, L->ffn, L->d, ks, W.xh, W.xl, ulist, ucount, dense_min(L),
                        W.zpart);
-    hipLaunchKernelGGL((pib::k_bup_epi<ACT>), dim3(cdiv(L->ffn, 256 / kBatchM)), dim3(256), 0, st, W.zpart, ks,
+    hipLaunchKernelGGL((pib::k_bup_epi<ACT>), dim3(std::min(cdiv(L->ffn, 256 / kBatchM), 2 * kUpGrid)), dim3(256), 0,
+                       st, W.zpart, ks,
                        L->ffn, ulist, ucount, dense_min(L), L->bias, W.mnm, W.sx, W.h32, W.hmax);
   }
   mark(tr, 6, st);

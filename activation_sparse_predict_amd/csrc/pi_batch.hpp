@@ -505,8 +505,9 @@ __device__ __forceinline__ int ffn_rows(const int32_t* __restrict__ ucount, int 
 }
 
 // ------------------------------------------------------------ up / gate
-// z = X W^T over the union rows.  Block q covers union list entries [32 q,
-// 32 q + 32) (blocks past the union's end return); its BUP_W waves split K
+// z = X W^T over the union rows (fp16 and fp32 weights).  A block takes tiles
+// q = blockIdx.x, blockIdx.x + gridDim.x, ... of 32 union list entries [32 q,
+// 32 q + 32) while they exist; its BUP_W waves split K
 // into contiguous ranges and their partial tiles are summed through LDS in
 // wave order.  Epilogue: z's row b times 1 / sx[b]; h[b] = m[i][b] ?
 // act(z + bias) : 0, written in fp32 to h32 as a [32][h_stride] operand-order
@@ -534,100 +535,57 @@ k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, con
   const int col = lane % 32, half = lane / 32;
   bool dense;
   const int n = ffn_rows(ucount, f, dense_min, &dense);
-  const int t0 = blockIdx.x * BM;
-  if (t0 >= n) return;                                        // block-uniform
-  const int row = dense ? min(t0 + col, n - 1) : ulist[min(t0 + col, n - 1)];
-  f16v acc[NMAT];
+  // union tiles blockIdx.x, blockIdx.x + gridDim.x, ... (the grid is sized for the
+  // chip, the tile count is on the device)
+  for (int tile = blockIdx.x; tile * BM < n; tile += gridDim.x) {
+    const int t0 = tile * BM;
+    const int row = dense ? min(t0 + col, n - 1) : ulist[min(t0 + col, n - 1)];
+    f16v acc[NMAT];
 #pragma unroll
-  for (int mt = 0; mt < NMAT; ++mt) acc[mt] = f16v{};
-  if constexpr (WT == DT_Q4) {
-    // one Q4_0 block (32 k) per step pair: low nibbles give k 0..15, high nibbles k 16..31;
-    // KU / 2 blocks per batch of loads; this wave's blocks [kb0, kb1)
-    constexpr int QB = KU / 2;
-    const int nq = d / 32, kbeg = 32 * (w * nq / BUP_W), kend = 32 * ((w + 1) * nq / BUP_W);
-    for (int k = kbeg; k < kend; k += 32 * QB) {
-      uint4 cq[NMAT][QB];
-      float sc[NMAT][QB];
-      h8v ah[QB][2], al[QB][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int kb = min(k + 32 * qb, kend - 32);
-#pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt) {
-          const void* wp = (NMAT == 2 && mt == 0) ? gate_w : up_w;
-          const uint16_t* sp = (NMAT == 2 && mt == 0) ? gate_sc : up_sc;
-          cq[mt][qb] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(wp) + (size_t)row * (d / 2) + kb / 2);
-          sc[mt][qb] = (float)__builtin_bit_cast(_Float16, sp[(size_t)row * (d / 32) + kb / 32]);
-        }
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const size_t xo = (size_t)((kb + 16 * st) >> 4) * 512 + 8 * lane;
-          ah[qb][st] = *reinterpret_cast<const h8v*>(xh + xo);
-          al[qb][st] = *reinterpret_cast<const h8v*>(xl + xo);
-        }
-      }
-      PI_ISSUE_FENCE();
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        if (k + 32 * qb >= kend) continue;
-#pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt) {
-          f16v p = {};
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const h8v bw = q4_h8(cq[mt][qb], 8 * half, st == 1);
-            p = mfma(ah[qb][st], bw, p);
-            p = mfma(al[qb][st], bw, p);
-          }
-          // the block's scale belongs to this lane's column (neuron)
-#pragma unroll
-          for (int x = 0; x < 16; ++x) acc[mt][x] = fmaf(sc[mt][qb], p[x], acc[mt][x]);
-        }
-      }
-    }
-  } else {
+    for (int mt = 0; mt < NMAT; ++mt) acc[mt] = f16v{};
     const int ns = d / 16, kbeg = 16 * (w * ns / BUP_W), kend = 16 * ((w + 1) * ns / BUP_W);
     for (int k = kbeg; k < kend; k += 16 * KU) {
 #pragma unroll
       for (int mt = 0; mt < NMAT; ++mt)
         mfma_window<WT>(acc[mt], xh, xl, (NMAT == 2 && mt == 0) ? gate_w : up_w, (size_t)row, d, k, kend, 16, lane);
     }
-  }
-  // the waves' partial tiles: lane holds neuron column col, batch rows 8g + 4*half + v
+    // the waves' partial tiles: lane holds neuron column col, batch rows 8g + 4*half + v
 #pragma unroll
-  for (int mt = 0; mt < NMAT; ++mt)
+    for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[w][mt][(8 * g + 4 * half + v) * BM + col] = acc[mt][4 * g + v];
-  if (tid < BM) rmax[tid] = 0u;
-  __syncthreads();
-  for (int e = tid; e < BM * BM; e += blockDim.x) {
-    const int b = e / BM, c = e % BM;
-    if (t0 + c >= n) continue;
-    const float ix = 1.f / sx[b];
-    float z[NMAT];
+        for (int v = 0; v < 4; ++v) red[w][mt][(8 * g + 4 * half + v) * BM + col] = acc[mt][4 * g + v];
+    if (tid < BM) rmax[tid] = 0u;
+    __syncthreads();
+    for (int e = tid; e < BM * BM; e += blockDim.x) {
+      const int b = e / BM, c = e % BM;
+      if (t0 + c >= n) continue;
+      const float ix = 1.f / sx[b];
+      float z[NMAT];
 #pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt) {
-      float s = 0.f;
+      for (int mt = 0; mt < NMAT; ++mt) {
+        float s = 0.f;
 #pragma unroll
-      for (int v = 0; v < BUP_W; ++v) s += red[v][mt][e];
-      z[mt] = s * ix;
+        for (int v = 0; v < BUP_W; ++v) s += red[v][mt][e];
+        z[mt] = s * ix;
+      }
+      const int rw = dense ? t0 + c : ulist[t0 + c];
+      float h = act_h<ACT>(z[0], bias[rw], z[NMAT - 1]);
+      if (m_nm[(size_t)rw * BM + b] == 0) h = 0.f;
+      h32[aop(b, t0 + c)] = h;
+      atomicMax(&rmax[b], __float_as_uint(fabsf(h)));         // LDS atomic
     }
-    const int rw = dense ? t0 + c : ulist[t0 + c];
-    float h = act_h<ACT>(z[0], bias[rw], z[NMAT - 1]);
-    if (m_nm[(size_t)rw * BM + b] == 0) h = 0.f;
-    h32[aop(b, t0 + c)] = h;
-    atomicMax(&rmax[b], __float_as_uint(fabsf(h)));         // LDS atomic
+    __syncthreads();
+    if (tid < BM && rmax[tid] != 0u) atomicMax(&hmax[tid], rmax[tid]);
+    __syncthreads();                                            // red and rmax are reused by the next tile
   }
-  __syncthreads();
-  if (tid < BM && rmax[tid] != 0u) atomicMax(&hmax[tid], rmax[tid]);
 }
 
 // ---------------------------------------------- up / gate, K-split (Q4_0)
 // z = X W^T over the union rows with the batch operand staged in LDS once per
-// block and used for BU_TPB row tiles.  Block id = g KS + s: row tiles
-// [g BU_TPB, (g + 1) BU_TPB) of the union list and K split s (the blocks of
+// block and used for BU_TPB row tiles.  Work item g KS + s: row tiles
+// [g BU_TPB, (g + 1) BU_TPB) of the union list and K split s (the items of
 // one split land on one XCD when KS = 8, so its X slice stays in that L2).
 // The split's K range is walked in chunks of KC: the chunk of X (fp16 hi and
 // lo, operand order) goes to LDS by LDS-DMA while each wave loads its weights
@@ -658,101 +616,106 @@ k_bup2(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, co
   static_assert(sizeof(float) * 8 * NMAT * BM * BM <= sizeof(xs), "red fits");
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int col = lane % 32, half = lane / 32;
-  const int g = blockIdx.x / KS, s = blockIdx.x % KS;
   bool dense;
   const int n = ffn_rows(ucount, f, dense_min, &dense);
-  const int t0 = g * BU_TPB * BM;
-  if (t0 >= n) return;                                        // block-uniform
-  const int tl = w % BU_TPB, kp = w / BU_TPB;                 // this wave's row tile and chunk half
-  const int pos = min(t0 + tl * BM + col, n - 1);
-  const size_t row = (size_t)(dense ? pos : ulist[pos]);
-  const int ksz = d / KS, kbeg = s * ksz;
-  f16v acc[NMAT];
+  // items blockIdx.x, blockIdx.x + gridDim.x, ... while their row tiles exist: item
+  // g KS + s is row-tile group g and K split s (gridDim.x is a multiple of KS, so
+  // a block keeps its split and its XCD)
+  for (int item = blockIdx.x; (item / KS) * BU_TPB * BM < n; item += gridDim.x) {
+    const int g = item / KS, s = item % KS;
+    const int t0 = g * BU_TPB * BM;
+    const int tl = w % BU_TPB, kp = w / BU_TPB;                 // this wave's row tile and chunk half
+    const int pos = min(t0 + tl * BM + col, n - 1);
+    const size_t row = (size_t)(dense ? pos : ulist[pos]);
+    const int ksz = d / KS, kbeg = s * ksz;
+    f16v acc[NMAT];
 #pragma unroll
-  for (int mt = 0; mt < NMAT; ++mt) acc[mt] = f16v{};
-  for (int kc = kbeg; kc < kbeg + ksz; kc += KC) {
-    const int kcn = min(KC, kbeg + ksz - kc);                 // a multiple of 64
-    // the chunk of X: K steps kc/16 .. (kc + kcn)/16 of hi and lo, 1 KB each
-    __syncthreads();                                          // the previous chunk is consumed
-    for (int p = w; p < 2 * (kcn / 16); p += 8) {
-      const int hl = p & 1, st = p >> 1;
-      const _Float16* src = (hl ? xl : xh) + (size_t)(kc / 16 + st) * 512;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 8 * lane),
-                                       (__attribute__((address_space(3))) void*)(&xs[hl][st * 512]), 16, 0, 0);
-    }
-    const int kw = kc + kp * (kcn / 2), kwn = kcn / 2;        // this wave's half
-    constexpr int QB = KH / 32;
-    // the row's nibbles for the half chunk (one 16-byte block per load) and its block
-    // scales two at a time: aligned words from the even block a0 = kw / 32 rounded
-    // down (d / 32 is even, so a word lies wholly inside the row or wholly past it,
-    // then clamped to the row's last word and not used); block kw / 32 + qb is
-    // half (o + qb) & 1 of word (o + qb) / 2, o = kw / 32 - a0
-    const int a0 = (kw / 32) & ~1, o = (kw / 32) & 1;
-    uint4 cq[NMAT][QB];
-    uint32_t scw[NMAT][QB / 2 + 1];
-#pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt) {
-      const void* wp = (NMAT == 2 && mt == 0) ? gate_w : up_w;
-      const uint16_t* sp = (NMAT == 2 && mt == 0) ? gate_sc : up_sc;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int kb = kw + 32 * min(qb, kwn / 32 - 1);
-        cq[mt][qb] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(wp) + row * (d / 2) + kb / 2);
+    for (int mt = 0; mt < NMAT; ++mt) acc[mt] = f16v{};
+    for (int kc = kbeg; kc < kbeg + ksz; kc += KC) {
+      const int kcn = min(KC, kbeg + ksz - kc);                 // a multiple of 64
+      // the chunk of X: K steps kc/16 .. (kc + kcn)/16 of hi and lo, 1 KB each
+      __syncthreads();                                          // the previous chunk is consumed
+      for (int p = w; p < 2 * (kcn / 16); p += 8) {
+        const int hl = p & 1, st = p >> 1;
+        const _Float16* src = (hl ? xl : xh) + (size_t)(kc / 16 + st) * 512;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 8 * lane),
+                                         (__attribute__((address_space(3))) void*)(&xs[hl][st * 512]), 16, 0, 0);
       }
-#pragma unroll
-      for (int p = 0; p <= QB / 2; ++p)
-        scw[mt][p] = *reinterpret_cast<const uint32_t*>(sp + row * (d / 32) + min(a0 + 2 * p, d / 32 - 2));
-    }
-    PI_ISSUE_FENCE();
-    wait_vm_lds<0>();
-    __syncthreads();                                        // every wave's part of the chunk is in LDS
-    // every block of the half chunk is multiplied (blocks past a short last
-    // chunk read clamped weights and LDS steps inside xs, and are dropped by a
-    // select): a branch around the use would sink the loads into it, one HBM
-    // round trip per block
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const bool valid = 32 * qb < kwn;
-      const int st0 = (kw - kc) / 16 + 2 * min(qb, kwn / 32 - 1);   // K step within the chunk
+      const int kw = kc + kp * (kcn / 2), kwn = kcn / 2;        // this wave's half
+      constexpr int QB = KH / 32;
+      // the row's nibbles for the half chunk (one 16-byte block per load) and its block
+      // scales two at a time: aligned words from the even block a0 = kw / 32 rounded
+      // down (d / 32 is even, so a word lies wholly inside the row or wholly past it,
+      // then clamped to the row's last word and not used); block kw / 32 + qb is
+      // half (o + qb) & 1 of word (o + qb) / 2, o = kw / 32 - a0
+      const int a0 = (kw / 32) & ~1, o = (kw / 32) & 1;
+      uint4 cq[NMAT][QB];
+      uint32_t scw[NMAT][QB / 2 + 1];
 #pragma unroll
       for (int mt = 0; mt < NMAT; ++mt) {
-        f16v p = {};
+        const void* wp = (NMAT == 2 && mt == 0) ? gate_w : up_w;
+        const uint16_t* sp = (NMAT == 2 && mt == 0) ? gate_sc : up_sc;
 #pragma unroll
-        for (int stp = 0; stp < 2; ++stp) {
-          const h8v bw = q4_h8(cq[mt][qb], 8 * half, stp == 1);
-          const h8v ah = *reinterpret_cast<const h8v*>(&xs[0][(st0 + stp) * 512 + 8 * lane]);
-          const h8v al = *reinterpret_cast<const h8v*>(&xs[1][(st0 + stp) * 512 + 8 * lane]);
-          p = mfma(ah, bw, p);
-          p = mfma(al, bw, p);
+        for (int qb = 0; qb < QB; ++qb) {
+          const int kb = kw + 32 * min(qb, kwn / 32 - 1);
+          cq[mt][qb] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(wp) + row * (d / 2) + kb / 2);
         }
-        const uint32_t wd = o ? scw[mt][(qb + 1) / 2] : scw[mt][qb / 2];
-        const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> (16 * ((o + qb) & 1))));
 #pragma unroll
-        for (int x = 0; x < 16; ++x) acc[mt][x] = valid ? fmaf(sc, p[x], acc[mt][x]) : acc[mt][x];
+        for (int p = 0; p <= QB / 2; ++p)
+          scw[mt][p] = *reinterpret_cast<const uint32_t*>(sp + row * (d / 32) + min(a0 + 2 * p, d / 32 - 2));
+      }
+      PI_ISSUE_FENCE();
+      wait_vm_lds<0>();
+      __syncthreads();                                        // every wave's part of the chunk is in LDS
+      // every block of the half chunk is multiplied (blocks past a short last
+      // chunk read clamped weights and LDS steps inside xs, and are dropped by a
+      // select): a branch around the use would sink the loads into it, one HBM
+      // round trip per block
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const bool valid = 32 * qb < kwn;
+        const int st0 = (kw - kc) / 16 + 2 * min(qb, kwn / 32 - 1);   // K step within the chunk
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt) {
+          f16v p = {};
+#pragma unroll
+          for (int stp = 0; stp < 2; ++stp) {
+            const h8v bw = q4_h8(cq[mt][qb], 8 * half, stp == 1);
+            const h8v ah = *reinterpret_cast<const h8v*>(&xs[0][(st0 + stp) * 512 + 8 * lane]);
+            const h8v al = *reinterpret_cast<const h8v*>(&xs[1][(st0 + stp) * 512 + 8 * lane]);
+            p = mfma(ah, bw, p);
+            p = mfma(al, bw, p);
+          }
+          const uint32_t wd = o ? scw[mt][(qb + 1) / 2] : scw[mt][qb / 2];
+          const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> (16 * ((o + qb) & 1))));
+#pragma unroll
+          for (int x = 0; x < 16; ++x) acc[mt][x] = valid ? fmaf(sc, p[x], acc[mt][x]) : acc[mt][x];
+        }
       }
     }
-  }
-  __syncthreads();                                            // the last chunk is consumed: reuse its LDS
+    __syncthreads();                                            // the last chunk is consumed: reuse its LDS
 #pragma unroll
-  for (int mt = 0; mt < NMAT; ++mt)
+    for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4)
+      for (int g4 = 0; g4 < 4; ++g4)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[((size_t)w * NMAT + mt) * BM * BM + (8 * g4 + 4 * half + v) * BM + col] = acc[mt][4 * g4 + v];
-  __syncthreads();
-  // the two halves of each tile, in order, to z_part[s][mt][position][b]
-  const size_t fpad = (size_t)(f + BM - 1) / BM * BM;
-  for (int e = tid; e < BU_TPB * NMAT * BM * BM; e += blockDim.x) {
-    const int b = e % BM, c = (e / BM) % BM, mt = (e / (BM * BM)) % NMAT, t = e / (NMAT * BM * BM);
-    const int p = t0 + t * BM + c;
-    if (p >= n) continue;
-    const float v = red[((size_t)t * NMAT + mt) * BM * BM + b * BM + c] +
-                    red[((size_t)(t + BU_TPB) * NMAT + mt) * BM * BM + b * BM + c];
-    z_part[(((size_t)s * NMAT + mt) * fpad + p) * BM + b] = v;
+        for (int v = 0; v < 4; ++v) red[((size_t)w * NMAT + mt) * BM * BM + (8 * g4 + 4 * half + v) * BM + col] = acc[mt][4 * g4 + v];
+    __syncthreads();
+    // the two halves of each tile, in order, to z_part[s][mt][position][b]
+    const size_t fpad = (size_t)(f + BM - 1) / BM * BM;
+    for (int e = tid; e < BU_TPB * NMAT * BM * BM; e += blockDim.x) {
+      const int b = e % BM, c = (e / BM) % BM, mt = (e / (BM * BM)) % NMAT, t = e / (NMAT * BM * BM);
+      const int p = t0 + t * BM + c;
+      if (p >= n) continue;
+      const float v = red[((size_t)t * NMAT + mt) * BM * BM + b * BM + c] +
+                      red[((size_t)(t + BU_TPB) * NMAT + mt) * BM * BM + b * BM + c];
+      z_part[(((size_t)s * NMAT + mt) * fpad + p) * BM + b] = v;
+    }
+    __syncthreads();                                            // red is the next item's chunk buffer
   }
 }
 
-// h from the K splits of z: position j of the union list (8 per block), row b
+// h from the K splits of z: position j of the union list (8 per block step), row b
 // (b fastest): z = (sum of the KS partials in split order) / sx[b]; h = m ? act(z
 // + bias) : 0, written in fp32 to h32 in operand order; hmax[b] collects the
 // largest |h[b]|.
@@ -765,27 +728,36 @@ k_bup_epi(const float* __restrict__ z_part, int KS, int f, const int32_t* __rest
   constexpr int NMAT = act_nmat<ACT>();
   __shared__ uint32_t rmax[BM];
   const int tid = threadIdx.x, b = tid % BM;
-  const int j = blockIdx.x * (256 / BM) + tid / BM;
   bool dense;
   const int n = ffn_rows(ucount, f, dense_min, &dense);
-  if ((int)blockIdx.x * (256 / BM) >= n) return;              // block-uniform
   if (tid < BM) rmax[tid] = 0u;
   __syncthreads();
-  if (j < n) {
-    const size_t fpad = (size_t)(f + BM - 1) / BM * BM;
-    const int rw = dense ? j : ulist[j];
-    const float ix = 1.f / sx[b];
-    float z[NMAT];
+  const size_t fpad = (size_t)(f + BM - 1) / BM * BM;
+  const float ix = 1.f / sx[b];
+  // positions 8 q .. 8 q + 7 for q = blockIdx.x, blockIdx.x + gridDim.x, ...; all
+  // BU_KSMAX partials of a value loaded before the first add (splits past KS read
+  // split 0 and are dropped)
+  for (int q = blockIdx.x; q * (256 / BM) < n; q += gridDim.x) {
+    const int j = q * (256 / BM) + tid / BM;
+    if (j < n) {
+      const int rw = dense ? j : ulist[j];
+      float z[NMAT];
 #pragma unroll
-    for (int mt = 0; mt < NMAT; ++mt) {
-      float a = z_part[((size_t)mt * fpad + j) * BM + b];
-      for (int s2 = 1; s2 < KS; ++s2) a += z_part[(((size_t)s2 * NMAT + mt) * fpad + j) * BM + b];
-      z[mt] = a * ix;
+      for (int mt = 0; mt < NMAT; ++mt) {
+        float pz[BU_KSMAX];
+#pragma unroll
+        for (int s2 = 0; s2 < BU_KSMAX; ++s2)
+          pz[s2] = z_part[(((size_t)(s2 < KS ? s2 : 0) * NMAT + mt) * fpad + j) * BM + b];
+        float a = pz[0];
+#pragma unroll
+        for (int s2 = 1; s2 < BU_KSMAX; ++s2) a += s2 < KS ? pz[s2] : 0.f;
+        z[mt] = a * ix;
+      }
+      float h = act_h<ACT>(z[0], bias[rw], z[NMAT - 1]);
+      if (m_nm[(size_t)rw * BM + b] == 0) h = 0.f;
+      h32[aop(b, j)] = h;
+      atomicMax(&rmax[b], __float_as_uint(fabsf(h)));          // LDS atomic
     }
-    float h = act_h<ACT>(z[0], bias[rw], z[NMAT - 1]);
-    if (m_nm[(size_t)rw * BM + b] == 0) h = 0.f;
-    h32[aop(b, j)] = h;
-    atomicMax(&rmax[b], __float_as_uint(fabsf(h)));          // LDS atomic
   }
   __syncthreads();
   if (tid < BM && rmax[tid] != 0u) atomicMax(&hmax[tid], rmax[tid]);
