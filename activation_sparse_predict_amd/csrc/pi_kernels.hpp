@@ -931,7 +931,8 @@ k_up_list(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc,
 // Each wave copies its share of the (neuron, h) entries into LDS -- in the
 // stack, the per-block lists of the score kernel (wave s of S = 8*NC takes
 // the lists of score blocks s, s + S, ...; a wave prefix sum of their counts
-// places them); for pi_sparse_ffn, the caller's list with its h values
+// places them; their first entries are read together with the counts, and
+// only a list longer than that is read again after them); for pi_sparse_ffn, the caller's list with its h values
 // (entries s, s + S, ... with h != 0) -- then gathers the tile's segments of
 // those rows, RPW = 64 / TWC rows per wave-wide load and K3_LOADS loads per
 // HBM round trip, accumulating in fp32 in list order.  The lanes of one chunk
@@ -968,6 +969,7 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
   __shared__ __attribute__((aligned(16))) int l_id[K3_WAVES][K3_CAP];
   __shared__ float l_h[K3_WAVES][K3_CAP];
   __shared__ int l_pre[K3_WAVES][K3_MAXLISTS];
+  __shared__ int l_cnt[K3_WAVES][K3_MAXLISTS];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int nblk = CT * NC;
   int L = blockIdx.x;
@@ -1026,47 +1028,79 @@ k_down(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int
   };
 
   if constexpr (!EXPLICIT) {
-    // the counts of this wave's score-block lists (block s + S i in lane i),
-    // their exclusive prefix sums in LDS, and the wave's total
+    // the counts of this wave's score-block lists (block s + S i in lane i), and --
+    // in the same round trip, before the counts are known -- the first `spec`
+    // entries of every list (slot k of the 256 read ahead is entry k % spec of list
+    // k / spec; spec is a power of two, at most the list capacity)
     const int nlw = n_cnt_blk > s ? (n_cnt_blk - 1 - s) / S + 1 : 0;     // <= K3_MAXLISTS
+    int lg = 8;                                                          // log2(spec)
+    while (lg > 0 && ((1 << lg) * nlw > 4 * WAVE || (1 << lg) > cap)) --lg;
     const int cl = lane < nlw ? cnt_blk[n_cnt_blk + s + S * lane] : 0;
+    int sid[4];
+    float sh[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int slot = k * WAVE + lane, li = slot >> lg, e = slot & ((1 << lg) - 1);
+      const size_t at = li < nlw ? (size_t)(s + S * li) * cap + e : 0;   // a valid entry either way
+      sid[k] = pair_id[at];
+      sh[k] = pair_h[at];
+    }
+    PI_ISSUE_FENCE();
     const int incl = wave_scan(cl);
     l_pre[w][lane] = incl - cl;
+    l_cnt[w][lane] = cl;
     const int ntot = lane_i(incl, WAVE - 1);
-    // entries e0 .. e0 + K3_CAP at a time; entry e is in the list i whose
-    // prefix bounds it (a search over the nlw prefixes), at offset e - pre[i]
-    for (int e0 = 0; e0 < ntot; e0 += K3_CAP) {
-      const int ne = min(K3_CAP, ntot - e0);
-      for (int k0 = 0; k0 < ne; k0 += 4 * WAVE) {
-        size_t slot[4];
+    // every entry read ahead (no list longer than spec) and the wave's list fits: place
+    // them; otherwise the general path below reads every entry again
+    const bool all_ahead = __ballot(cl > (1 << lg)) == 0 && ntot <= K3_CAP;
+    if (all_ahead) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int e = e0 + min(k0 + k * WAVE + lane, ne - 1);
-          int lo = 0;
-#pragma unroll
-          for (int step = K3_MAXLISTS / 2; step >= 1; step >>= 1)
-            if (lo + step < nlw && l_pre[w][min(lo + step, K3_MAXLISTS - 1)] <= e) lo += step;
-          slot[k] = (size_t)(s + S * lo) * cap + (e - l_pre[w][lo]);
-        }
-        int id4[4];
-        float h4[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          id4[k] = pair_id[slot[k]];
-          h4[k] = pair_h[slot[k]];
-        }
-        PI_ISSUE_FENCE();
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int e = k0 + k * WAVE + lane;
-          if (e < ne) {
-            l_id[w][e] = id4[k];
-            l_h[w][e] = h4[k];
-          }
+      for (int k = 0; k < 4; ++k) {
+        const int slot = k * WAVE + lane, li = slot >> lg, e = slot & ((1 << lg) - 1);
+        const int lic = min(li, K3_MAXLISTS - 1);
+        if (li < nlw && e < l_cnt[w][lic]) {
+          l_id[w][l_pre[w][lic] + e] = sid[k];
+          l_h[w][l_pre[w][lic] + e] = sh[k];
         }
       }
-      n = ne;
+      n = ntot;
       flush();
+    } else {
+      // entries e0 .. e0 + K3_CAP at a time; entry e is in the list i whose
+      // prefix bounds it (a search over the nlw prefixes), at offset e - pre[i]
+      for (int e0 = 0; e0 < ntot; e0 += K3_CAP) {
+        const int ne = min(K3_CAP, ntot - e0);
+        for (int k0 = 0; k0 < ne; k0 += 4 * WAVE) {
+          size_t slot[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int e = e0 + min(k0 + k * WAVE + lane, ne - 1);
+            int lo = 0;
+#pragma unroll
+            for (int step = K3_MAXLISTS / 2; step >= 1; step >>= 1)
+              if (lo + step < nlw && l_pre[w][min(lo + step, K3_MAXLISTS - 1)] <= e) lo += step;
+            slot[k] = (size_t)(s + S * lo) * cap + (e - l_pre[w][lo]);
+          }
+          int id4[4];
+          float h4[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            id4[k] = pair_id[slot[k]];
+            h4[k] = pair_h[slot[k]];
+          }
+          PI_ISSUE_FENCE();
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int e = k0 + k * WAVE + lane;
+            if (e < ne) {
+              l_id[w][e] = id4[k];
+              l_h[w][e] = h4[k];
+            }
+          }
+        }
+        n = ne;
+        flush();
+      }
     }
   } else {
     const int cnt = min(max(*count, 0), f);
