@@ -435,6 +435,29 @@ def test_stack_hot_prefix(name, hot):
     check_list(mask.astype(bool), idx, count)
 
 
+def test_stack_long_score_lists():
+    """Every neuron on (hot prefix over the whole ffn, biases that keep every h
+    nonzero) at a shape whose score-block lists (64 entries each) are longer than
+    what the down projection reads ahead with the counts (32 per list): the
+    lists are read again after the counts, and each layer's y is still the
+    oracle's on the GPU's own input and mask."""
+    cfg = workload.CONFIGS[2].with_(d=512, ffn=32768, rank=64, n_layers=2)
+    say(f"[long_lists] d {cfg.d} ffn {cfg.ffn}")
+    host = [workload.make_layer(cfg, l) for l in range(cfg.n_layers)]
+    for h in host:
+        h.hot = cfg.ffn
+        h.bias = np.full_like(h.bias, 4.0)
+    layers = [pi.DeviceLayer.upload(h, DEV) for h in host]
+    x = workload.make_x(cfg, 5)
+    out, trace = run_stack_traced(layers, x[0], cfg)
+    for t in trace:
+        assert t["count"] == cfg.ffn
+    st = replay_stack(host, trace, out, x, cfg.w_dtype, cfg.act)
+    say(f"  {st}")
+    del layers
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.timeout(600)
 def test_full_size_stack_hot_prefix():
     """The OPT-175B-shaped Q4_0 stack with the byte model's hot prefix (hot_count)."""
