@@ -537,14 +537,20 @@ void b_predict(const pi_layer* L, int batch, const Ws& W, float* scores, uint8_t
   hipLaunchKernelGGL(pib::k_bsplit_t, dim3(kBatchM), dim3(pib::BT_T), 0, st, W.tpart, ks, L->rank, W.sx, W.th, W.tl,
                      W.st);
   mark(tr, 3, st);
-  const dim3 g2(cdiv(L->ffn, pib::BS_T * pib::BM));
+  // four 32-neuron tiles per block (t read once per 128 neurons) while that leaves
+  // about a block per compute unit, else one
   const float* pb = L->pbias ? L->pbias : L->bias;
-  if (L->p_dtype == PI_F16)
-    hipLaunchKernelGGL(pib::k_bscore<DT_F16>, g2, dim3(256), 0, st, L->B, pb, L->ffn, L->rank, batch, W.th, W.tl,
-                       W.st, W.mnm, W.mask, W.cnt, scores, mask_out, L->hot);
-  else
-    hipLaunchKernelGGL(pib::k_bscore<DT_F32>, g2, dim3(256), 0, st, L->B, pb, L->ffn, L->rank, batch, W.th, W.tl,
-                       W.st, W.mnm, W.mask, W.cnt, scores, mask_out, L->hot);
+  const bool t4 = cdiv(L->ffn, 4 * kBatchM) >= 192;
+  const dim3 g2(cdiv(L->ffn, (t4 ? 4 : 1) * kBatchM));
+#define PI_BSCORE(PT, NT)                                                                                      \
+  hipLaunchKernelGGL((pib::k_bscore<PT, NT>), g2, dim3(256), 0, st, L->B, pb, L->ffn, L->rank, batch, W.th, W.tl, \
+                     W.st, W.mnm, W.mask, W.cnt, scores, mask_out, L->hot)
+  if (L->p_dtype == PI_F16) {
+    if (t4) PI_BSCORE(DT_F16, 4); else PI_BSCORE(DT_F16, 1);
+  } else {
+    if (t4) PI_BSCORE(DT_F32, 4); else PI_BSCORE(DT_F32, 1);
+  }
+#undef PI_BSCORE
   mark(tr, 4, st);
   // the union list from the score kernel's union bytes and per-tile counts (multi-block, no atomics)
   hipLaunchKernelGGL(pib::k_bcompact, dim3(cdiv(bscore_blocks(L->ffn), 256)), dim3(256), 0, st, W.mask, W.cnt,

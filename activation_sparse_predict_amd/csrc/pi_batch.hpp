@@ -359,15 +359,15 @@ k_bsplit_t(const float* __restrict__ t_part, int ksplit, int r, const float* __r
 // in every sequence without a score: a block wholly inside the prefix reads no
 // row of B, and no score of the prefix is written.
 constexpr int BS_W = 4;                  // waves (K split)
-constexpr int BS_T = 4;                  // 32-neuron tiles per block
 
-template <int PT>
+// BS_T tiles per block: 4 when that still gives about one block per compute unit, else 1
+template <int PT, int BS_T>
 __global__ void __launch_bounds__(BS_W * WAVE) __attribute__((amdgpu_waves_per_eu(2)))
 k_bscore(const void* __restrict__ Bm, const float* __restrict__ pbias, int f, int r, int batch,
          const _Float16* __restrict__ th, const _Float16* __restrict__ tl, const float* __restrict__ st,
          uint8_t* __restrict__ m_nm, uint8_t* __restrict__ u, int32_t* __restrict__ cnt_blk,
          float* __restrict__ scores, uint8_t* __restrict__ mask_out, int hot) {
-  constexpr int KS_U = PT == DT_F32 ? 2 : 4;         // K steps per batch of loads
+  constexpr int KS_U = (PT == DT_F32 ? 4 : 8) / (BS_T > 1 ? 2 : 1);   // K steps per batch of loads
   constexpr int WV = PT == DT_F32 ? 2 : 1;           // 16-byte pieces per 8 weights
   __shared__ float red[BS_W][BS_T][BM * BM];
   __shared__ uint32_t onr[BS_T][BS_W * WAVE];

@@ -110,7 +110,7 @@ def test_summarize_traffic(tmp_path):
 
 def test_hot_prefix_bytes():
     """A hot-dense prefix drops its rows of B and predictor biases from the score
-    kernel's bytes (batch 1: every prefix slot; batch > 1: whole 128-neuron blocks)."""
+    kernel's bytes (batch 1: every prefix slot; batch > 1: whole blocks of 128 or 32 neurons)."""
     cfg = workload.CONFIGS[4]
     pb = 2
     a, b = bench.kernel_bytes(cfg, 1, 4000, 3900), bench.kernel_bytes(cfg, 1, 4000, 3900, hot=1109)
@@ -120,4 +120,8 @@ def test_hot_prefix_bytes():
     assert a["k_bscore"] == b["k_bscore"]
     a, b = bench.kernel_bytes(cfg, 32, 5000), bench.kernel_bytes(cfg, 32, 5000, hot=300)
     assert a["k_bscore"] - b["k_bscore"] == 256 * (cfg.rank * pb + 4)
+    # a narrow ffn runs one 32-neuron tile per block
+    c1 = workload.CONFIGS[1]
+    a, b = bench.kernel_bytes(c1, 32, 5000), bench.kernel_bytes(c1, 32, 5000, hot=77)
+    assert a["k_bscore"] - b["k_bscore"] == 64 * (c1.rank * bench.sizes(c1)[0] + 4)
 
