@@ -499,7 +499,15 @@ int bksplit(int r) { return std::max(1, std::min(kMaxKSplit, cdiv(256, cdiv(r, k
 // y_prev is NULL) to x_out / x_trace and as fp16 hi/lo operands.
 void b_glue(const float* x_prev, const float* y_prev, int batch, int d, float* x_out, float* x_trace, const Ws& W,
             hipStream_t st) {
-  hipLaunchKernelGGL(pib::k_bglue, dim3(kBatchM), dim3(pib::BG_T), 0, st, x_prev, y_prev,
+  const int bgv = d <= 4096 ? 1 : d <= 8192 ? 2 : 4;
+  if (bgv == 1)
+    hipLaunchKernelGGL(pib::k_bglue<1>, dim3(kBatchM), dim3(pib::BG_T), 0, st, x_prev, y_prev,
+                     y_prev ? pib::bd_splits(d) : 0, batch, d, x_out, x_trace, W.xh, W.xl, W.sx, W.hmax);
+  else if (bgv == 2)
+    hipLaunchKernelGGL(pib::k_bglue<2>, dim3(kBatchM), dim3(pib::BG_T), 0, st, x_prev, y_prev,
+                     y_prev ? pib::bd_splits(d) : 0, batch, d, x_out, x_trace, W.xh, W.xl, W.sx, W.hmax);
+  else
+    hipLaunchKernelGGL(pib::k_bglue<4>, dim3(kBatchM), dim3(pib::BG_T), 0, st, x_prev, y_prev,
                      y_prev ? pib::bd_splits(d) : 0, batch, d, x_out, x_trace, W.xh, W.xl, W.sx, W.hmax);
 }
 
@@ -676,7 +684,7 @@ pi_status run_stack(const pi_layer* layers, int32_t n_layers, const float* x, in
                            tr->y);
     }
     const int last = (n_layers - 1) & 1;
-    hipLaunchKernelGGL(pib::k_bglue_out, dim3(batch), dim3(256), sizeof(float) * D.d, st, W.x[last], W.y[last],
+    hipLaunchKernelGGL(pib::k_bglue_out, dim3(batch), dim3(pib::BG_T), 0, st, W.x[last], W.y[last],
                        pib::bd_splits(D.d), D.d, out);
     return launch_status();
   }

@@ -100,8 +100,10 @@ __device__ __forceinline__ h8v q4_h8(uint4 c, int b0, bool hi_nib) {
 // so that they contribute nothing to any product.  Block b also clears the
 // row maximum hmax[b] of the layer's h.
 constexpr int BG_T = 1024;               // threads of a glue block
-constexpr int BG_V = 4;                  // float4 per thread held at once (d <= 16384)
-
+// BG_V float4 per thread held at once (d <= 4096 BG_V); the partial vectors are
+// read 16 / BG_V at a time, so at the usual widths all of them are in flight
+// together with x (bd_splits(d) <= 16 / BG_V + 1)
+template <int BG_V>
 __global__ void __launch_bounds__(BG_T)
 k_bglue(const float* __restrict__ x_prev, const float* __restrict__ y_part, int np, int B, int d,
         float* __restrict__ x_out, float* __restrict__ x_trace, _Float16* __restrict__ xh,
@@ -131,9 +133,9 @@ k_bglue(const float* __restrict__ x_prev, const float* __restrict__ y_part, int 
 #pragma unroll
     for (int j = 0; j < BG_V; ++j)
       y[j] = reinterpret_cast<const float4*>(y_part + (size_t)b * d)[min(tid + BG_T * j, nv - 1)];
-    // the other partials, four at a time: all their loads before the first add,
+    // the other partials, GP at a time: all their loads before the first add,
     // added in partial order (partials past np are read clamped and dropped)
-    constexpr int GP = 4;
+    constexpr int GP = 16 / BG_V;
     for (int p0 = 1; p0 < np; p0 += GP) {
       float4 u[GP][BG_V];
 #pragma unroll
@@ -1094,25 +1096,38 @@ __global__ void k_blist(const int32_t* __restrict__ idx, const int32_t* __restri
 }
 
 // out[b] = glue(x[b], sum of the np partials y[p][b]) for b < batch (one
-// block per sequence); partial p of row b is at y_part + (p * 32 + b) * d
-__global__ void __launch_bounds__(256)
+// 1024-thread block per sequence, d <= 16384); partial p of row b is at
+// y_part + (p * 32 + b) * d.  Each thread's values and all their partials
+// (np <= BD_MAXSPLIT) are loaded before the first add; out needs no alignment.
+__global__ void __launch_bounds__(BG_T)
 k_bglue_out(const float* __restrict__ x, const float* __restrict__ y_part, int np, int d, float* __restrict__ out) {
-  extern __shared__ float vs[];
-  __shared__ float red[4];
+  constexpr int NJ = 16;                   // values per thread (d <= 16384)
+  __shared__ float red[BG_T / WAVE];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  float v[NJ];
   float ss = 0.f;
-  for (int k = tid; k < d; k += blockDim.x) {
-    float yv = y_part[(size_t)b * d + k];
-    for (int p = 1; p < np; ++p) yv += y_part[((size_t)p * BM + b) * d + k];
-    const float v = x[(size_t)b * d + k] + yv;
-    vs[k] = v;
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int k = min(tid + BG_T * j, d - 1);
+    float yp[BD_MAXSPLIT];
+#pragma unroll
+    for (int p = 0; p < BD_MAXSPLIT; ++p) yp[p] = y_part[((size_t)min(p, np - 1) * BM + b) * d + k];
+    float yv = yp[0];
+#pragma unroll
+    for (int p = 1; p < BD_MAXSPLIT; ++p) yv += p < np ? yp[p] : 0.f;
+    v[j] = x[(size_t)b * d + k] + yv;
+    if (tid + BG_T * j < d) ss = fmaf(v[j], v[j], ss);
   }
   ss = wave_sum(ss);
   if (lane == 0) red[w] = ss;
   __syncthreads();
-  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + 1e-6f);
-  for (int k = tid; k < d; k += blockDim.x) out[(size_t)b * d + k] = vs[k] * inv;
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < BG_T / WAVE; ++i) tot += red[i];
+  const float inv = 1.0f / sqrtf(tot / (float)d + 1e-6f);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    if (tid + BG_T * j < d) out[(size_t)b * d + tid + BG_T * j] = v[j] * inv;
 }
 
 }  // namespace pib
