@@ -545,19 +545,32 @@ void b_predict(const pi_layer* L, int batch, const Ws& W, float* scores, uint8_t
   hipLaunchKernelGGL(pib::k_bsplit_t, dim3(kBatchM), dim3(pib::BT_T), 0, st, W.tpart, ks, L->rank, W.sx, W.th, W.tl,
                      W.st);
   mark(tr, 3, st);
-  // four 32-neuron tiles per block (t read once per 128 neurons) while that leaves
-  // about a block per compute unit, else one
+  // T 32-neuron tiles per block (t read once per 32 T neurons): the T of 4, 3, 2, 1
+  // whose blocks spread most evenly over the compute units, the larger on a tie
+  // (the time is about rounds of 256 blocks times T)
   const float* pb = L->pbias ? L->pbias : L->bias;
-  const bool t4 = cdiv(L->ffn, 4 * kBatchM) >= 192;
-  const dim3 g2(cdiv(L->ffn, (t4 ? 4 : 1) * kBatchM));
+  int nt = 4, best = 1 << 30;
+  for (int t : {4, 3, 2, 1}) {
+    const int cost = cdiv(cdiv(L->ffn, t * kBatchM), 256) * t;
+    if (cost < best) { best = cost; nt = t; }
+  }
+  const dim3 g2(cdiv(L->ffn, nt * kBatchM));
 #define PI_BSCORE(PT, NT)                                                                                      \
   hipLaunchKernelGGL((pib::k_bscore<PT, NT>), g2, dim3(256), 0, st, L->B, pb, L->ffn, L->rank, batch, W.th, W.tl, \
                      W.st, W.mnm, W.mask, W.cnt, scores, mask_out, L->hot)
-  if (L->p_dtype == PI_F16) {
-    if (t4) PI_BSCORE(DT_F16, 4); else PI_BSCORE(DT_F16, 1);
-  } else {
-    if (t4) PI_BSCORE(DT_F32, 4); else PI_BSCORE(DT_F32, 1);
+#define PI_BSCORE_T(PT)                                                                                         \
+  switch (nt) {                                                                                                 \
+    case 4: PI_BSCORE(PT, 4); break;                                                                            \
+    case 3: PI_BSCORE(PT, 3); break;                                                                            \
+    case 2: PI_BSCORE(PT, 2); break;                                                                            \
+    default: PI_BSCORE(PT, 1); break;                                                                           \
   }
+  if (L->p_dtype == PI_F16) {
+    PI_BSCORE_T(DT_F16)
+  } else {
+    PI_BSCORE_T(DT_F32)
+  }
+#undef PI_BSCORE_T
 #undef PI_BSCORE
   mark(tr, 4, st);
   // the union list from the score kernel's union bytes and per-tile counts (multi-block, no atomics)

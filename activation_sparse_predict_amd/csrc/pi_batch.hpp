@@ -362,7 +362,7 @@ k_bsplit_t(const float* __restrict__ t_part, int ksplit, int r, const float* __r
 // row of B, and no score of the prefix is written.
 constexpr int BS_W = 4;                  // waves (K split)
 
-// BS_T tiles per block: 4 when that still gives about one block per compute unit, else 1
+// BS_T (1..4) tiles per block, chosen by the host for an even spread over the compute units
 template <int PT, int BS_T>
 __global__ void __launch_bounds__(BS_W * WAVE) __attribute__((amdgpu_waves_per_eu(2)))
 k_bscore(const void* __restrict__ Bm, const float* __restrict__ pbias, int f, int r, int batch,
@@ -370,6 +370,7 @@ k_bscore(const void* __restrict__ Bm, const float* __restrict__ pbias, int f, in
          uint8_t* __restrict__ m_nm, uint8_t* __restrict__ u, int32_t* __restrict__ cnt_blk,
          float* __restrict__ scores, uint8_t* __restrict__ mask_out, int hot) {
   constexpr int KS_U = (PT == DT_F32 ? 4 : 8) / (BS_T > 1 ? 2 : 1);   // K steps per batch of loads
+  static_assert(BS_T >= 1 && BS_T <= 4, "tiles per block");
   constexpr int WV = PT == DT_F32 ? 2 : 1;           // 16-byte pieces per 8 weights
   __shared__ float red[BS_W][BS_T][BM * BM];
   __shared__ uint32_t onr[BS_T][BS_W * WAVE];

@@ -128,8 +128,8 @@ def kernel_bytes(cfg, batch, k, k_nz=None, hot=0):
     (r*d + f*r)*pb + 4f + k*((n_mat-1)*d*wb + 4) + k_nz*(d*wb + 4) + 8*d*B.
     With a hot-dense prefix of `hot` slots, only the tail's rows of B and
     predictor biases are read (f - hot rows at batch 1; at batch > 1 the
-    score kernel's blocks -- 128 neurons, or 32 when fewer than 192 blocks of
-    128 would exist -- not wholly inside the prefix), and k includes the prefix.
+    score kernel's blocks of 32 * bscore_tiles(f) neurons not wholly inside the
+    prefix), and k includes the prefix.
     """
     pb, wb, n_mat = sizes(cfg)
     d, f, r = cfg.d, cfg.ffn, cfg.rank
@@ -141,11 +141,23 @@ def kernel_bytes(cfg, batch, k, k_nz=None, hot=0):
         return {"k_predict_t": r * d * pb + 8 * d,
                 "k_score": fp * r * pb + 4 * fp + k * (n_up * d * wb + 4),
                 "k_down": k_nz * d * wb + 4 * k_nz}
-    blk = 128 if -(-f // 128) >= 192 else 32        # neurons per block of the batched score kernel
+    blk = 32 * bscore_tiles(f)                       # neurons per block of the batched score kernel
     fp = f - blk * (hot // blk)
     return {"k_bglue": 8 * d * batch, "k_bpred1": r * d * pb, "k_bsplit_t": 0,
             "k_bscore": fp * r * pb + 4 * fp, "k_compact": 0,
             "k_bup": k * (n_up * d * wb + 4), "k_bdown": k * d * wb + 4 * k}
+
+
+def bscore_tiles(f):
+    """32-neuron tiles per block of the batched score kernel: of 4, 3, 2, 1 the one
+    with the fewest rounds of 256 blocks times tiles, the larger on a tie (the
+    library's launch rule)."""
+    best, nt = None, 4
+    for t in (4, 3, 2, 1):
+        cost = -(-(-(-f // (32 * t))) // 256) * t
+        if best is None or cost < best:
+            best, nt = cost, t
+    return nt
 
 
 def layer_bytes(cfg, k, batch=1, k_nz=None, hot=0):

@@ -119,9 +119,11 @@ def test_hot_prefix_bytes():
     a, b = bench.kernel_bytes(cfg, 32, 5000), bench.kernel_bytes(cfg, 32, 5000, hot=77)
     assert a["k_bscore"] == b["k_bscore"]
     a, b = bench.kernel_bytes(cfg, 32, 5000), bench.kernel_bytes(cfg, 32, 5000, hot=300)
-    assert a["k_bscore"] - b["k_bscore"] == 256 * (cfg.rank * pb + 4)
-    # a narrow ffn runs one 32-neuron tile per block
+    assert bench.bscore_tiles(cfg.ffn) == 3                  # 512 blocks of 96 neurons
+    assert a["k_bscore"] - b["k_bscore"] == 288 * (cfg.rank * pb + 4)
+    # narrower ffns: blocks of 64 neurons (172 blocks) and of 128 (256 blocks)
     c1 = workload.CONFIGS[1]
+    assert bench.bscore_tiles(c1.ffn) == 2 and bench.bscore_tiles(workload.CONFIGS[3].ffn) == 4
     a, b = bench.kernel_bytes(c1, 32, 5000), bench.kernel_bytes(c1, 32, 5000, hot=77)
     assert a["k_bscore"] - b["k_bscore"] == 64 * (c1.rank * bench.sizes(c1)[0] + 4)
 
