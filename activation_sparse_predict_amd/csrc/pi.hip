@@ -590,7 +590,7 @@ template <int WT, int ACT>
 void b_ffn_t(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, const int32_t* ucount, float* y,
              hipStream_t st, const pi_trace* tr) {
   if constexpr (WT != DT_Q4) {
-    hipLaunchKernelGGL((pib::k_bup<WT, ACT>), dim3(std::min(cdiv(L->ffn, kBatchM), kUpGrid)), dim3(pib::BUP_W * WAVE),
+    hipLaunchKernelGGL((pib::k_bup<WT, ACT>), dim3(std::min(cdiv(L->ffn, kBatchM), kUpGrid)), dim3(pib::bup_waves(act_nmat<ACT>()) * WAVE),
                        0, st,
                        L->gate.w, L->gate.scale, L->up.w, L->up.scale, L->bias, L->ffn, L->d, W.xh, W.xl, ulist,
                        ucount, W.mnm, W.sx, W.h32, W.hmax, dense_min(L));

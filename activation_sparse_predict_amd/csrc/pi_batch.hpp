@@ -510,14 +510,16 @@ __device__ __forceinline__ int ffn_rows(const int32_t* __restrict__ ucount, int 
 // ------------------------------------------------------------ up / gate
 // z = X W^T over the union rows (fp16 and fp32 weights).  A block takes tiles
 // q = blockIdx.x, blockIdx.x + gridDim.x, ... of 32 union list entries [32 q,
-// 32 q + 32) while they exist; its BUP_W waves split K
+// 32 q + 32) while they exist; its bup_waves(NMAT) waves split K
 // into contiguous ranges and their partial tiles are summed through LDS in
 // wave order.  Epilogue: z's row b times 1 / sx[b]; h[b] = m[i][b] ?
 // act(z + bias) : 0, written in fp32 to h32 as a [32][h_stride] operand-order
 // matrix (row b, column j = the neuron's position in the union list), in which
 // the down projection reads it as its A operand; hmax[b] collects the largest
 // |h[b]| (as the bits of a non-negative float, by atomic maximum).
-constexpr int BUP_W = 8;
+// waves per block: 8, or 4 for ReGLU (two z tiles per wave in the LDS sum, so that
+// four blocks fit on a compute unit; 66.1 -> 60.7 us at the LLaMA-2-7B shape, batch 32)
+__host__ __device__ constexpr int bup_waves(int nmat) { return nmat == 2 ? 4 : 8; }
 constexpr int BD_CH = 128;               // union positions per chunk of the down projection
 
 // K extent (halves) of the h operand: whole chunks, so that a chunk's
@@ -525,13 +527,14 @@ constexpr int BD_CH = 128;               // union positions per chunk of the dow
 __host__ __device__ constexpr int h_stride(int f) { return (f + BD_CH - 1) / BD_CH * BD_CH; }
 
 template <int WT, int ACT>
-__global__ void __launch_bounds__(BUP_W * WAVE)
+__global__ void __launch_bounds__(bup_waves(act_nmat<ACT>()) * WAVE)
 k_bup(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, const void* __restrict__ up_w,
       const uint16_t* __restrict__ up_sc, const float* __restrict__ bias, int f, int d,
       const _Float16* __restrict__ xh, const _Float16* __restrict__ xl, const int32_t* __restrict__ ulist,
       const int32_t* __restrict__ ucount, const uint8_t* __restrict__ m_nm, const float* __restrict__ sx,
       float* __restrict__ h32, uint32_t* __restrict__ hmax, int dense_min) {
   constexpr int NMAT = act_nmat<ACT>();
+  constexpr int BUP_W = bup_waves(NMAT);
   __shared__ float red[BUP_W][NMAT][BM * BM];
   __shared__ uint32_t rmax[BM];
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
