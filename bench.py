@@ -266,7 +266,7 @@ def summarize_counters(paths, kernels, trace_csv, title, commands, out):
             k = next((k for k in kernels if k in kn), None)
             if k is not None:
                 dur.setdefault(k, []).append(float(_col(r, "End_Timestamp")) - float(_col(r, "Start_Timestamp")))
-    L = [f"# Counters: {title}", "", "Commands (from the repository root on the GPU box):", "", "```"]
+    L = [f"# Counters: {title}", "", "Commands (from the repository root, on a machine with the GPU):", "", "```"]
     L += commands + ["```", "", "Summarized by `python bench.py --summarize-counters`: per-launch means.", ""]
     names = sorted({c for k in vals for c in vals[k]})
     L.append("| kernel | launches | " + " | ".join(names) + " | mean us | MFMA TFLOP/s (fp16) | of 2.5 PFLOP/s |")
@@ -309,7 +309,7 @@ def summarize_trace(path, title, commands, out):
                    _col(r, "Group_Segment_Size", "LDS_Block_Size", default="?"),
                    _col(r, "Private_Segment_Size", "Scratch_Size", default="?"))
     total = sum(sum(v) for v in agg.values())
-    L = [f"# Kernel trace: {title}", "", "Command (from the repository root on the GPU box):", "", "```"]
+    L = [f"# Kernel trace: {title}", "", "Command (from the repository root, on a machine with the GPU):", "", "```"]
     L += commands + ["```", "",
                      f"Summarized by `python bench.py --summarize-trace` from the trace CSV of that run "
                      f"({len(rows)} dispatches).  Durations are end minus start timestamps of each dispatch.", "",
