@@ -608,9 +608,14 @@ void b_ffn_t(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, co
                        L->ffn, ulist, ucount, dense_min(L), L->bias, W.mnm, W.sx, W.h32, W.hmax);
   }
   mark(tr, 6, st);
-  hipLaunchKernelGGL(pib::k_bdown<WT>, dim3(cdiv(L->d, pib::BD_COLS) * pib::bd_splits(L->d)), dim3(512), 0, st,
-                     L->downT.w, L->downT.scale, L->ffn, L->d, ulist, ucount, W.h32, W.hmax, L->b_down, batch, y,
-                     dense_min(L), pib::bd_splits(L->d));
+  if constexpr (WT == DT_Q4)
+    hipLaunchKernelGGL(pib::k_bdown_q4, dim3(cdiv(L->d, pib::BD_COLS) * pib::bd_splits(L->d)), dim3(512), 0, st,
+                       static_cast<const uint8_t*>(L->downT.w), L->downT.scale, L->ffn, L->d, ulist, ucount, W.h32,
+                       W.hmax, L->b_down, batch, y, dense_min(L), pib::bd_splits(L->d));
+  else
+    hipLaunchKernelGGL(pib::k_bdown<WT>, dim3(cdiv(L->d, pib::BD_COLS) * pib::bd_splits(L->d)), dim3(512), 0, st,
+                       L->downT.w, L->ffn, L->d, ulist, ucount, W.h32, W.hmax, L->b_down, batch, y, dense_min(L),
+                       pib::bd_splits(L->d));
   mark(tr, 7, st);
 }
 

@@ -844,14 +844,15 @@ k_bcompact(const uint8_t* __restrict__ u, const int32_t* __restrict__ tile_cnt, 
 // Per chunk the block stages, in LDS,
 //  - the A operands once for all eight tiles: h (read in its operand-order
 //    layout) times the row scale from hmax, split into fp16 hi/lo;
-//  - each tile's weights transposed to [column][position] as fp16 (fp32 and
-//    Q4_0 weights -- times their block scale -- as hi + lo pairs).
+//  - each tile's weights transposed to [column][position] as fp16 (fp32
+//    weights as hi + lo pairs).
 // Every thread converts four positions of eight columns in each of its two
 // items (adjacent tiles) and writes each column's values in pairs.  The next chunk's
 // weights and h, and the row ids of the chunk after it, are in flight while a
 // chunk is converted and multiplied.  Blocks that read a whole 128-byte line
 // (or several) of every row they gather, and h once per 256 columns instead
-// of once per 32 or 64.
+// of once per 32 or 64.  Q4_0 weights take k_bdown_q4 (same blocks, chunks and
+// results, more of them in flight).
 constexpr int BD_COLS = 256;             // columns per block (eight 32-column tiles, one per wave)
 constexpr int BD_PAD = BD_CH + 8;        // padded position stride (halves) of a transposed column
 constexpr int BD_MAXSPLIT = 16;          // most splits of the union list (partial y vectors)
@@ -865,11 +866,11 @@ __host__ __device__ constexpr int bd_splits(int d) {
 
 template <int WT>
 __global__ void __launch_bounds__(512)
-k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, int f, int d,
-        const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount, const float* __restrict__ h32,
-        const uint32_t* __restrict__ hmax, const float* __restrict__ b_down, int batch,
-        float* __restrict__ y_part, int dense_min, int nsplit) {
-  constexpr int NW = (WT == DT_F16) ? 1 : 2;       // weight operands: hi (and lo for fp32 and Q4_0)
+k_bdown(const void* __restrict__ downT, int f, int d, const int32_t* __restrict__ ulist,
+        const int32_t* __restrict__ ucount, const float* __restrict__ h32, const uint32_t* __restrict__ hmax,
+        const float* __restrict__ b_down, int batch, float* __restrict__ y_part, int dense_min, int nsplit) {
+  static_assert(WT == DT_F32 || WT == DT_F16, "Q4_0 weights take k_bdown_q4");
+  constexpr int NW = (WT == DT_F16) ? 1 : 2;       // weight operands: hi (and lo for fp32)
   constexpr int NWV = 2 * (WT == DT_F32 ? 2 : 1);  // 16-byte pieces per row segment of 8 columns, times items
   __shared__ __attribute__((aligned(16))) _Float16 wt[NW][BD_COLS][BD_PAD];
   __shared__ __attribute__((aligned(16))) _Float16 as[2][BD_CH / 16][512];
@@ -894,11 +895,9 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
     for (int q = 0; q < 4; ++q) id[q] = ulist[max(0, min(base + 4 * pg + q, n - 1))];
   };
   // Items of a thread: i = 0, 1 are the adjacent tiles 2 (t >> 7) + i (t = tid), in
-  // both at columns 8 cq .. 8 cq + 7 with cq = (t >> 5) & 3, so a row's two
-  // Q4_0 block scales are one aligned 4-byte word (d / 32 is even).
+  // both at columns 8 cq .. 8 cq + 7 with cq = (t >> 5) & 3.
   struct Stage {
     uint4 wv[2][4][NWV / 2];  // items x four rows: 16 bytes (fp32: 32) of each row segment
-    uint32_t sc[4];           // Q4_0: the two tiles' block scales of each row (fp16 bits)
     float4 hv[2];             // 8 values of h for the A operands
   };
   auto fetch = [&](int c, const int (&id)[4], Stage& st) __attribute__((always_inline)) {
@@ -906,18 +905,10 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const size_t row = (size_t)(dense ? max(0, min(base + 4 * pg + q, n - 1)) : id[q]);
-      if constexpr (WT == DT_Q4)   // a pair wholly past d is clamped to the row's last pair (dropped)
-        st.sc[q] = *reinterpret_cast<const uint32_t*>(down_sc + row * (d / 32) +
-                                                      min(c0 / 32 + 2 * (tid >> 7), d / 32 - 2));
-      else
-        st.sc[q] = 0u;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int tile = 2 * (tid >> 7) + i;
-        if constexpr (WT == DT_Q4) {
-          const int cb = min(c0 + BM * tile, d - BM);               // the tile's Q4_0 block (clamped)
-          st.wv[i][q][0] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(downT) + row * (d / 2) + cb / 2);
-        } else {
+        {
           const int col = min(c0 + BM * tile + 8 * ((tid >> 5) & 3), d - 8);
           if constexpr (WT == DT_F16) {
             st.wv[i][q][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(downT) + row * d + col);
@@ -964,36 +955,23 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
           *reinterpret_cast<h4v*>(&wt[NW - 1][BM * tile + 8 * cq + e][4 * pg]) = h4v{lo[0], lo[1], lo[2], lo[3]};
         }
       } else {
-        // fp16: the weights themselves; Q4_0: (q - 8) exact in fp16 times the block
-        // scale as hi = fl16(q s) and lo = fl16(q s - hi) (one packed multiply and one
-        // packed fused multiply-add: q s - hi needs at most 4 significant bits).  Two
-        // rows at a time, each column's pair of positions written at once.
+        // fp16: the weights themselves, two rows at a time, each column's pair of
+        // positions written at once
 #pragma unroll
         for (int rp = 0; rp < 4; rp += 2) {
-          h8v hi[2], lo[2];
+          h8v hi[2];
 #pragma unroll
           for (int q2 = 0; q2 < 2; ++q2) {
             const int q = rp + q2;
             // zeroed by an AND with a mask (a select here becomes a branch that the
             // compiler places next to the loads, with a wait for all of them)
             const uint32_t m = 0u - (uint32_t)(okc && c < nch && base + 4 * pg + q < n);
-            if constexpr (WT == DT_F16) {
-              const uint4 wv = st.wv[i][q][0];
-              hi[q2] = as_h8(make_uint4(wv.x & m, wv.y & m, wv.z & m, wv.w & m));
-            } else {
-              const h8v qv = q4_h8(st.wv[i][q][0], 8 * (cq & 1), cq >= 2);
-              const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)((st.sc[q] >> (16 * i)) & m));
-              const h8v s8 = {sv, sv, sv, sv, sv, sv, sv, sv};
-              hi[q2] = qv * s8;
-              lo[q2] = __builtin_elementwise_fma(qv, s8, -hi[q2]);
-            }
+            const uint4 wv = st.wv[i][q][0];
+            hi[q2] = as_h8(make_uint4(wv.x & m, wv.y & m, wv.z & m, wv.w & m));
           }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
+          for (int e = 0; e < 8; ++e)
             *reinterpret_cast<h2v*>(dst0 + e * BD_PAD + rp) = h2v{hi[0][e], hi[1][e]};
-            if constexpr (NW == 2)
-              *reinterpret_cast<h2v*>(&wt[NW - 1][BM * tile + 8 * cq + e][4 * pg + rp]) = h2v{lo[0][e], lo[1][e]};
-          }
         }
       }
     }
@@ -1053,6 +1031,184 @@ k_bdown(const void* __restrict__ downT, const uint16_t* __restrict__ down_sc, in
   }
   __syncthreads();                                 // rsc is written
   // lane holds column c0 + 32 w + lane % 32, batch rows 8 g + 4 (lane / 32) + v
+  const int cg = c0 + BM * w + (lane & 31);
+  if (cg < d) {
+    const float bd = (b_down && split == 0) ? b_down[cg] : 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int b = 8 * g + 4 * (lane / 32) + v;
+        if (b < batch) y_part[((size_t)split * BM + b) * d + cg] = acc[4 * g + v] * rsc[b] + bd;
+      }
+  }
+}
+
+// ------------------------------------------------- down projection (Q4_0)
+// k_bdown's product for Q4_0 weights, organised for memory-level parallelism:
+// wave w converts the tile it multiplies (32 columns, the 16-byte Q4_0 block
+// of each row) and lane l takes chunk positions 2 l and 2 l + 1, so every
+// 16-byte block is loaded once and each column's pair of positions is one
+// 4-byte LDS write (64 lanes, 64 consecutive words).  Three chunks are in
+// flight while one is converted and multiplied.  Loads complete in issue
+// order, so the row ids of a chunk are loaded two steps before its weights,
+// first in their step: the wait for them then covers only the chunk that is
+// converted in that same step.  Results are those of k_bdown (the same hi/lo
+// values, products and order).
+__global__ void __launch_bounds__(512)
+k_bdown_q4(const uint8_t* __restrict__ downT, const uint16_t* __restrict__ down_sc, int f, int d,
+           const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount, const float* __restrict__ h32,
+           const uint32_t* __restrict__ hmax, const float* __restrict__ b_down, int batch,
+           float* __restrict__ y_part, int dense_min, int nsplit) {
+  __shared__ __attribute__((aligned(16))) _Float16 wt[2][BD_COLS][BD_PAD];
+  __shared__ __attribute__((aligned(16))) _Float16 as[2][BD_CH / 16][512];
+  __shared__ float rsc[BM];
+  static_assert(BD_CH == 2 * WAVE && BD_COLS == 8 * BM, "a lane's two positions, a wave's tile");
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const int ngroup = (d + BD_COLS - 1) / BD_COLS;
+  const int c0 = (int)(blockIdx.x % ngroup) * BD_COLS, split = (int)blockIdx.x / ngroup;
+  bool dense;
+  const int n = ffn_rows(ucount, f, dense_min, &dense);
+  const int nch_all = (n + BD_CH - 1) / BD_CH, cps = (nch_all + nsplit - 1) / nsplit;
+  const int ch0 = split * cps;
+  const int nch = max(0, min(nch_all, ch0 + cps) - ch0);
+  const float hs = pow2_scale(__uint_as_float(hmax[lane & 31]));
+  if (tid < BM) rsc[tid] = 1.f / pow2_scale(__uint_as_float(hmax[tid]));
+  // wave w's tile: its Q4_0 block in every row (clamped into the row when the
+  // tile is past d, then dropped), and the aligned word of two block scales
+  // that holds its scale (half w & 1: c0 / 32 is a multiple of 8, d / 32 even)
+  const bool okc = c0 + BM * w < d;
+  const int cb = min(c0 + BM * w, d - BM);
+  const int sw = min(c0 / 32 + (w & ~1), d / 32 - 2);
+  const int ssh = 16 * (w & 1);
+  f16v acc = {};
+
+  struct Stage {
+    uint4 wv[2];      // the tile's block of rows 2 lane, 2 lane + 1
+    uint32_t sc[2];   // their scale words
+    float4 hv[2];     // 8 values of h for the A operands
+  };
+  // chunk c's rows for positions 2 lane + q (clamped into the list and the split)
+  // (the dense and the list case are separate instantiations of the loop below:
+  // any select between a loaded id and a position is placed by the compiler next
+  // to the load, with a wait for every load before it)
+  auto load_ids = [&](auto dense_c, int c, int (&id)[2]) __attribute__((always_inline)) {
+    const int base = (ch0 + min(c, nch - 1)) * BD_CH + 2 * lane;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int p = max(0, min(base + q, n - 1));
+      id[q] = decltype(dense_c)::value ? p : ulist[p];
+    }
+  };
+  auto fetch = [&](int c, const int (&id)[2], Stage& st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const size_t row = (size_t)id[q];
+      st.wv[q] = *reinterpret_cast<const uint4*>(downT + row * (d / 2) + cb / 2);
+      st.sc[q] = *reinterpret_cast<const uint32_t*>(down_sc + row * (d / 32) + sw);
+    }
+    const float4* hp =
+        reinterpret_cast<const float4*>(h32 + (size_t)((ch0 + min(c, nch - 1)) * (BD_CH / 16) + w) * 512 + 8 * lane);
+    st.hv[0] = hp[0];
+    st.hv[1] = hp[1];
+  };
+  // a chunk's operands into LDS; positions past the split or the list and columns
+  // past d are zero (a zero scale; h there is whatever an earlier call left)
+  auto convert = [&](const Stage& st, int c) __attribute__((always_inline)) {
+    const int base = (ch0 + c) * BD_CH;
+    const uint32_t m0 = 0u - (uint32_t)(okc && c < nch && base + 2 * lane < n);
+    const uint32_t m1 = 0u - (uint32_t)(okc && c < nch && base + 2 * lane + 1 < n);
+    const h2v s2 = {__builtin_bit_cast(_Float16, (uint16_t)((st.sc[0] >> ssh) & m0)),
+                    __builtin_bit_cast(_Float16, (uint16_t)((st.sc[1] >> ssh) & m1))};
+    const h2v off = {(_Float16)1032.f, (_Float16)1032.f};
+    _Float16* dh = &wt[0][BM * w][2 * lane];
+    _Float16* dl = &wt[1][BM * w][2 * lane];
+    const uint32_t a[4] = {st.wv[0].x, st.wv[0].y, st.wv[0].z, st.wv[0].w};
+    const uint32_t b[4] = {st.wv[1].x, st.wv[1].y, st.wv[1].z, st.wv[1].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // byte j of word k (columns 4 k + j, low nibble, and 4 k + j + 16, high
+        // nibble) of both rows, in the low bytes of two 16-bit lanes
+        const uint32_t p = __builtin_amdgcn_perm(b[k], a[k], 0x0c000c00u | (uint32_t)j | ((uint32_t)(4 + j) << 16));
+        const h2v ql = __builtin_bit_cast(h2v, (p & 0x000F000Fu) | 0x64006400u) - off;
+        const h2v qh = __builtin_bit_cast(h2v, ((p >> 4) & 0x000F000Fu) | 0x64006400u) - off;
+        const h2v hl = ql * s2, hh = qh * s2;
+        const h2v ll = __builtin_elementwise_fma(ql, s2, -hl), lh = __builtin_elementwise_fma(qh, s2, -hh);
+        const int e = 4 * k + j;
+        *reinterpret_cast<h2v*>(dh + e * BD_PAD) = hl;
+        *reinterpret_cast<h2v*>(dl + e * BD_PAD) = ll;
+        *reinterpret_cast<h2v*>(dh + (e + 16) * BD_PAD) = hh;
+        *reinterpret_cast<h2v*>(dl + (e + 16) * BD_PAD) = lh;
+      }
+    // A operands: K step w of the chunk, operand slot lane (batch row lane % 32)
+    const int jj = base + 16 * w + 8 * (lane / 32);
+    const float hv8[8] = {st.hv[0].x, st.hv[0].y, st.hv[0].z, st.hv[0].w,
+                          st.hv[1].x, st.hv[1].y, st.hv[1].z, st.hv[1].w};
+    h8v ahi, alo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      _Float16 hi, lo;
+      split_f16(c < nch && jj + e < n ? hv8[e] * hs : 0.f, &hi, &lo);
+      ahi[e] = hi;
+      alo[e] = lo;
+    }
+    *reinterpret_cast<h8v*>(&as[0][w][8 * lane]) = ahi;
+    *reinterpret_cast<h8v*>(&as[1][w][8 * lane]) = alo;
+  };
+  // chunk c: the row ids of chunk c + 5, the loads of chunk c + 3, then chunk c's
+  // operands and products.  No branch: the loop runs whole groups of four
+  // chunks, a chunk past the split converts to zeros, and loads past it repeat
+  // the split's last chunk.
+  auto step = [&](auto dense_c, int c, const Stage& cur, Stage& far, const int (&id_far)[2], int (&id_new)[2])
+      __attribute__((always_inline)) {
+    load_ids(dense_c, c + 5, id_new);
+    fetch(c + 3, id_far, far);
+    PI_ISSUE_FENCE();
+    convert(cur, c);
+    PI_ISSUE_FENCE();
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < BD_CH / 16; ++ks) {
+      const int kb = 16 * ks + 8 * (lane / 32);
+      const h8v ah = *reinterpret_cast<const h8v*>(&as[0][ks][8 * lane]);
+      const h8v al = *reinterpret_cast<const h8v*>(&as[1][ks][8 * lane]);
+      const h8v bw = *reinterpret_cast<const h8v*>(&wt[0][BM * w + (lane & 31)][kb]);
+      const h8v bl = *reinterpret_cast<const h8v*>(&wt[1][BM * w + (lane & 31)][kb]);
+      acc = mfma(ah, bw, acc);
+      acc = mfma(al, bw, acc);
+      acc = mfma(ah, bl, acc);
+    }
+    __syncthreads();
+    PI_ISSUE_FENCE();   // no operand math of the next chunk above the barrier (it would wait for its loads)
+  };
+  auto run = [&](auto dc) __attribute__((always_inline)) {
+    // chunk k's row ids in slot k % 4, its loads in stage k % 4
+    int id0[2], id1[2], id2[2], id3[2];
+    Stage s0, s1, s2, s3;
+    load_ids(dc, 0, id0);
+    load_ids(dc, 1, id1);
+    load_ids(dc, 2, id2);
+    load_ids(dc, 3, id3);
+    fetch(0, id0, s0);
+    load_ids(dc, 4, id0);
+    fetch(1, id1, s1);
+    fetch(2, id2, s2);
+    for (int c = 0; c < nch; c += 4) {
+      step(dc, c, s0, s3, id3, id1);
+      step(dc, c + 1, s1, s0, id0, id2);
+      step(dc, c + 2, s2, s1, id1, id3);
+      step(dc, c + 3, s3, s2, id2, id0);
+    }
+  };
+  if (nch > 0) {
+    if (dense)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
+  }
+  __syncthreads();                                 // rsc is written
   const int cg = c0 + BM * w + (lane & 31);
   if (cg < d) {
     const float bd = (b_down && split == 0) ? b_down[cg] : 0.f;
