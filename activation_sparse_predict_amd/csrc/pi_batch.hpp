@@ -1045,25 +1045,33 @@ k_bdown(const void* __restrict__ downT, int f, int d, const int32_t* __restrict_
 }
 
 // ------------------------------------------------- down projection (Q4_0)
-// k_bdown's product for Q4_0 weights, organised for memory-level parallelism:
-// wave w converts the tile it multiplies (32 columns, the 16-byte Q4_0 block
-// of each row) and lane l takes chunk positions 2 l and 2 l + 1, so every
-// 16-byte block is loaded once and each column's pair of positions is one
-// 4-byte LDS write (64 lanes, 64 consecutive words).  Three chunks are in
-// flight while one is converted and multiplied.  Loads complete in issue
-// order, so the row ids of a chunk are loaded two steps before its weights,
-// first in their step: the wait for them then covers only the chunk that is
-// converted in that same step.  Results are those of k_bdown (the same hi/lo
-// values, products and order).
+// k_bdown's blocks, splits and chunks for Q4_0 weights, organised for
+// memory-level parallelism.  Thread t of the block takes chunk positions
+// 16 (t / 64) + 2 r and + 1 (r = (t % 64) / 8) of tile q = t % 8: eight lanes
+// read the 128 bytes of a row's segment (one line per row, not one per lane),
+// every 16-byte Q4_0 block is loaded once, and each column's pair of
+// positions is one 4-byte LDS write.  A column's positions are stored in
+// 16-byte groups (8 positions) with group g at g ^ 2 (c / 32 % 8): the 64 lanes
+// of a write then hit 64 different banks, and a wave's MFMA reads (one tile,
+// one XOR value) are as without the swizzle.  The weights enter as hi = fl16(q s)
+// and lo = fl16(q s - hi) with (q - 8) exact in fp16 (q s - hi has at most 4
+// significant bits).  Three chunks are in flight while one is converted and
+// multiplied.  Loads complete in issue order, so the row ids of a chunk are
+// loaded two steps before its weights, first in their step: the wait for them
+// then covers only the chunk that is converted in that same step.
+__host__ __device__ constexpr int bdq_slot(int col, int pos) {   // halves offset of (col, pos) in a wt plane
+  return col * BD_PAD + 8 * ((pos / 8) ^ (2 * ((col / BM) % 8))) + pos % 8;
+}
+
 __global__ void __launch_bounds__(512)
 k_bdown_q4(const uint8_t* __restrict__ downT, const uint16_t* __restrict__ down_sc, int f, int d,
            const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount, const float* __restrict__ h32,
            const uint32_t* __restrict__ hmax, const float* __restrict__ b_down, int batch,
            float* __restrict__ y_part, int dense_min, int nsplit) {
-  __shared__ __attribute__((aligned(16))) _Float16 wt[2][BD_COLS][BD_PAD];
+  __shared__ __attribute__((aligned(16))) _Float16 wt[2][BD_COLS * BD_PAD];
   __shared__ __attribute__((aligned(16))) _Float16 as[2][BD_CH / 16][512];
   __shared__ float rsc[BM];
-  static_assert(BD_CH == 2 * WAVE && BD_COLS == 8 * BM, "a lane's two positions, a wave's tile");
+  static_assert(BD_CH == 128 && BD_COLS == 8 * BM, "16 positions per wave, 8 tiles per block");
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int ngroup = (d + BD_COLS - 1) / BD_COLS;
   const int c0 = (int)(blockIdx.x % ngroup) * BD_COLS, split = (int)blockIdx.x / ngroup;
@@ -1074,38 +1082,39 @@ k_bdown_q4(const uint8_t* __restrict__ downT, const uint16_t* __restrict__ down_
   const int nch = max(0, min(nch_all, ch0 + cps) - ch0);
   const float hs = pow2_scale(__uint_as_float(hmax[lane & 31]));
   if (tid < BM) rsc[tid] = 1.f / pow2_scale(__uint_as_float(hmax[tid]));
-  // wave w's tile: its Q4_0 block in every row (clamped into the row when the
-  // tile is past d, then dropped), and the aligned word of two block scales
-  // that holds its scale (half w & 1: c0 / 32 is a multiple of 8, d / 32 even)
-  const bool okc = c0 + BM * w < d;
-  const int cb = min(c0 + BM * w, d - BM);
-  const int sw = min(c0 / 32 + (w & ~1), d / 32 - 2);
-  const int ssh = 16 * (w & 1);
+  // this thread's tile (its Q4_0 block in every row, clamped into the row when the
+  // tile is past d, then dropped), the aligned word of two block scales that holds
+  // its scale (half q & 1: c0 / 32 is a multiple of 8, d / 32 even), its positions
+  const int q = tid & 7, p0 = 16 * w + 2 * ((tid & 63) >> 3);
+  const bool okc = c0 + BM * q < d;
+  const int cb = min(c0 + BM * q, d - BM);
+  const int sw = min(c0 / 32 + (q & ~1), d / 32 - 2);
+  const int ssh = 16 * (q & 1);
   f16v acc = {};
 
   struct Stage {
-    uint4 wv[2];      // the tile's block of rows 2 lane, 2 lane + 1
+    uint4 wv[2];      // the tile's block of the rows at positions p0, p0 + 1
     uint32_t sc[2];   // their scale words
     float4 hv[2];     // 8 values of h for the A operands
   };
-  // chunk c's rows for positions 2 lane + q (clamped into the list and the split)
+  // chunk c's rows at positions p0 + k (clamped into the list and the split)
   // (the dense and the list case are separate instantiations of the loop below:
   // any select between a loaded id and a position is placed by the compiler next
   // to the load, with a wait for every load before it)
   auto load_ids = [&](auto dense_c, int c, int (&id)[2]) __attribute__((always_inline)) {
-    const int base = (ch0 + min(c, nch - 1)) * BD_CH + 2 * lane;
+    const int base = (ch0 + min(c, nch - 1)) * BD_CH + p0;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int p = max(0, min(base + q, n - 1));
-      id[q] = decltype(dense_c)::value ? p : ulist[p];
+    for (int k = 0; k < 2; ++k) {
+      const int p = max(0, min(base + k, n - 1));
+      id[k] = decltype(dense_c)::value ? p : ulist[p];
     }
   };
   auto fetch = [&](int c, const int (&id)[2], Stage& st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const size_t row = (size_t)id[q];
-      st.wv[q] = *reinterpret_cast<const uint4*>(downT + row * (d / 2) + cb / 2);
-      st.sc[q] = *reinterpret_cast<const uint32_t*>(down_sc + row * (d / 32) + sw);
+    for (int k = 0; k < 2; ++k) {
+      const size_t row = (size_t)id[k];
+      st.wv[k] = *reinterpret_cast<const uint4*>(downT + row * (d / 2) + cb / 2);
+      st.sc[k] = *reinterpret_cast<const uint32_t*>(down_sc + row * (d / 32) + sw);
     }
     const float4* hp =
         reinterpret_cast<const float4*>(h32 + (size_t)((ch0 + min(c, nch - 1)) * (BD_CH / 16) + w) * 512 + 8 * lane);
@@ -1116,13 +1125,13 @@ k_bdown_q4(const uint8_t* __restrict__ downT, const uint16_t* __restrict__ down_
   // past d are zero (a zero scale; h there is whatever an earlier call left)
   auto convert = [&](const Stage& st, int c) __attribute__((always_inline)) {
     const int base = (ch0 + c) * BD_CH;
-    const uint32_t m0 = 0u - (uint32_t)(okc && c < nch && base + 2 * lane < n);
-    const uint32_t m1 = 0u - (uint32_t)(okc && c < nch && base + 2 * lane + 1 < n);
+    const uint32_t m0 = 0u - (uint32_t)(okc && c < nch && base + p0 < n);
+    const uint32_t m1 = 0u - (uint32_t)(okc && c < nch && base + p0 + 1 < n);
     const h2v s2 = {__builtin_bit_cast(_Float16, (uint16_t)((st.sc[0] >> ssh) & m0)),
                     __builtin_bit_cast(_Float16, (uint16_t)((st.sc[1] >> ssh) & m1))};
     const h2v off = {(_Float16)1032.f, (_Float16)1032.f};
-    _Float16* dh = &wt[0][BM * w][2 * lane];
-    _Float16* dl = &wt[1][BM * w][2 * lane];
+    _Float16* dh = &wt[0][bdq_slot(BM * q, p0)];
+    _Float16* dl = &wt[1][bdq_slot(BM * q, p0)];
     const uint32_t a[4] = {st.wv[0].x, st.wv[0].y, st.wv[0].z, st.wv[0].w};
     const uint32_t b[4] = {st.wv[1].x, st.wv[1].y, st.wv[1].z, st.wv[1].w};
 #pragma unroll
@@ -1136,7 +1145,7 @@ k_bdown_q4(const uint8_t* __restrict__ downT, const uint16_t* __restrict__ down_
         const h2v qh = __builtin_bit_cast(h2v, ((p >> 4) & 0x000F000Fu) | 0x64006400u) - off;
         const h2v hl = ql * s2, hh = qh * s2;
         const h2v ll = __builtin_elementwise_fma(ql, s2, -hl), lh = __builtin_elementwise_fma(qh, s2, -hh);
-        const int e = 4 * k + j;
+        const int e = 4 * k + j;   // columns of one tile share the swizzle: a column's offset is e BD_PAD
         *reinterpret_cast<h2v*>(dh + e * BD_PAD) = hl;
         *reinterpret_cast<h2v*>(dl + e * BD_PAD) = ll;
         *reinterpret_cast<h2v*>(dh + (e + 16) * BD_PAD) = hh;
@@ -1172,10 +1181,11 @@ k_bdown_q4(const uint8_t* __restrict__ downT, const uint16_t* __restrict__ down_
 #pragma unroll
     for (int ks = 0; ks < BD_CH / 16; ++ks) {
       const int kb = 16 * ks + 8 * (lane / 32);
+      const int at = bdq_slot(BM * w + (lane & 31), kb);
       const h8v ah = *reinterpret_cast<const h8v*>(&as[0][ks][8 * lane]);
       const h8v al = *reinterpret_cast<const h8v*>(&as[1][ks][8 * lane]);
-      const h8v bw = *reinterpret_cast<const h8v*>(&wt[0][BM * w + (lane & 31)][kb]);
-      const h8v bl = *reinterpret_cast<const h8v*>(&wt[1][BM * w + (lane & 31)][kb]);
+      const h8v bw = *reinterpret_cast<const h8v*>(&wt[0][at]);
+      const h8v bl = *reinterpret_cast<const h8v*>(&wt[1][at]);
       acc = mfma(ah, bw, acc);
       acc = mfma(al, bw, acc);
       acc = mfma(ah, bl, acc);
