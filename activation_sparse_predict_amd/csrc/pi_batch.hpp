@@ -70,13 +70,13 @@ __device__ __forceinline__ h8v as_h8(uint4 c) { return __builtin_bit_cast(h8v, c
 
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
-// 8 weights of a Q4_0 chunk as (q - 8) in fp16, exact: nibbles of bytes
-// [b0, b0+8) (b0 = 0 or 8), low (hi_nib = false) or high nibble.  Two bytes at a
+// 8 weights of a Q4_0 block as (q - 8) in fp16, exact: nibbles of 8 of its
+// bytes (the words w0, w1), low (hi_nib = false) or high nibble.  Two bytes at a
 // time go to the low bits of two 16-bit lanes (a byte permute), the nibble is
 // masked into the mantissa of the fp16 1024 (0x6400 | q = 1024 + q), and 1032 is
 // subtracted from both lanes at once: four operations per pair of weights.
-__device__ __forceinline__ h8v q4_h8(uint4 c, int b0, bool hi_nib) {
-  const uint32_t wd[2] = {b0 ? c.z : c.x, b0 ? c.w : c.y};
+__device__ __forceinline__ h8v q4_h8w(uint32_t w0, uint32_t w1, bool hi_nib) {
+  const uint32_t wd[2] = {w0, w1};
   const h2v off = {(_Float16)1032.f, (_Float16)1032.f};
   h8v r;
 #pragma unroll
@@ -90,6 +90,18 @@ __device__ __forceinline__ h8v q4_h8(uint4 c, int b0, bool hi_nib) {
     r[2 * k + 1] = h[1];
   }
   return r;
+}
+
+// A row's Q4_0 blocks 2m and 2m + 1 for an MFMA operand whose lane half h
+// (lanes 32 h .. 32 h + 31, one row per lane) needs bytes [8 h, 8 h + 8) of
+// each: half h loads block 2m + h whole, and two swaps of the halves' words
+// (v_permlane32_swap exchanges a register's upper 32 lanes with another's
+// lower 32) leave each half its bytes of block 2m in lo and of 2m + 1 in hi.
+__device__ __forceinline__ void q4_pair(uint4 c, uint2& lo, uint2& hi) {
+  const auto a = __builtin_amdgcn_permlane32_swap(c.x, c.z, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(c.y, c.w, false, false);
+  lo = make_uint2(a[0], b[0]);
+  hi = make_uint2(a[1], b[1]);
 }
 
 // ------------------------------------------------------------------- glue
@@ -649,22 +661,24 @@ k_bup2(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, co
       }
       const int kw = kc + kp * (kcn / 2), kwn = kcn / 2;        // this wave's half
       constexpr int QB = KH / 32;
-      // the row's nibbles for the half chunk (one 16-byte block per load) and its block
-      // scales two at a time: aligned words from the even block a0 = kw / 32 rounded
-      // down (d / 32 is even, so a word lies wholly inside the row or wholly past it,
-      // then clamped to the row's last word and not used); block kw / 32 + qb is
-      // half (o + qb) & 1 of word (o + qb) / 2, o = kw / 32 - a0
+      // the row's nibbles for the half chunk (one 16-byte block per load; the two lane
+      // halves hold the same rows and load alternate blocks) and its block scales two
+      // at a time: aligned words from the even block a0 = kw / 32 rounded down (d / 32
+      // is even, so a word lies wholly inside the row or wholly past it, then clamped
+      // to the row's last word and not used); block kw / 32 + qb is half (o + qb) & 1
+      // of word (o + qb) / 2, o = kw / 32 - a0
       const int a0 = (kw / 32) & ~1, o = (kw / 32) & 1;
-      uint4 cq[NMAT][QB];
+      static_assert(QB % 2 == 0, "blocks in pairs");
+      uint4 cq[NMAT][QB / 2];     // block 2m + half of the pair m (exchanged by q4_pair)
       uint32_t scw[NMAT][QB / 2 + 1];
 #pragma unroll
       for (int mt = 0; mt < NMAT; ++mt) {
         const void* wp = (NMAT == 2 && mt == 0) ? gate_w : up_w;
         const uint16_t* sp = (NMAT == 2 && mt == 0) ? gate_sc : up_sc;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int kb = kw + 32 * min(qb, kwn / 32 - 1);
-          cq[mt][qb] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(wp) + row * (d / 2) + kb / 2);
+        for (int m = 0; m < QB / 2; ++m) {
+          const int kb = kw + 32 * min(2 * m + half, kwn / 32 - 1);
+          cq[mt][m] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(wp) + row * (d / 2) + kb / 2);
         }
 #pragma unroll
         for (int p = 0; p <= QB / 2; ++p)
@@ -673,6 +687,11 @@ k_bup2(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, co
       PI_ISSUE_FENCE();
       wait_vm_lds<0>();
       __syncthreads();                                        // every wave's part of the chunk is in LDS
+      uint2 cw[NMAT][QB];                                     // this half's 8 bytes of each block
+#pragma unroll
+      for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+        for (int m = 0; m < QB / 2; ++m) q4_pair(cq[mt][m], cw[mt][2 * m], cw[mt][2 * m + 1]);
       // every block of the half chunk is multiplied (blocks past a short last
       // chunk read clamped weights and LDS steps inside xs, and are dropped by a
       // select): a branch around the use would sink the loads into it, one HBM
@@ -686,7 +705,7 @@ k_bup2(const void* __restrict__ gate_w, const uint16_t* __restrict__ gate_sc, co
           f16v p = {};
 #pragma unroll
           for (int stp = 0; stp < 2; ++stp) {
-            const h8v bw = q4_h8(cq[mt][qb], 8 * half, stp == 1);
+            const h8v bw = q4_h8w(cw[mt][qb].x, cw[mt][qb].y, stp == 1);
             const h8v ah = *reinterpret_cast<const h8v*>(&xs[0][(st0 + stp) * 512 + 8 * lane]);
             const h8v al = *reinterpret_cast<const h8v*>(&xs[1][(st0 + stp) * 512 + 8 * lane]);
             p = mfma(ah, bw, p);
