@@ -612,6 +612,10 @@ void b_ffn_t(const pi_layer* L, int batch, const Ws& W, const int32_t* ulist, co
     hipLaunchKernelGGL(pib::k_bdown_q4, dim3(cdiv(L->d, pib::BD_COLS) * pib::bd_splits(L->d)), dim3(512), 0, st,
                        static_cast<const uint8_t*>(L->downT.w), L->downT.scale, L->ffn, L->d, ulist, ucount, W.h32,
                        W.hmax, L->b_down, batch, y, dense_min(L), pib::bd_splits(L->d));
+  else if constexpr (WT == DT_F16)
+    hipLaunchKernelGGL(pib::k_bdown_f16, dim3(cdiv(L->d, pib::BD_COLS) * pib::bd_splits(L->d)), dim3(512), 0, st,
+                       static_cast<const uint16_t*>(L->downT.w), L->ffn, L->d, ulist, ucount, W.h32, W.hmax,
+                       L->b_down, batch, y, dense_min(L), pib::bd_splits(L->d));
   else
     hipLaunchKernelGGL(pib::k_bdown<WT>, dim3(cdiv(L->d, pib::BD_COLS) * pib::bd_splits(L->d)), dim3(512), 0, st,
                        L->downT.w, L->ffn, L->d, ulist, ucount, W.h32, W.hmax, L->b_down, batch, y, dense_min(L),

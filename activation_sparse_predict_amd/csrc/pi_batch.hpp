@@ -863,15 +863,15 @@ k_bcompact(const uint8_t* __restrict__ u, const int32_t* __restrict__ tile_cnt, 
 // Per chunk the block stages, in LDS,
 //  - the A operands once for all eight tiles: h (read in its operand-order
 //    layout) times the row scale from hmax, split into fp16 hi/lo;
-//  - each tile's weights transposed to [column][position] as fp16 (fp32
-//    weights as hi + lo pairs).
-// Every thread converts four positions of eight columns in each of its two
-// items (adjacent tiles) and writes each column's values in pairs.  The next chunk's
-// weights and h, and the row ids of the chunk after it, are in flight while a
-// chunk is converted and multiplied.  Blocks that read a whole 128-byte line
-// (or several) of every row they gather, and h once per 256 columns instead
-// of once per 32 or 64.  Q4_0 weights take k_bdown_q4 (same blocks, chunks and
-// results, more of them in flight).
+//  - each tile's weights transposed to [column][position] as fp16 hi + lo
+//    pairs.
+// k_bdown takes fp32 weights: every thread converts four positions of eight
+// columns in each of its two items (adjacent tiles) and writes each column's
+// values in pairs; the next chunk's weights and h, and the row ids of the chunk
+// after it, are in flight while a chunk is converted and multiplied.  Blocks
+// read a whole 128-byte line (or several) of every row they gather, and h once
+// per 256 columns instead of once per 32 or 64.  Q4_0 and fp16 weights take
+// k_bdown_q4 and k_bdown_f16 (same blocks and chunks, more chunks in flight).
 constexpr int BD_COLS = 256;             // columns per block (eight 32-column tiles, one per wave)
 constexpr int BD_PAD = BD_CH + 8;        // padded position stride (halves) of a transposed column
 constexpr int BD_MAXSPLIT = 16;          // most splits of the union list (partial y vectors)
@@ -888,9 +888,9 @@ __global__ void __launch_bounds__(512)
 k_bdown(const void* __restrict__ downT, int f, int d, const int32_t* __restrict__ ulist,
         const int32_t* __restrict__ ucount, const float* __restrict__ h32, const uint32_t* __restrict__ hmax,
         const float* __restrict__ b_down, int batch, float* __restrict__ y_part, int dense_min, int nsplit) {
-  static_assert(WT == DT_F32 || WT == DT_F16, "Q4_0 weights take k_bdown_q4");
-  constexpr int NW = (WT == DT_F16) ? 1 : 2;       // weight operands: hi (and lo for fp32)
-  constexpr int NWV = 2 * (WT == DT_F32 ? 2 : 1);  // 16-byte pieces per row segment of 8 columns, times items
+  static_assert(WT == DT_F32, "Q4_0 and fp16 weights take k_bdown_q4 and k_bdown_f16");
+  constexpr int NW = 2;                            // weight operands: hi and lo
+  constexpr int NWV = 4;                           // 16-byte pieces per row segment of 8 columns, times items
   __shared__ __attribute__((aligned(16))) _Float16 wt[NW][BD_COLS][BD_PAD];
   __shared__ __attribute__((aligned(16))) _Float16 as[2][BD_CH / 16][512];
   __shared__ float rsc[BM];                        // 1 / row scale of h, per batch row
@@ -916,7 +916,7 @@ k_bdown(const void* __restrict__ downT, int f, int d, const int32_t* __restrict_
   // Items of a thread: i = 0, 1 are the adjacent tiles 2 (t >> 7) + i (t = tid), in
   // both at columns 8 cq .. 8 cq + 7 with cq = (t >> 5) & 3.
   struct Stage {
-    uint4 wv[2][4][NWV / 2];  // items x four rows: 16 bytes (fp32: 32) of each row segment
+    uint4 wv[2][4][NWV / 2];  // items x four rows: the 32 bytes of each row segment
     float4 hv[2];             // 8 values of h for the A operands
   };
   auto fetch = [&](int c, const int (&id)[4], Stage& st) __attribute__((always_inline)) {
@@ -927,16 +927,10 @@ k_bdown(const void* __restrict__ downT, int f, int d, const int32_t* __restrict_
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int tile = 2 * (tid >> 7) + i;
-        {
-          const int col = min(c0 + BM * tile + 8 * ((tid >> 5) & 3), d - 8);
-          if constexpr (WT == DT_F16) {
-            st.wv[i][q][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(downT) + row * d + col);
-          } else {
-            const float* fp = static_cast<const float*>(downT) + row * d + col;
-            st.wv[i][q][0] = *reinterpret_cast<const uint4*>(fp);
-            st.wv[i][q][1] = *reinterpret_cast<const uint4*>(fp + 4);
-          }
-        }
+        const int col = min(c0 + BM * tile + 8 * ((tid >> 5) & 3), d - 8);
+        const float* fp = static_cast<const float*>(downT) + row * d + col;
+        st.wv[i][q][0] = *reinterpret_cast<const uint4*>(fp);
+        st.wv[i][q][1] = *reinterpret_cast<const uint4*>(fp + 4);
       }
     }
     const float4* hp = reinterpret_cast<const float4*>(h32 + (size_t)((ch0 + c) * (BD_CH / 16) + w) * 512 + 8 * lane);
@@ -953,45 +947,24 @@ k_bdown(const void* __restrict__ downT, int f, int d, const int32_t* __restrict_
       const int tile = 2 * (tid >> 7) + i, cq = (tid >> 5) & 3;
       const bool okc = c0 + BM * tile + 8 * cq < d;
       _Float16* dst0 = &wt[0][BM * tile + 8 * cq][4 * pg];
-      if constexpr (WT == DT_F32) {
-        float v[4][8];
+      float v[4][8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const bool ok = okc && c < nch && base + 4 * pg + q < n;
-          const float a8[8] = {__uint_as_float(st.wv[i][q][0].x), __uint_as_float(st.wv[i][q][0].y),
-                               __uint_as_float(st.wv[i][q][0].z), __uint_as_float(st.wv[i][q][0].w),
-                               __uint_as_float(st.wv[i][q][1].x), __uint_as_float(st.wv[i][q][1].y),
-                               __uint_as_float(st.wv[i][q][1].z), __uint_as_float(st.wv[i][q][1].w)};
+      for (int q = 0; q < 4; ++q) {
+        const bool ok = okc && c < nch && base + 4 * pg + q < n;
+        const float a8[8] = {__uint_as_float(st.wv[i][q][0].x), __uint_as_float(st.wv[i][q][0].y),
+                             __uint_as_float(st.wv[i][q][0].z), __uint_as_float(st.wv[i][q][0].w),
+                             __uint_as_float(st.wv[i][q][1].x), __uint_as_float(st.wv[i][q][1].y),
+                             __uint_as_float(st.wv[i][q][1].z), __uint_as_float(st.wv[i][q][1].w)};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[q][e] = ok ? a8[e] : 0.f;
-        }
+        for (int e = 0; e < 8; ++e) v[q][e] = ok ? a8[e] : 0.f;
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          _Float16 hi[4], lo[4];
+      for (int e = 0; e < 8; ++e) {
+        _Float16 hi[4], lo[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) split_f16(v[q][e], &hi[q], &lo[q]);
-          *reinterpret_cast<h4v*>(dst0 + e * BD_PAD) = h4v{hi[0], hi[1], hi[2], hi[3]};
-          *reinterpret_cast<h4v*>(&wt[NW - 1][BM * tile + 8 * cq + e][4 * pg]) = h4v{lo[0], lo[1], lo[2], lo[3]};
-        }
-      } else {
-        // fp16: the weights themselves, two rows at a time, each column's pair of
-        // positions written at once
-#pragma unroll
-        for (int rp = 0; rp < 4; rp += 2) {
-          h8v hi[2];
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) {
-            const int q = rp + q2;
-            // zeroed by an AND with a mask (a select here becomes a branch that the
-            // compiler places next to the loads, with a wait for all of them)
-            const uint32_t m = 0u - (uint32_t)(okc && c < nch && base + 4 * pg + q < n);
-            const uint4 wv = st.wv[i][q][0];
-            hi[q2] = as_h8(make_uint4(wv.x & m, wv.y & m, wv.z & m, wv.w & m));
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            *reinterpret_cast<h2v*>(dst0 + e * BD_PAD + rp) = h2v{hi[0][e], hi[1][e]};
-        }
+        for (int q = 0; q < 4; ++q) split_f16(v[q][e], &hi[q], &lo[q]);
+        *reinterpret_cast<h4v*>(dst0 + e * BD_PAD) = h4v{hi[0], hi[1], hi[2], hi[3]};
+        *reinterpret_cast<h4v*>(&wt[NW - 1][BM * tile + 8 * cq + e][4 * pg]) = h4v{lo[0], lo[1], lo[2], lo[3]};
       }
     }
     // A operands: K step w of the chunk, operand slot lane (batch row lane % 32)
@@ -1030,10 +1003,8 @@ k_bdown(const void* __restrict__ downT, int f, int d, const int32_t* __restrict_
       const h8v bw = *reinterpret_cast<const h8v*>(&wt[0][BM * w + (lane & 31)][kb]);
       acc = mfma(ah, bw, acc);
       acc = mfma(al, bw, acc);
-      if constexpr (NW == 2) {
-        const h8v bl = *reinterpret_cast<const h8v*>(&wt[1][BM * w + (lane & 31)][kb]);
-        acc = mfma(ah, bl, acc);
-      }
+      const h8v bl = *reinterpret_cast<const h8v*>(&wt[1][BM * w + (lane & 31)][kb]);
+      acc = mfma(ah, bl, acc);
     }
     __syncthreads();
   };
@@ -1186,9 +1157,7 @@ k_bdown_q4(const uint8_t* __restrict__ downT, const uint16_t* __restrict__ down_
     *reinterpret_cast<h8v*>(&as[1][w][8 * lane]) = alo;
   };
   // chunk c: the row ids of chunk c + 5, the loads of chunk c + 3, then chunk c's
-  // operands and products.  No branch: the loop runs whole groups of four
-  // chunks, a chunk past the split converts to zeros, and loads past it repeat
-  // the split's last chunk.
+  // operands and products.  Loads past the split repeat its last chunk.
   auto step = [&](auto dense_c, int c, const Stage& cur, Stage& far, const int (&id_far)[2], int (&id_new)[2])
       __attribute__((always_inline)) {
     load_ids(dense_c, c + 5, id_new);
@@ -1224,11 +1193,197 @@ k_bdown_q4(const uint8_t* __restrict__ downT, const uint16_t* __restrict__ down_
     load_ids(dc, 4, id0);
     fetch(1, id1, s1);
     fetch(2, id2, s2);
-    for (int c = 0; c < nch; c += 4) {
+    int c = 0;
+    for (; c + 4 <= nch; c += 4) {
       step(dc, c, s0, s3, id3, id1);
       step(dc, c + 1, s1, s0, id0, id2);
       step(dc, c + 2, s2, s1, id1, id3);
       step(dc, c + 3, s3, s2, id2, id0);
+    }
+    // the last 1..3 chunks without a whole group of four (the stages are in their
+    // group-start roles here)
+    const int rem = nch - c;
+    if (rem == 1) {
+      step(dc, c, s0, s3, id3, id1);
+    } else if (rem == 2) {
+      step(dc, c, s0, s3, id3, id1);
+      step(dc, c + 1, s1, s0, id0, id2);
+    } else if (rem == 3) {
+      step(dc, c, s0, s3, id3, id1);
+      step(dc, c + 1, s1, s0, id0, id2);
+      step(dc, c + 2, s2, s1, id1, id3);
+    }
+  };
+  if (nch > 0) {
+    if (dense)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
+  }
+  __syncthreads();                                 // rsc is written
+  const int cg = c0 + BM * w + (lane & 31);
+  if (cg < d) {
+    const float bd = (b_down && split == 0) ? b_down[cg] : 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int b = 8 * g + 4 * (lane / 32) + v;
+        if (b < batch) y_part[((size_t)split * BM + b) * d + cg] = acc[4 * g + v] * rsc[b] + bd;
+      }
+  }
+}
+
+// ------------------------------------------------- down projection (fp16)
+// k_bdown's blocks, splits and chunks for fp16 weights with the pipeline of
+// k_bdown_q4: thread t takes the 16-byte piece t % 32 (8 columns) of the
+// block's 512-byte row segment at chunk positions 2 p and 2 p + 1 for the four
+// position pairs p = t / 32 + 16 k, so 32 lanes read a row's whole segment (four
+// lines) per load.  A column's positions are stored in 16-byte groups with
+// group g at g ^ (c / 16 % 16): a write of the 64 lanes hits each bank at most
+// twice, the MFMA reads once.  Three chunks are in flight while one is
+// converted and multiplied, the row ids two steps ahead of their weights.
+__host__ __device__ constexpr int bdh_slot(int col, int pos) {   // halves offset of (col, pos) in wt
+  return col * BD_PAD + 8 * ((pos / 8) ^ ((col / 16) % 16)) + pos % 8;
+}
+
+__global__ void __launch_bounds__(512)
+k_bdown_f16(const uint16_t* __restrict__ downT, int f, int d, const int32_t* __restrict__ ulist,
+            const int32_t* __restrict__ ucount, const float* __restrict__ h32, const uint32_t* __restrict__ hmax,
+            const float* __restrict__ b_down, int batch, float* __restrict__ y_part, int dense_min, int nsplit) {
+  __shared__ __attribute__((aligned(16))) _Float16 wt[BD_COLS * BD_PAD];
+  __shared__ __attribute__((aligned(16))) _Float16 as[2][BD_CH / 16][512];
+  __shared__ float rsc[BM];
+  static_assert(BD_CH == 128 && BD_COLS == 256, "32 pieces of 8 columns, 64 position pairs");
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const int ngroup = (d + BD_COLS - 1) / BD_COLS;
+  const int c0 = (int)(blockIdx.x % ngroup) * BD_COLS, split = (int)blockIdx.x / ngroup;
+  bool dense;
+  const int n = ffn_rows(ucount, f, dense_min, &dense);
+  const int nch_all = (n + BD_CH - 1) / BD_CH, cps = (nch_all + nsplit - 1) / nsplit;
+  const int ch0 = split * cps;
+  const int nch = max(0, min(nch_all, ch0 + cps) - ch0);
+  const float hs = pow2_scale(__uint_as_float(hmax[lane & 31]));
+  if (tid < BM) rsc[tid] = 1.f / pow2_scale(__uint_as_float(hmax[tid]));
+  // this thread's 8 columns (clamped into the row when past d, then dropped) and
+  // its first position pair
+  const int pc = tid & 31, rp0 = tid >> 5;
+  const bool okc = c0 + 8 * pc < d;
+  const int colc = min(c0 + 8 * pc, d - 8);
+  f16v acc = {};
+
+  struct Stage {
+    uint4 wv[4][2];   // the 16-byte piece of the rows at positions 2 p, 2 p + 1 (p = rp0 + 16 k)
+    float4 hv[2];     // 8 values of h for the A operands
+  };
+  // chunk c's rows (positions clamped into the list and the split); the dense and
+  // the list case are separate instantiations (see k_bdown_q4)
+  auto load_ids = [&](auto dense_c, int c, int (&id)[4][2]) __attribute__((always_inline)) {
+    const int base = (ch0 + min(c, nch - 1)) * BD_CH + 2 * rp0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int p = max(0, min(base + 32 * k + q, n - 1));
+        id[k][q] = decltype(dense_c)::value ? p : ulist[p];
+      }
+  };
+  auto fetch = [&](int c, const int (&id)[4][2], Stage& st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        st.wv[k][q] = *reinterpret_cast<const uint4*>(downT + (size_t)id[k][q] * d + colc);
+    const float4* hp =
+        reinterpret_cast<const float4*>(h32 + (size_t)((ch0 + min(c, nch - 1)) * (BD_CH / 16) + w) * 512 + 8 * lane);
+    st.hv[0] = hp[0];
+    st.hv[1] = hp[1];
+  };
+  // a chunk's operands into LDS; positions past the split or the list and columns
+  // past d are zero (h there is whatever an earlier call left)
+  auto convert = [&](const Stage& st, int c) __attribute__((always_inline)) {
+    const int base = (ch0 + c) * BD_CH;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p2 = 2 * (rp0 + 16 * k);
+      // zeroed by an AND with a mask (a select becomes a branch next to the loads)
+      const uint32_t m0 = 0u - (uint32_t)(okc && c < nch && base + p2 < n);
+      const uint32_t m1 = 0u - (uint32_t)(okc && c < nch && base + p2 + 1 < n);
+      const uint32_t a[4] = {st.wv[k][0].x & m0, st.wv[k][0].y & m0, st.wv[k][0].z & m0, st.wv[k][0].w & m0};
+      const uint32_t b[4] = {st.wv[k][1].x & m1, st.wv[k][1].y & m1, st.wv[k][1].z & m1, st.wv[k][1].w & m1};
+      _Float16* dst = &wt[bdh_slot(8 * pc, p2)];   // the 8 columns share the swizzle
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // columns 2 j and 2 j + 1: (row p2, row p2 + 1) pairs
+        *reinterpret_cast<uint32_t*>(dst + (2 * j) * BD_PAD) = __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(dst + (2 * j + 1) * BD_PAD) = __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);
+      }
+    }
+    // A operands: K step w of the chunk, operand slot lane (batch row lane % 32)
+    const int jj = base + 16 * w + 8 * (lane / 32);
+    const float hv8[8] = {st.hv[0].x, st.hv[0].y, st.hv[0].z, st.hv[0].w,
+                          st.hv[1].x, st.hv[1].y, st.hv[1].z, st.hv[1].w};
+    h8v ahi, alo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      _Float16 hi, lo;
+      split_f16(c < nch && jj + e < n ? hv8[e] * hs : 0.f, &hi, &lo);
+      ahi[e] = hi;
+      alo[e] = lo;
+    }
+    *reinterpret_cast<h8v*>(&as[0][w][8 * lane]) = ahi;
+    *reinterpret_cast<h8v*>(&as[1][w][8 * lane]) = alo;
+  };
+  auto step = [&](auto dense_c, int c, const Stage& cur, Stage& far, const int (&id_far)[4][2],
+                  int (&id_new)[4][2]) __attribute__((always_inline)) {
+    load_ids(dense_c, c + 5, id_new);
+    fetch(c + 3, id_far, far);
+    PI_ISSUE_FENCE();
+    convert(cur, c);
+    PI_ISSUE_FENCE();
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < BD_CH / 16; ++ks) {
+      const int kb = 16 * ks + 8 * (lane / 32);
+      const h8v ah = *reinterpret_cast<const h8v*>(&as[0][ks][8 * lane]);
+      const h8v al = *reinterpret_cast<const h8v*>(&as[1][ks][8 * lane]);
+      const h8v bw = *reinterpret_cast<const h8v*>(&wt[bdh_slot(BM * w + (lane & 31), kb)]);
+      acc = mfma(ah, bw, acc);
+      acc = mfma(al, bw, acc);
+    }
+    __syncthreads();
+    PI_ISSUE_FENCE();
+  };
+  auto run = [&](auto dc) __attribute__((always_inline)) {
+    int id0[4][2], id1[4][2], id2[4][2], id3[4][2];
+    Stage s0, s1, s2, s3;
+    load_ids(dc, 0, id0);
+    load_ids(dc, 1, id1);
+    load_ids(dc, 2, id2);
+    load_ids(dc, 3, id3);
+    fetch(0, id0, s0);
+    load_ids(dc, 4, id0);
+    fetch(1, id1, s1);
+    fetch(2, id2, s2);
+    int c = 0;
+    for (; c + 4 <= nch; c += 4) {
+      step(dc, c, s0, s3, id3, id1);
+      step(dc, c + 1, s1, s0, id0, id2);
+      step(dc, c + 2, s2, s1, id1, id3);
+      step(dc, c + 3, s3, s2, id2, id0);
+    }
+    // the last 1..3 chunks without a whole group of four (the stages are in their
+    // group-start roles here)
+    const int rem = nch - c;
+    if (rem == 1) {
+      step(dc, c, s0, s3, id3, id1);
+    } else if (rem == 2) {
+      step(dc, c, s0, s3, id3, id1);
+      step(dc, c + 1, s1, s0, id0, id2);
+    } else if (rem == 3) {
+      step(dc, c, s0, s3, id3, id1);
+      step(dc, c + 1, s1, s0, id0, id2);
+      step(dc, c + 2, s2, s1, id1, id3);
     }
   };
   if (nch > 0) {
