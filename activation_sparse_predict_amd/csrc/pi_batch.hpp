@@ -1064,7 +1064,13 @@ k_bdown_q4(const uint8_t* __restrict__ downT, const uint16_t* __restrict__ down_
   static_assert(BD_CH == 128 && BD_COLS == 8 * BM, "16 positions per wave, 8 tiles per block");
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int ngroup = (d + BD_COLS - 1) / BD_COLS;
-  const int c0 = (int)(blockIdx.x % ngroup) * BD_COLS, split = (int)blockIdx.x / ngroup;
+  // consecutive launch indices go to the 8 XCDs in turn: each XCD takes a run of
+  // consecutive (split, column group) items, so the column groups that share a
+  // line of a row's block scales, and the blocks that share a split's h, meet in
+  // one L2
+  const int nblk = (int)gridDim.x;
+  const int L = nblk % 8 == 0 ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)blockIdx.x / 8 : (int)blockIdx.x;
+  const int c0 = (L % ngroup) * BD_COLS, split = L / ngroup;
   bool dense;
   const int n = ffn_rows(ucount, f, dense_min, &dense);
   const int nch_all = (n + BD_CH - 1) / BD_CH, cps = (nch_all + nsplit - 1) / nsplit;
@@ -1257,7 +1263,13 @@ k_bdown_f16(const uint16_t* __restrict__ downT, int f, int d, const int32_t* __r
   static_assert(BD_CH == 128 && BD_COLS == 256, "32 pieces of 8 columns, 64 position pairs");
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int ngroup = (d + BD_COLS - 1) / BD_COLS;
-  const int c0 = (int)(blockIdx.x % ngroup) * BD_COLS, split = (int)blockIdx.x / ngroup;
+  // consecutive launch indices go to the 8 XCDs in turn: each XCD takes a run of
+  // consecutive (split, column group) items, so the column groups that share a
+  // line of a row's block scales, and the blocks that share a split's h, meet in
+  // one L2
+  const int nblk = (int)gridDim.x;
+  const int L = nblk % 8 == 0 ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)blockIdx.x / 8 : (int)blockIdx.x;
+  const int c0 = (L % ngroup) * BD_COLS, split = L / ngroup;
   bool dense;
   const int n = ffn_rows(ucount, f, dense_min, &dense);
   const int nch_all = (n + BD_CH - 1) / BD_CH, cps = (nch_all + nsplit - 1) / nsplit;
