@@ -335,6 +335,43 @@ def test_batch_hot_prefix():
 
 
 
+# ------------------------- chunk counts of the pipelined down projections
+# The Q4_0 and fp16 down projections take their split of the union in chunks of 128
+# positions, in a loop of four steps and then 1..3 straight-line steps.  At d = 1024
+# there are 16 splits, so a union of 128 * 16 * k rows gives every split k chunks;
+# d = 4160 has 17 column groups (a block count that is no multiple of 8, and column
+# tiles past d in the last group).
+REMAINDER_CASES = [(1024, 128 * 16 * 2), (1024, 128 * 16 * 3), (1024, 128 * 16 * 5 - 77),
+                   (1024, 128 * 16 * 8), (4160, 1500)]
+
+
+@pytest.mark.parametrize("name", ["q4-relu", "f16-relu"])
+def test_batch_down_chunk_remainders(name):
+    """pi_sparse_ffn over explicit unions whose splits hold 2, 3, 5 (the last chunk
+    ragged) and 8 chunks, gathered and dense, against the oracle; every sequence's
+    mask a random half of the union."""
+    nb = 8
+    rng = np.random.default_rng(2024)
+    for d, n in REMAINDER_CASES:
+        cfg = SMALL[name].with_(d=d, ffn=max(16384 + 111, n + 111) if d == 1024 else 3001, n_layers=1)
+        say(f"[batch_chunks] {name} d={d} f={cfg.ffn} union {n} batch {nb}")
+        lw = workload.make_layer(cfg, 0)
+        X = workload.make_x(cfg, 5, seqs=nb)
+        union = np.sort(rng.choice(cfg.ffn, size=n, replace=False)).astype(np.int32)
+        M = np.zeros((nb, cfg.ffn), np.uint8)
+        for b in range(nb):
+            M[b, union[rng.random(n) < 0.5]] = 1
+        Yr = oracle.sparse_ffn(cfg.act, lw.gate, lw.up, lw.downT, oracle.ffn_bias(lw), X, M)
+        for tag, frac in (("gathered", 2.0), ("dense", 1e-6)) if d == 1024 else (("gathered", 2.0),):
+            lw.dense_frac = frac
+            L = pi.DeviceLayer.upload(lw, DEV)
+            Y = run_sparse_ffn(L, X, union, M)
+            for b in range(nb):
+                check_y(Y[b], Yr[b], TOL[cfg.w_dtype])
+            say(f"  {tag}: max rel err {max(rel_err(Y[b], Yr[b]) for b in range(nb)):.2e}")
+            del L
+
+
 # ------------------------------------------- dense fallback at a large union
 def _high_union_layer(cfg, layer, shift):
     lw = workload.make_layer(cfg, layer)
